@@ -1,0 +1,152 @@
+// C ABI of the library (declared in include/qgemm.h): host-side argument
+// checks, then one launcher per entry point.  Nothing here allocates device
+// memory or synchronises the stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qgemm.h"
+#include "qg_launch.hpp"
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline qg_status_t hip_status(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_HIP; }
+
+inline bool is_float_dtype(int d) { return d == QG_F32 || d == QG_F16 || d == QG_BF16; }
+
+// Largest K for which K * 127 * 127 still fits int32.
+constexpr int64_t kMaxK8 = 2147483647LL / (127 * 127);
+constexpr int64_t kMaxDim = 2147483647LL;
+
+qg_status_t check_dims(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return QG_ERR_SHAPE;
+  return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qg_status_string(int status) {
+  switch (status) {
+    case QG_OK: return "QG_OK";
+    case QG_ERR_NULL: return "QG_ERR_NULL: a required pointer is NULL";
+    case QG_ERR_SHAPE: return "QG_ERR_SHAPE: a size is out of range or breaks a divisibility rule";
+    case QG_ERR_ALIGN: return "QG_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case QG_ERR_DTYPE: return "QG_ERR_DTYPE: unsupported dtype for this function";
+    case QG_ERR_HIP: return "QG_ERR_HIP: the HIP runtime refused the launch";
+    default: return "unknown qg status";
+  }
+}
+
+int qg_abi_version(void) { return 1; }
+
+qg_status_t quantize_per_token_i8(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* xq,
+                                  float* x_scale, void* stream) {
+  if (qg_status_t s = check_dims(M, 1, K)) return s;
+  if (K % 16) return QG_ERR_SHAPE;
+  if (!is_float_dtype(x_dtype)) return QG_ERR_DTYPE;
+  if (M == 0) return QG_OK;
+  if (!x || !xq || !x_scale) return QG_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xq)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_quant_per_token(x, x_dtype, M, K, xq, x_scale,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t quantize_weight_i8_per_channel(const float* w, int64_t K, int64_t N, int8_t* wq,
+                                           float* w_scale, void* stream) {
+  if (qg_status_t s = check_dims(1, N, K)) return s;
+  if (K % 16) return QG_ERR_SHAPE;
+  if (N == 0) return QG_OK;
+  if (!w || !wq || !w_scale) return QG_ERR_NULL;
+  if (!aligned16(w) || !aligned16(wq)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_quant_weight_i8(w, K, N, wq, w_scale, static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t quantize_weight_u4_g128(const float* w, int64_t K, int64_t N, int32_t* wq,
+                                    uint16_t* w_scale_f16, uint16_t* w_zero_f16, void* stream) {
+  if (qg_status_t s = check_dims(1, N, K)) return s;
+  if (K % 128 || K / 128 > 65535) return QG_ERR_SHAPE;
+  if (N == 0) return QG_OK;
+  if (!w || !wq || !w_scale_f16 || !w_zero_f16) return QG_ERR_NULL;
+  if (!aligned16(w) || !aligned16(wq)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_quant_weight_u4(w, K, N, wq, w_scale_f16, w_zero_f16,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                      const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                      void* stream) {
+  if (qg_status_t s = check_dims(M, N, K)) return s;
+  if (K % 16 || K > kMaxK8) return QG_ERR_SHAPE;
+  if (!is_float_dtype(y_dtype) && y_dtype != QG_I32) return QG_ERR_DTYPE;
+  if (M == 0 || N == 0) return QG_OK;
+  if (!xq || !wq || !y) return QG_ERR_NULL;
+  if (y_dtype != QG_I32 && (!x_scale || !w_scale)) return QG_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(wq)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_gemm_w8a8(xq, x_scale, wq, w_scale, M, N, K, y, y_dtype,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t gemm_w4a8_g128(const int8_t* xq, const float* x_scale, const int32_t* wq,
+                           const uint16_t* w_scale_f16, const uint16_t* w_zero_f16, int64_t M,
+                           int64_t N, int64_t K, void* y, int y_dtype, void* stream) {
+  if (qg_status_t s = check_dims(M, N, K)) return s;
+  if (K % 128) return QG_ERR_SHAPE;
+  if (y_dtype == QG_I32 && M * (K / 128) * N > kMaxDim) return QG_ERR_SHAPE;
+  if (!is_float_dtype(y_dtype) && y_dtype != QG_I32) return QG_ERR_DTYPE;
+  if (M == 0 || N == 0) return QG_OK;
+  if (!xq || !wq || !w_zero_f16 || !y) return QG_ERR_NULL;
+  if (y_dtype != QG_I32 && (!x_scale || !w_scale_f16)) return QG_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(wq)) return QG_ERR_ALIGN;
+  // the kernel reads the scales unconditionally; in I32 mode point them at
+  // the zero points (same shape, values unused)
+  const uint16_t* ws = w_scale_f16 ? w_scale_f16 : w_zero_f16;
+  return hip_status(qg::launch_gemm_w4a8(xq, x_scale, wq, ws, w_zero_f16, M, N, K, y, y_dtype,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t gemm_w4a16_g128(const void* x, int x_dtype, const int32_t* wq,
+                            const uint16_t* w_scale_f16, const uint16_t* w_zero_f16, int64_t M,
+                            int64_t N, int64_t K, void* y, int y_dtype, void* stream) {
+  if (qg_status_t s = check_dims(M, N, K)) return s;
+  if (K % 128) return QG_ERR_SHAPE;
+  if (x_dtype != QG_F16 && x_dtype != QG_BF16) return QG_ERR_DTYPE;
+  if (!is_float_dtype(y_dtype)) return QG_ERR_DTYPE;
+  if (M == 0 || N == 0) return QG_OK;
+  if (!x || !wq || !w_scale_f16 || !w_zero_f16 || !y) return QG_ERR_NULL;
+  if (!aligned16(x) || !aligned16(wq)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_gemm_w4a16(x, x_dtype, wq, w_scale_f16, w_zero_f16, M, N, K, y,
+                                          y_dtype, static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t smoothquant_fold(const float* x_cal, int64_t T, const float* w, int64_t K, int64_t N,
+                             float* s, float* w_out, void* stream) {
+  if (T <= 0 || N < 0 || K <= 0 || T > kMaxDim || K > kMaxDim || N > kMaxDim) return QG_ERR_SHAPE;
+  if (K % 4) return QG_ERR_SHAPE;
+  if (!x_cal || !w || !s || !w_out) return QG_ERR_NULL;
+  return hip_status(qg::launch_smoothquant_fold(x_cal, T, w, K, N, s, w_out,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t awq_fold(const float* x_cal, int64_t T, const float* w, int64_t K, int64_t N, float* s,
+                     float* w_out, void* stream) {
+  if (T <= 0 || N < 0 || K <= 0 || T > kMaxDim || K > kMaxDim || N > kMaxDim) return QG_ERR_SHAPE;
+  if (K % 4) return QG_ERR_SHAPE;
+  if (!x_cal || !w || !s || !w_out) return QG_ERR_NULL;
+  return hip_status(qg::launch_awq_fold(x_cal, T, w, K, N, s, w_out, static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t apply_smoothing(const float* x, int64_t M, int64_t K, const float* s, void* x_out,
+                            int out_dtype, void* stream) {
+  if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxDim) return QG_ERR_SHAPE;
+  if (K % 4) return QG_ERR_SHAPE;
+  if (!is_float_dtype(out_dtype)) return QG_ERR_DTYPE;
+  if (M == 0) return QG_OK;
+  if (!x || !s || !x_out) return QG_ERR_NULL;
+  return hip_status(qg::launch_apply_smoothing(x, M, K, s, x_out, out_dtype,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,209 @@
+// W4A16 weight-only GEMM: 16-bit float activations x g=128 uint4 weights, the
+// dequantization fused into the GEMM.
+// 「第4章：量化」 §3.1 (weight-only 4-bit, activations stay 16-bit) and §3.5
+// (a separate dequantize-then-GEMM pass is slower than fp16 at small batch;
+// fuse it); 「Quantization & Flash Attention」 §2.2 (AWQ-folded weights).
+//
+// Per group g:  p[m,g,n] = sum_{k in g} x[m,k] (q[n,k] - z[n,g])  on the fp16
+// (or bf16) matrix cores with binary32 accumulation, then
+// y[m,n] = sum_g s[n,g] p[m,g,n] in binary32.  The operand (q - z) is an
+// exact small integer; the scale multiplies the binary32 group sum, never
+// the 16-bit operand, so the only roundings are those of binary32 sums.
+//
+// fp16 unpack: (w >> 4i) & 0x000F000F | 0x64006400 is the fp16 pair
+// (1024 + q_i, 1024 + q_{i+4}); a packed fp16 subtract of (1024 + z) leaves
+// (q - z) exactly.  The activation halves are shuffled into the matching
+// [0,4,1,5,2,6,3,7] order.
+#include "qg_device.hpp"
+#include "qg_launch.hpp"
+
+namespace qg {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// halves [h0..h7] of an activation fragment -> [h0 h4 h1 h5 h2 h6 h3 h7]
+__device__ __forceinline__ v4i shuffle_halves(v4i x) {
+  const u32 d0 = (u32)x[0], d1 = (u32)x[1], d2 = (u32)x[2], d3 = (u32)x[3];
+  return v4i{(int)__builtin_amdgcn_perm(d2, d0, 0x05040100u),
+             (int)__builtin_amdgcn_perm(d2, d0, 0x07060302u),
+             (int)__builtin_amdgcn_perm(d3, d1, 0x05040100u),
+             (int)__builtin_amdgcn_perm(d3, d1, 0x07060302u)};
+}
+
+// 8 codes of word w -> (q - z) as fp16 halves in order [q0 q4 q1 q5 q2 q6 q3 q7]
+__device__ __forceinline__ v4i unpack_f16(u32 w, u32 zz /* fp16 pair of 1024 + z */) {
+  v4i r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32 t = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+    const h2 d = __builtin_bit_cast(h2, t) - __builtin_bit_cast(h2, zz);
+    r[i] = __builtin_bit_cast(int, d);
+  }
+  return r;
+}
+
+// bf16: (q - z) built exactly in binary32 (2^23 + q minus 2^23 + z), whose
+// upper half is the bf16 value; same output order as unpack_f16.
+__device__ __forceinline__ v4i unpack_bf16(u32 w, float zb /* 2^23 + z */) {
+  v4i r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(0x4B000000u | ((w >> (4 * i)) & 0xFu)) - zb;
+    const float hi = __uint_as_float(0x4B000000u | ((w >> (4 * i + 16)) & 0xFu)) - zb;
+    r[i] = (int)((__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u));
+  }
+  return r;
+}
+
+// Workgroup = WAVES waves owning 16*NT columns and 16*MT rows; groups split
+// across waves.  Lane l: row/column (l & 15); in a group it loads words
+// 4j..4j+3 of its column (j = l >> 4), MFMA h (0..3) takes word 4j+h, i.e.
+// k = 32j + 8h + 0..7.
+template <int MT, int NT, int WAVES, int U, int XDT, typename OutT>
+__global__ __launch_bounds__(64 * WAVES) void k_w4a16(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ wq,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
+    OutT* __restrict__ y) {
+  __shared__ v4f red[WAVES][MT][NT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, j = lane >> 4;
+  const int n_base = blockIdx.x * 16 * NT;
+  const int m_base = blockIdx.y * 16 * MT;
+  const int G = K >> 7, Kw = K >> 3;
+  const int gb = (int)((int64_t)G * wave / WAVES), ge = (int)((int64_t)G * (wave + 1) / WAVES);
+
+  bool nok[NT];
+  int ncol[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    ncol[t] = n_base + 16 * t + r;
+    nok[t] = ncol[t] < N;
+  }
+  bool mok[MT];
+  const uint16_t* xrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = m_base + 16 * mt + r;
+    mok[mt] = m < M;
+    xrow[mt] = x + (int64_t)(mok[mt] ? m : 0) * K + 32 * j;
+  }
+
+  v4f yacc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) yacc[mt][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int g0 = gb; g0 < ge; g0 += U) {
+    v4i wv[U][NT], xa[U][MT][4];
+    uint16_t sbits[U][NT], zbits[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = g0 + u;
+      const bool gin = g < ge;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bool ok = gin && nok[t];
+        const int64_t n = ok ? ncol[t] : 0;
+        wv[u][t] = ok ? ld16_stream(wq + n * Kw + 16 * g + 4 * j) : v4i{0, 0, 0, 0};
+        sbits[u][t] = ok ? wscale[n * G + g] : (uint16_t)0;
+        zbits[u][t] = ok ? wzero[n * G + g] : (uint16_t)0;
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bool ok = gin && mok[mt];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          xa[u][mt][h] = ok ? ld16(xrow[mt] + 128 * g + 8 * h) : v4i{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (g0 + u >= ge) break;
+      v4i a[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) a[mt][h] = shuffle_halves(xa[u][mt][h]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float zf = f16_bits_to_f32(zbits[u][t]);
+        const float s = f16_bits_to_f32(sbits[u][t]);
+        v4i b[4];
+        if constexpr (XDT == F16) {
+          const u32 zh = f32_to_f16_bits(1024.f + zf);
+          const u32 zz = zh | (zh << 16);
+#pragma unroll
+          for (int h = 0; h < 4; ++h) b[h] = unpack_f16((u32)wv[u][t][h], zz);
+        } else {
+          const float zb = 8388608.f + zf;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) b[h] = unpack_bf16((u32)wv[u][t][h], zb);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v4f p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            if constexpr (XDT == F16)
+              p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a[mt][h]),
+                                                         __builtin_bit_cast(v8h, b[h]), p, 0, 0, 0);
+            else
+              p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[mt][h]),
+                                                          __builtin_bit_cast(v8bf, b[h]), p, 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) yacc[mt][t][i] = __builtin_fmaf(s, p[i], yacc[mt][t][i]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[wave][mt][t][lane] = yacc[mt][t];
+  __syncthreads();
+  for (int it = threadIdx.x; it < MT * NT * 64; it += 64 * WAVES) {
+    const int l = it & 63, t = (it >> 6) % NT, mt = (it >> 6) / NT;
+    v4f sum = red[0][mt][t][l];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) sum += red[w][mt][t][l];
+    const int n = n_base + 16 * t + (l & 15);
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m_base + 16 * mt + 4 * (l >> 4) + i;
+      if (m < M) y[(int64_t)m * N + n] = Out<OutT>::cvt(sum[i]);
+    }
+  }
+}
+
+template <int XDT, typename OutT>
+static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
+                               const uint16_t* wz, int M, int N, int K, OutT* y, hipStream_t st) {
+  constexpr int MT = 1, NT = 1, WAVES = 8, U = 4;
+  dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
+  k_w4a16<MT, NT, WAVES, U, XDT, OutT><<<grid, dim3(64 * WAVES), 0, st>>>(x, wq, ws, wz, M, N, K, y);
+  return hipGetLastError();
+}
+
+template <int XDT>
+static hipError_t gemm_w4a16_x(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
+                               const uint16_t* wz, int M, int N, int K, void* y, int y_dtype,
+                               hipStream_t st) {
+  switch (y_dtype) {
+    case F32: return gemm_w4a16_t<XDT, float>(x, wq, ws, wz, M, N, K, (float*)y, st);
+    case BF16: return gemm_w4a16_t<XDT, uint16_t>(x, wq, ws, wz, M, N, K, (uint16_t*)y, st);
+    default: return gemm_w4a16_t<XDT, _Float16>(x, wq, ws, wz, M, N, K, (_Float16*)y, st);
+  }
+}
+
+hipError_t launch_gemm_w4a16(const void* x, int x_dtype, const int32_t* wq, const uint16_t* ws,
+                             const uint16_t* wz, int64_t M, int64_t N, int64_t K, void* y,
+                             int y_dtype, hipStream_t st) {
+  const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
+  if (x_dtype == F16) return gemm_w4a16_x<F16>(xh, wq, ws, wz, (int)M, (int)N, (int)K, y, y_dtype, st);
+  return gemm_w4a16_x<BF16>(xh, wq, ws, wz, (int)M, (int)N, (int)K, y, y_dtype, st);
+}
+
+}  // namespace qg

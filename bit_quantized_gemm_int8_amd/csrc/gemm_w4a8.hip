@@ -1,0 +1,198 @@
+// W4A8 GEMM with g=128 asymmetric uint4 weights dequantized inside the kernel.
+// 「LLM推理降本五要素」 §2.2 (W4A8, group size 128, per-group scale and zero
+// point); 「第4章：量化」 §1.1 (x_hat = (x_int - z) s) and §3.5 (fuse the
+// dequantization into the GEMM rather than running a separate pass).
+//
+// Per group g of 128 input channels (exact int32):
+//   acc[m,g,n] = sum_{k in g} xq[m,k] q[n,k]  -  z[n,g] * sum_{k in g} xq[m,k]
+// then y[m,n] = s_x[m] * sum_g s[n,g] * acc[m,g,n] in binary32.
+//
+// Unpack in registers: a packed word holds 8 codes (nibble j = k 8i+j);
+// w & 0x0F0F0F0F gives the even-k codes as bytes and (w >> 4) & 0x0F0F0F0F the
+// odd-k codes -- each already a valid int8 operand (0..15).  The activation
+// bytes are shuffled into the same [0,2,4,6,1,3,5,7] order, so the matrix core
+// pairs every code with its own activation.  The zero point enters once per
+// group through the token sums sum_k xq[m,k], which one extra MFMA against an
+// all-ones operand produces in the accumulator layout.
+#include "qg_device.hpp"
+#include "qg_launch.hpp"
+
+namespace qg {
+
+// bytes [b0..b7] of (lo, hi) -> [b0 b2 b4 b6 | b1 b3 b5 b7]
+__device__ __forceinline__ void even_odd_bytes(u32 lo, u32 hi, u32& e, u32& o) {
+  e = __builtin_amdgcn_perm(hi, lo, 0x06040200u);
+  o = __builtin_amdgcn_perm(hi, lo, 0x07050301u);
+}
+
+__device__ __forceinline__ v4i shuffle_act16(v4i x) {
+  v4i r;
+  u32 e, o;
+  even_odd_bytes((u32)x[0], (u32)x[1], e, o);
+  r[0] = (int)e;
+  r[1] = (int)o;
+  even_odd_bytes((u32)x[2], (u32)x[3], e, o);
+  r[2] = (int)e;
+  r[3] = (int)o;
+  return r;
+}
+
+__device__ __forceinline__ v4i unpack_u4_pair(u32 w0, u32 w1) {
+  return v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
+             (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store_out(OutT* y, int64_t idx, float v) {
+  y[idx] = Out<OutT>::cvt(v);
+}
+
+// Workgroup = WAVES waves owning 16*NT output columns and 16*MT rows; the
+// groups of K are split across the waves (contiguous runs), U groups issued
+// per batch.  Lane l: MFMA row/column (l & 15); within a group, words
+// 4j..4j+3 of its column with j = l >> 4 (one 16-byte load), of which MFMA h
+// takes words 4j+2h and 4j+2h+1 (k = 32j + 16h + 0..15).
+template <int MT, int NT, int WAVES, int U, typename OutT>
+__global__ __launch_bounds__(64 * WAVES) void k_w4a8(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, const int32_t* __restrict__ wq,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
+    OutT* __restrict__ y) {
+  constexpr bool kI32 = __is_same(OutT, int32_t);
+  __shared__ v4f red[kI32 ? 1 : WAVES][MT][NT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, j = lane >> 4;
+  const int n_base = blockIdx.x * 16 * NT;
+  const int m_base = blockIdx.y * 16 * MT;
+  const int G = K >> 7, Kw = K >> 3;
+  const int gb = (int)((int64_t)G * wave / WAVES), ge = (int)((int64_t)G * (wave + 1) / WAVES);
+
+  bool nok[NT];
+  int ncol[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    ncol[t] = n_base + 16 * t + r;
+    nok[t] = ncol[t] < N;
+  }
+  bool mok[MT];
+  const int8_t* xrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = m_base + 16 * mt + r;
+    mok[mt] = m < M;
+    xrow[mt] = xq + (int64_t)(mok[mt] ? m : 0) * K + 32 * j;
+  }
+  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+
+  v4f yacc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) yacc[mt][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int g0 = gb; g0 < ge; g0 += U) {
+    v4i wv[U][NT], xa[U][MT][2];
+    uint16_t sbits[U][NT], zbits[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = g0 + u;
+      const bool gin = g < ge;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bool ok = gin && nok[t];
+        const int64_t n = ok ? ncol[t] : 0;
+        wv[u][t] = ok ? ld16_stream(wq + n * Kw + 16 * g + 4 * j) : v4i{0, 0, 0, 0};
+        sbits[u][t] = ok ? wscale[n * G + g] : (uint16_t)0;
+        zbits[u][t] = ok ? wzero[n * G + g] : (uint16_t)0;
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bool ok = gin && mok[mt];
+        xa[u][mt][0] = ok ? ld16(xrow[mt] + 128 * g) : v4i{0, 0, 0, 0};
+        xa[u][mt][1] = ok ? ld16(xrow[mt] + 128 * g + 16) : v4i{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = g0 + u;
+      if (g >= ge) break;
+      v4i a[MT][2], rs[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        a[mt][0] = shuffle_act16(xa[u][mt][0]);
+        a[mt][1] = shuffle_act16(xa[u][mt][1]);
+        rs[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][0], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+        rs[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][1], ones, rs[mt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const v4i b0 = unpack_u4_pair((u32)wv[u][t][0], (u32)wv[u][t][1]);
+        const v4i b1 = unpack_u4_pair((u32)wv[u][t][2], (u32)wv[u][t][3]);
+        const int z = (int)f16_bits_to_f32(zbits[u][t]);
+        const float s = f16_bits_to_f32(sbits[u][t]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v4i acc = -z * rs[mt];
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][0], b0, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][1], b1, acc, 0, 0, 0);
+          if constexpr (kI32) {
+            // test output: per-group accumulators y[m][g][n]
+            if (nok[t]) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int m = m_base + 16 * mt + 4 * j + i;
+                if (m < M) y[((int64_t)m * G + g) * N + ncol[t]] = acc[i];
+              }
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yacc[mt][t][i] = __builtin_fmaf(s, (float)acc[i], yacc[mt][t][i]);
+          }
+        }
+      }
+    }
+  }
+  if constexpr (!kI32) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) red[wave][mt][t][lane] = yacc[mt][t];
+    __syncthreads();
+    for (int it = threadIdx.x; it < MT * NT * 64; it += 64 * WAVES) {
+      const int l = it & 63, t = (it >> 6) % NT, mt = (it >> 6) / NT;
+      v4f sum = red[0][mt][t][l];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) sum += red[w][mt][t][l];
+      const int n = n_base + 16 * t + (l & 15);
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m_base + 16 * mt + 4 * (l >> 4) + i;
+        if (m < M) store_out<OutT>(y, (int64_t)m * N + n, sum[i] * xs[m]);
+      }
+    }
+  }
+}
+
+template <typename OutT>
+static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* wq,
+                              const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
+                              hipStream_t st) {
+  constexpr int MT = 1, NT = 1, WAVES = 8, U = 4;
+  dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
+  k_w4a8<MT, NT, WAVES, U, OutT><<<grid, dim3(64 * WAVES), 0, st>>>(xq, xs, wq, ws, wz, M, N, K, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a8(const int8_t* xq, const float* xs, const int32_t* wq,
+                            const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
+                            int64_t K, void* y, int y_dtype, hipStream_t st) {
+  const int m = (int)M, n = (int)N, k = (int)K;
+  switch (y_dtype) {
+    case F32: return gemm_w4a8_t<float>(xq, xs, wq, ws, wz, m, n, k, (float*)y, st);
+    case F16: return gemm_w4a8_t<_Float16>(xq, xs, wq, ws, wz, m, n, k, (_Float16*)y, st);
+    case BF16: return gemm_w4a8_t<uint16_t>(xq, xs, wq, ws, wz, m, n, k, (uint16_t*)y, st);
+    default: return gemm_w4a8_t<int32_t>(xq, xs, wq, ws, wz, m, n, k, (int32_t*)y, st);
+  }
+}
+
+}  // namespace qg

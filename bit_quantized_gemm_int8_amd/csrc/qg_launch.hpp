@@ -1,0 +1,34 @@
+// Internal launchers: one per C-ABI entry point.  Arguments are already
+// validated by api.hip; each launcher only picks a kernel variant and
+// enqueues it on the stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+enum DType { F32 = 0, F16 = 1, BF16 = 2, I32 = 3 };
+
+hipError_t launch_quant_per_token(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* xq,
+                                  float* x_scale, hipStream_t st);
+hipError_t launch_quant_weight_i8(const float* w, int64_t K, int64_t N, int8_t* wq, float* ws,
+                                  hipStream_t st);
+hipError_t launch_quant_weight_u4(const float* w, int64_t K, int64_t N, int32_t* wq,
+                                  uint16_t* ws, uint16_t* wz, hipStream_t st);
+hipError_t launch_gemm_w8a8(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
+                            int64_t M, int64_t N, int64_t K, void* y, int y_dtype, hipStream_t st);
+hipError_t launch_gemm_w4a8(const int8_t* xq, const float* xs, const int32_t* wq,
+                            const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
+                            int64_t K, void* y, int y_dtype, hipStream_t st);
+hipError_t launch_gemm_w4a16(const void* x, int x_dtype, const int32_t* wq, const uint16_t* ws,
+                             const uint16_t* wz, int64_t M, int64_t N, int64_t K, void* y,
+                             int y_dtype, hipStream_t st);
+hipError_t launch_smoothquant_fold(const float* x_cal, int64_t T, const float* w, int64_t K,
+                                   int64_t N, float* s, float* w_out, hipStream_t st);
+hipError_t launch_awq_fold(const float* x_cal, int64_t T, const float* w, int64_t K, int64_t N,
+                           float* s, float* w_out, hipStream_t st);
+hipError_t launch_apply_smoothing(const float* x, int64_t M, int64_t K, const float* s,
+                                  void* x_out, int out_dtype, hipStream_t st);
+
+}  // namespace qg

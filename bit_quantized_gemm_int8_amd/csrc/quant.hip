@@ -1,0 +1,266 @@
+// Quantizers: per-token int8 activations (hot path), per-channel int8 and
+// g=128 uint4 weights (offline).
+//
+// 「第4章：量化」 §1.1 x_int = round(x/s) + z; §1.2 symmetric s = max|x|/127,
+// asymmetric scale from (max - min) over 2^bits - 1 steps; §1.3 per-token,
+// per-channel and per-group granularity.  「LLM推理降本五要素」 §5.2: round,
+// then clamp to the int8 range.
+#include "qg_device.hpp"
+#include "qg_launch.hpp"
+
+namespace qg {
+
+// ---------------------------------------------------------------------------
+// Per-token activation quantization.  One 256-thread workgroup per token
+// (row).  Each thread owns up to CH chunks of 16 consecutive elements, held in
+// registers between the absmax pass and the quantize pass, so the row is read
+// from HBM once; codes leave as one 16-byte store per chunk.
+// ---------------------------------------------------------------------------
+
+template <int DT>
+__device__ __forceinline__ void load_chunk16(const void* row, int c, float (&v)[16]) {
+  if constexpr (DT == F32) {
+    const float* p = reinterpret_cast<const float*>(row) + c * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v4i t = ld16(p + 4 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * i + e] = __int_as_float(t[e]);
+    }
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(row) + c * 16;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      v4i t = ld16(p + 8 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u32 u = (u32)t[e];
+        if constexpr (DT == BF16) {
+          v[8 * i + 2 * e] = bf16_bits_to_f32(u & 0xFFFFu);
+          v[8 * i + 2 * e + 1] = bf16_bits_to_f32(u >> 16);
+        } else {
+          v[8 * i + 2 * e] = f16_bits_to_f32((uint16_t)(u & 0xFFFFu));
+          v[8 * i + 2 * e + 1] = f16_bits_to_f32((uint16_t)(u >> 16));
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ v4i codes16(const float (&v)[16], float s, bool nz) {
+  v4i out;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    u32 word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      int q = nz ? sym_code_i8(v[4 * w + b], s) : 0;
+      word |= ((u32)q & 0xFFu) << (8 * b);
+    }
+    out[w] = (int)word;
+  }
+  return out;
+}
+
+template <int DT>
+constexpr int esize() { return DT == F32 ? 4 : 2; }
+
+// CH > 0: row cached in registers.  CH == 0: rows too long for that; the
+// second pass re-reads the row (it is then L2 resident).
+template <int DT, int CH>
+__global__ __launch_bounds__(256) void k_quant_per_token(const void* __restrict__ x, int64_t K,
+                                                         int8_t* __restrict__ xq,
+                                                         float* __restrict__ xs) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const char* xr = reinterpret_cast<const char*>(x) + row * K * esize<DT>();
+  int8_t* qr = xq + row * K;
+  const int nch = (int)(K >> 4);
+  float amax = 0.f;
+  if constexpr (CH > 0) {
+    float v[CH][16];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = threadIdx.x + c * 256;
+      if (idx < nch) {
+        load_chunk16<DT>(xr, idx, v[c]);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[c][e]));
+      }
+    }
+    amax = block_max<256>(amax, red);
+    const float s = amax / 127.f;
+    if (threadIdx.x == 0) xs[row] = amax > 0.f ? s : 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = threadIdx.x + c * 256;
+      if (idx < nch) st16(qr + (int64_t)idx * 16, codes16(v[c], s, amax > 0.f));
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < nch; idx += 256) {
+      float v[16];
+      load_chunk16<DT>(xr, idx, v);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+    amax = block_max<256>(amax, red);
+    const float s = amax / 127.f;
+    if (threadIdx.x == 0) xs[row] = amax > 0.f ? s : 0.f;
+    for (int idx = threadIdx.x; idx < nch; idx += 256) {
+      float v[16];
+      load_chunk16<DT>(xr, idx, v);
+      st16(qr + (int64_t)idx * 16, codes16(v, s, amax > 0.f));
+    }
+  }
+}
+
+template <int DT>
+static hipError_t quant_per_token_dt(const void* x, int64_t M, int64_t K, int8_t* xq, float* xs,
+                                     hipStream_t st) {
+  const int64_t nch = K / 16;
+  dim3 grid((unsigned)M), block(256);
+  if (nch <= 256)
+    k_quant_per_token<DT, 1><<<grid, block, 0, st>>>(x, K, xq, xs);
+  else if (nch <= 512)
+    k_quant_per_token<DT, 2><<<grid, block, 0, st>>>(x, K, xq, xs);
+  else if (nch <= 768)
+    k_quant_per_token<DT, 3><<<grid, block, 0, st>>>(x, K, xq, xs);
+  else if (nch <= 1024)
+    k_quant_per_token<DT, 4><<<grid, block, 0, st>>>(x, K, xq, xs);
+  else
+    k_quant_per_token<DT, 0><<<grid, block, 0, st>>>(x, K, xq, xs);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_per_token(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* xq,
+                                  float* x_scale, hipStream_t st) {
+  switch (x_dtype) {
+    case F32: return quant_per_token_dt<F32>(x, M, K, xq, x_scale, st);
+    case F16: return quant_per_token_dt<F16>(x, M, K, xq, x_scale, st);
+    default: return quant_per_token_dt<BF16>(x, M, K, xq, x_scale, st);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-output-channel int8 weights.  A workgroup owns 64 output channels:
+// pass 1 reduces max|w| down each column (coalesced along N), pass 2 walks K
+// in 64-row tiles, transposes through LDS and writes K-contiguous codes.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_quant_weight_i8(const float* __restrict__ w, int64_t K,
+                                                         int64_t N, int8_t* __restrict__ wq,
+                                                         float* __restrict__ ws) {
+  __shared__ float red[4][64];
+  __shared__ float colmax[64];
+  __shared__ float tile[64][65];
+  const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  const int64_t n = n0 + c;
+  float amax = 0.f;
+  if (n < N)
+    for (int64_t k = r; k < K; k += 4) amax = fmaxf(amax, fabsf(w[k * N + n]));
+  red[r][c] = amax;
+  __syncthreads();
+  if (r == 0) {
+    const float a = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+    colmax[c] = a;
+    if (n < N) ws[n] = a > 0.f ? a / 127.f : 0.f;
+  }
+  __syncthreads();
+  const int cc = threadIdx.x >> 2, seg = threadIdx.x & 3;
+  const int64_t ncol = n0 + cc;
+  const float a = colmax[cc];
+  const float s = a / 127.f;
+  for (int64_t k0 = 0; k0 < K; k0 += 64) {
+    for (int kk = r; kk < 64; kk += 4)
+      tile[kk][c] = (k0 + kk < K && n < N) ? w[(k0 + kk) * N + n] : 0.f;
+    __syncthreads();
+    if (ncol < N && k0 + seg * 16 < K) {
+      float v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = tile[seg * 16 + e][cc];
+      st16(wq + ncol * K + k0 + seg * 16, codes16(v, s, a > 0.f));
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_quant_weight_i8(const float* w, int64_t K, int64_t N, int8_t* wq, float* ws,
+                                  hipStream_t st) {
+  dim3 grid((unsigned)((N + 63) / 64)), block(256);
+  k_quant_weight_i8<<<grid, block, 0, st>>>(w, K, N, wq, ws);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// g=128 asymmetric uint4 weights.  A workgroup owns 64 output channels x one
+// group; each thread holds 32 of a column's 128 weights, the four quarters
+// meet in LDS for min/max, then every thread derives the same (s, z) and packs
+// its 32 codes into 4 words (one 16-byte store).
+// ---------------------------------------------------------------------------
+
+// Smallest fp16 value >= t (t >= 0, finite): the stored scale never falls
+// below (max - min)/15, so codes stay within [0, 15].
+__device__ __forceinline__ _Float16 f16_round_up(float t) {
+  _Float16 h = (_Float16)t;  // round to nearest even
+  if ((float)h < t) h = __builtin_bit_cast(_Float16, (uint16_t)(__builtin_bit_cast(uint16_t, h) + 1));
+  return h;
+}
+
+__global__ __launch_bounds__(256) void k_quant_weight_u4(const float* __restrict__ w, int64_t K,
+                                                         int64_t N, int32_t* __restrict__ wq,
+                                                         uint16_t* __restrict__ wscale,
+                                                         uint16_t* __restrict__ wzero) {
+  __shared__ float rlo[4][64], rhi[4][64];
+  const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 64 + c;
+  const int64_t g = blockIdx.y;
+  const int64_t G = K >> 7;
+  float v[32];
+  float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+  if (n < N) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      v[i] = w[(g * 128 + r * 32 + i) * N + n];
+      lo = fminf(lo, v[i]);
+      hi = fmaxf(hi, v[i]);
+    }
+  }
+  rlo[r][c] = lo;
+  rhi[r][c] = hi;
+  __syncthreads();
+  if (n >= N) return;
+  lo = fminf(fminf(rlo[0][c], rlo[1][c]), fminf(rlo[2][c], rlo[3][c]));
+  hi = fmaxf(fmaxf(rhi[0][c], rhi[1][c]), fmaxf(rhi[2][c], rhi[3][c]));
+  const float t = (hi - lo) / 15.f;
+  const _Float16 h = f16_round_up(t);
+  const float s = (float)h;
+  float z = 0.f;
+  if (s > 0.f) z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.f), 15.f);
+  v4i words;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32 word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float q = 0.f;
+      if (s > 0.f) q = fminf(fmaxf(__builtin_rintf(v[8 * i + e] / s) + z, 0.f), 15.f);
+      word |= ((u32)q) << (4 * e);
+    }
+    words[i] = (int)word;
+  }
+  st16(wq + n * (K >> 3) + g * 16 + r * 4, words);
+  if (r == 0) {
+    wscale[n * G + g] = __builtin_bit_cast(uint16_t, h);
+    wzero[n * G + g] = __builtin_bit_cast(uint16_t, (_Float16)z);
+  }
+}
+
+hipError_t launch_quant_weight_u4(const float* w, int64_t K, int64_t N, int32_t* wq,
+                                  uint16_t* ws, uint16_t* wz, hipStream_t st) {
+  dim3 grid((unsigned)((N + 63) / 64), (unsigned)(K / 128)), block(256);
+  k_quant_weight_u4<<<grid, block, 0, st>>>(w, K, N, wq, ws, wz);
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -1,0 +1,212 @@
+/*
+ * qgemm.h -- C ABI of the quantized linear layer for AMD MI355X (gfx950).
+ *
+ * The layer computes Y[M,N] = X[M,K] . W[K,N] from quantized operands:
+ *   - per-token dynamic symmetric int8 activations,
+ *   - per-output-channel symmetric int8 weights (W8A8), or
+ *   - group-wise (128 along K) asymmetric uint4 weights dequantized inside the
+ *     GEMM, with int8 activations (W4A8) or 16-bit float activations (W4A16).
+ *
+ * Sources, cited by page title and section:
+ *   「第4章：量化」: §1.1 x_int = round(x/s) + z and x_hat = (x_int - z) s;
+ *     §1.2 symmetric s = max|x|/127 and asymmetric scale from max - min;
+ *     §1.3 per-channel, per-group (g = 32/64/128) and per-token (dynamic)
+ *     granularity; §2.2 the SmoothQuant fold; §2.3 W8A8 runs the GEMM on int8
+ *     units; §3.1 weight-only 4-bit keeps activations in 16-bit floats;
+ *     §3.2-3.3 bits = 4, group size 128, zero point on, contiguous groups;
+ *     §3.5 dequantize inside the GEMM instead of a separate pass.
+ *   「Quantization & Flash Attention」 §2.2-2.3: the AWQ per-channel fold.
+ *   「LLM推理降本五要素」 §2.1 (W8A8 decode is weight-bandwidth bound), §2.2
+ *     (W4A8 with per-group scale and zero; the quantized_matmul(x, weight,
+ *     scale, zero) argument order), §5.2 (round, then clamp to int8).
+ *
+ * Conventions for every function below.
+ *   Pointers: DEVICE pointers, allocated and freed by the caller, contiguous
+ *     row-major, 16-byte aligned.  The library allocates nothing, keeps no
+ *     state between calls and may be called from several host threads.
+ *   stream: a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; results are ready once the stream is
+ *     synchronised.
+ *   Sizes: int64_t counts of elements.  M == 0 or N == 0 is a valid empty
+ *     problem: nothing is launched and QG_OK is returned.
+ *   Errors: arguments are checked on the host before anything is enqueued; a
+ *     bad argument returns QG_ERR_NULL / QG_ERR_SHAPE / QG_ERR_ALIGN /
+ *     QG_ERR_DTYPE and enqueues nothing.  A failed launch returns QG_ERR_HIP.
+ *     A device fault surfaces at the caller's next synchronisation.  Inputs
+ *     holding NaN or Inf give undefined codes and outputs.
+ *   Rounding: quantization decisions use IEEE binary32 with correctly rounded
+ *     division and round-half-to-even; outputs are rounded to nearest even.
+ *   Packed uint4 format: a weight column n (output channel) stores K codes as
+ *     K/8 int32 words, K-contiguous; word i holds k = 8i .. 8i+7, the code of
+ *     k = 8i + j in bits 4j .. 4j+3.  Group g covers k in [128g, 128g+128);
+ *     its scale and zero point are fp16 values (raw uint16 bits) at [n][g].
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qg_status {
+  QG_OK = 0,
+  QG_ERR_NULL = 1,   /* a required pointer is NULL                              */
+  QG_ERR_SHAPE = 2,  /* a size is negative, zero where not allowed, or breaks a
+                        divisibility rule stated below                         */
+  QG_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned                        */
+  QG_ERR_DTYPE = 4,  /* a dtype argument is not one the function accepts       */
+  QG_ERR_HIP = 5     /* the HIP runtime refused the launch                      */
+} qg_status_t;
+
+typedef enum qg_dtype {
+  QG_F32 = 0,   /* IEEE binary32                                  */
+  QG_F16 = 1,   /* IEEE binary16                                  */
+  QG_BF16 = 2,  /* bfloat16 (upper half of a binary32)            */
+  QG_I32 = 3    /* int32: raw integer accumulators (test output) */
+} qg_dtype_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qg_status_string(int status);
+
+/* ABI version of this header: 1. */
+int qg_abi_version(void);
+
+/*
+ * Per-token dynamic symmetric int8 quantization of activations.
+ * 「第4章：量化」 §1.3 (per-token, dynamic), §1.2 (symmetric), §1.1;
+ * 「LLM推理降本五要素」 §5.2 (round then clamp).
+ *   For each row m:  a = max_k |x[m,k]|;  s = a / 127;
+ *                    xq[m,k] = clamp(rne(x[m,k] / s), -127, 127);
+ *   a row with a == 0 gets s = 0 and all-zero codes.
+ * x:        [M][K] of x_dtype (QG_F32, QG_F16 or QG_BF16), read only.
+ * xq:       [M][K] int8 codes, written.
+ * x_scale:  [M] float scales, written.
+ * K must be a positive multiple of 16.
+ */
+qg_status_t quantize_per_token_i8(const void* x, int x_dtype, int64_t M, int64_t K,
+                                  int8_t* xq, float* x_scale, void* stream);
+
+/*
+ * Per-output-channel symmetric int8 quantization of a weight matrix (offline).
+ * 「第4章：量化」 §1.3 (per-channel), §1.2 (symmetric), §1.1.
+ *   For each output channel n:  s = max_k |w[k,n]| / 127;
+ *                               wq[n,k] = clamp(rne(w[k,n] / s), -127, 127).
+ * w:        [K][N] float (logical W of Y = X W), read only.
+ * wq:       [N][K] int8 codes (K-contiguous per output channel), written.
+ * w_scale:  [N] float scales, written.
+ * K must be a positive multiple of 16.
+ */
+qg_status_t quantize_weight_i8_per_channel(const float* w, int64_t K, int64_t N,
+                                           int8_t* wq, float* w_scale, void* stream);
+
+/*
+ * Group-wise asymmetric uint4 quantization of a weight matrix (offline), with
+ * groups of 128 consecutive input channels.
+ * 「第4章：量化」 §1.1 (round(x/s) + z, rounded before z is added), §1.2
+ * (asymmetric, 2^4 - 1 = 15 steps), §1.3 (per-group), §3.2-3.3 (4 bits,
+ * group 128, zero point); 「LLM推理降本五要素」 §2.2.
+ *   For each output channel n and group g, over its 128 weights:
+ *     t = (max - min) / 15 (binary32);  s = the smallest fp16 value >= t;
+ *     z = clamp(rne(-min / s), 0, 15);
+ *     q = clamp(rne(w / s) + z, 0, 15);
+ *   a constant group gets s = 0, z = 0 and q = 0.
+ * w:           [K][N] float, read only; (max - min)/15 must fit fp16.
+ * wq:          [N][K/8] int32 packed codes (format above), written.
+ * w_scale_f16: [N][K/128] fp16 bits of s, written.
+ * w_zero_f16:  [N][K/128] fp16 bits of z (an integer 0..15), written.
+ * K must be a positive multiple of 128.
+ */
+qg_status_t quantize_weight_u4_g128(const float* w, int64_t K, int64_t N, int32_t* wq,
+                                    uint16_t* w_scale_f16, uint16_t* w_zero_f16,
+                                    void* stream);
+
+/*
+ * W8A8 GEMM: int8 x int8 -> exact int32 accumulation, then the per-token x
+ * per-output-channel scale epilogue.
+ * 「第4章：量化」 §2.3 (the GEMM on int8 units), §1.1 (x_hat = x_int s);
+ * 「LLM推理降本五要素」 §2.1.
+ *   acc[m,n] = sum_k xq[m,k] wq[n,k];   y[m,n] = (acc * x_scale[m]) * w_scale[n]
+ * xq [M][K] int8, x_scale [M] float, wq [N][K] int8, w_scale [N] float: read.
+ * y: [M][N] of y_dtype, written: QG_F32, QG_BF16 or QG_F16 (the scaled
+ *    result), or QG_I32 (acc itself, scales ignored and may be NULL).
+ * K must be a positive multiple of 16 (|acc| <= K 127^2 must fit int32, so
+ * K <= 133144).  M <= 64 runs the weight-streaming decode kernel, larger M the
+ * LDS-tiled matrix-core kernel.
+ */
+qg_status_t gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                      const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
+                      int y_dtype, void* stream);
+
+/*
+ * W4A8 GEMM with g=128 uint4 weights unpacked and zero-point corrected inside
+ * the kernel (no separate dequantization pass).
+ * 「LLM推理降本五要素」 §2.2 (W4A8, group 128, per-group scale and zero);
+ * 「第4章：量化」 §1.1, §3.5 (fused dequantization).
+ *   acc[m,g,n] = sum_{k in g} xq[m,k] (q[n,k] - z[n,g])   (exact int32)
+ *   y[m,n]     = x_scale[m] * sum_g s[n,g] acc[m,g,n]     (binary32)
+ * xq [M][K] int8, x_scale [M] float, wq [N][K/8] packed, w_scale_f16 and
+ * w_zero_f16 [N][K/128]: read.
+ * y: [M][N] of QG_F32, QG_BF16 or QG_F16; or QG_I32, in which case y is
+ *    [M][K/128][N] int32 holding acc[m,g,n] (x_scale and w_scale_f16 unused).
+ * K must be a positive multiple of 128.
+ */
+qg_status_t gemm_w4a8_g128(const int8_t* xq, const float* x_scale, const int32_t* wq,
+                           const uint16_t* w_scale_f16, const uint16_t* w_zero_f16,
+                           int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                           void* stream);
+
+/*
+ * W4A16 weight-only GEMM: 16-bit float activations, g=128 uint4 weights
+ * unpacked to exact (q - z) values in registers and fed to the fp16 (or bf16)
+ * matrix cores; each group's binary32 partial sum is then scaled by s.
+ * 「第4章：量化」 §3.1 (weight-only 4-bit), §3.5 (fused dequantization);
+ * 「Quantization & Flash Attention」 §2.2 (the AWQ-folded weights it serves).
+ *   p[m,g,n] = sum_{k in g} x[m,k] (q[n,k] - z[n,g]);  y[m,n] = sum_g s[n,g] p[m,g,n]
+ * x: [M][K] of x_dtype, QG_F16 (fp16 matrix cores) or QG_BF16 (bf16).
+ * y: [M][N] of y_dtype: QG_F16, QG_BF16 or QG_F32.
+ * K must be a positive multiple of 128.
+ */
+qg_status_t gemm_w4a16_g128(const void* x, int x_dtype, const int32_t* wq,
+                            const uint16_t* w_scale_f16, const uint16_t* w_zero_f16,
+                            int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                            void* stream);
+
+/*
+ * Offline SmoothQuant fold with alpha = 0.5 (「第4章：量化」 §2.2):
+ *   s[j] = sqrt(max_t |x_cal[t,j]|) / sqrt(max_n |w[j,n]|)  (binary32, each
+ *          root and the quotient correctly rounded; s = 1 if either max is 0)
+ *   w_out[j,n] = s[j] * w[j,n]
+ * x_cal [T][K] float (calibration activations), w [K][N] float: read.
+ * s [K] float and w_out [K][N] float: written (w_out may equal w).
+ * Activations are then divided by s (apply_smoothing).  K % 4 == 0.
+ */
+qg_status_t smoothquant_fold(const float* x_cal, int64_t T, const float* w, int64_t K,
+                             int64_t N, float* s, float* w_out, void* stream);
+
+/*
+ * Offline AWQ fold with alpha = 0.5 (「Quantization & Flash Attention」 §2.3):
+ *   s[c] = sqrt(mean_t |x_cal[t,c]|), the mean a binary64 sum in token order
+ *          divided by T and rounded to binary32, then a binary32 root
+ *          (s = 1 if the mean is 0);
+ *   w_out[c,n] = s[c] * w[c,n]
+ * Arguments as for smoothquant_fold.
+ */
+qg_status_t awq_fold(const float* x_cal, int64_t T, const float* w, int64_t K, int64_t N,
+                     float* s, float* w_out, void* stream);
+
+/*
+ * Divide activation columns by a fold's scales: x_out[m,j] = x[m,j] / s[j]
+ * (binary32, correctly rounded), stored as out_dtype (QG_F32, QG_F16 or
+ * QG_BF16, round to nearest even).  x [M][K] float, s [K]: read.  K % 4 == 0.
+ * (「第4章：量化」 §2.2: X diag(s)^-1.)
+ */
+qg_status_t apply_smoothing(const float* x, int64_t M, int64_t K, const float* s,
+                            void* x_out, int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

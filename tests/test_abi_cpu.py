@@ -1,0 +1,95 @@
+"""The C-ABI library loads without a GPU, exports every function the header
+declares, and rejects bad arguments on the host (nothing is launched).
+
+Failure handling is forced from the host: every call below fails validation
+before any HIP call, so no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+
+
+def _lib():
+    import bit_quantized_gemm_int8_amd as q
+    if not os.path.exists(q.LIB_PATH):
+        from bit_quantized_gemm_int8_amd.build import build
+        build()
+    return q.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = set(_declared())
+    for n in ["quantize_per_token_i8", "quantize_weight_i8_per_channel",
+              "quantize_weight_u4_g128", "gemm_w8a8", "gemm_w4a8_g128", "gemm_w4a16_g128",
+              "smoothquant_fold", "awq_fold", "apply_smoothing", "qg_status_string",
+              "qg_abi_version"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared():
+        assert hasattr(lib, name), f"{name} declared in qgemm.h but not exported"
+    assert lib.qg_abi_version() == 1
+
+
+P = ctypes.c_void_p
+A = P(4096)          # aligned dummy address, never dereferenced: validation fails first
+MIS = P(4097)        # misaligned
+
+
+def test_validation_codes():
+    lib = _lib()
+    OK, NULL, SHAPE, ALIGN, DTYPE = 0, 1, 2, 3, 4
+    q = lib.quantize_per_token_i8
+    assert q(None, 0, 4, 16, None, None, None) == NULL
+    assert q(A, 0, 4, 17, A, A, None) == SHAPE
+    assert q(A, 0, 4, 0, A, A, None) == SHAPE
+    assert q(A, 0, -1, 16, A, A, None) == SHAPE
+    assert q(A, 3, 4, 16, A, A, None) == DTYPE
+    assert q(MIS, 0, 4, 16, A, A, None) == ALIGN
+    assert q(None, 0, 0, 16, None, None, None) == OK          # empty: nothing to do
+    g = lib.gemm_w8a8
+    assert g(A, A, A, A, 4, 4, 16, None, 2, None) == NULL
+    assert g(A, None, A, None, 4, 4, 16, A, 2, None) == NULL   # scales needed unless I32
+    assert g(A, A, A, A, 4, 4, 24, A, 2, None) == SHAPE
+    assert g(A, A, A, A, 4, 4, 16 * 8400, A, 2, None) == SHAPE  # acc would overflow int32
+    assert g(A, A, A, A, 4, 4, 16, A, 9, None) == DTYPE
+    assert g(A, A, MIS, A, 4, 4, 16, A, 2, None) == ALIGN
+    assert g(None, None, None, None, 0, 4, 16, None, 2, None) == OK
+    assert g(None, None, None, None, 4, 0, 16, None, 2, None) == OK
+    w4 = lib.gemm_w4a8_g128
+    assert w4(A, A, A, A, A, 4, 4, 192, A, 2, None) == SHAPE
+    assert w4(A, A, A, A, None, 4, 4, 128, A, 2, None) == NULL
+    w16 = lib.gemm_w4a16_g128
+    assert w16(A, 0, A, A, A, 4, 4, 128, A, 1, None) == DTYPE  # fp32 activations
+    assert w16(A, 1, A, A, A, 4, 4, 128, A, 3, None) == DTYPE  # int32 output
+    assert w16(A, 1, A, A, A, 4, 4, 100, A, 1, None) == SHAPE
+    u4 = lib.quantize_weight_u4_g128
+    assert u4(A, 130, 8, A, A, A, None) == SHAPE
+    assert u4(A, 128, 8, A, None, A, None) == NULL
+    i8 = lib.quantize_weight_i8_per_channel
+    assert i8(A, 20, 8, A, A, None) == SHAPE
+    assert lib.smoothquant_fold(A, 0, A, 16, 4, A, A, None) == SHAPE
+    assert lib.awq_fold(A, 4, A, 18, 4, A, A, None) == SHAPE
+    assert lib.apply_smoothing(A, 4, 16, A, A, 3, None) == DTYPE
+    assert "SHAPE" in lib.qg_status_string(2).decode()
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    import bit_quantized_gemm_int8_amd as q
+    _lib()
+    with pytest.raises(TypeError):
+        q.quantize_per_token_i8(torch.zeros(4, 16))

@@ -1,0 +1,197 @@
+"""GPU parity of the three GEMMs against the oracle.
+
+Integer accumulators (the QG_I32 outputs) must match bit for bit; scaled
+outputs must meet tests/tolerance.py.  Operand codes come from the oracle so
+that the GEMMs are checked on their own; the chained runs live in
+test_gpu_workloads.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_gemm_int8_amd as qg
+import oracle
+from tests.gpu_util import to_dev, to_np, out_f64
+from tests.tolerance import assert_close
+from workloads import f32_to_bf16_bits, f32_to_f16
+
+pytestmark = pytest.mark.gpu
+
+TORCH_OUT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+W8A8_SHAPES = [(16, 512, 512), (1, 16, 16), (3, 17, 48), (8, 11008, 4096), (17, 40, 528),
+               (33, 100, 1024), (64, 64, 64), (65, 300, 272), (100, 257, 4096),
+               (300, 520, 1040), (257, 1000, 1936)]
+
+
+def _codes(rng, shape):
+    return rng.integers(-127, 128, shape).astype(np.int8)
+
+
+@pytest.mark.parametrize("M,N,K", W8A8_SHAPES)
+def test_w8a8_acc_bitwise(M, N, K):
+    rng = np.random.default_rng(M * 31 + N * 7 + K)
+    xq, wq = _codes(rng, (M, K)), _codes(rng, (N, K))
+    acc = qg.gemm_w8a8(to_dev(xq), None, to_dev(wq), None, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(acc), oracle.gemm_w8a8_acc(xq, wq))
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_w8a8_acc_extremes(M):
+    K, N = 4096, 48
+    xq = np.full((M, K), 127, np.int8)
+    xq[1::2] = -127
+    wq = np.full((N, K), -127, np.int8)
+    wq[::3] = 127
+    acc = to_np(qg.gemm_w8a8(to_dev(xq), None, to_dev(wq), None, out_dtype=torch.int32))
+    np.testing.assert_array_equal(acc, oracle.gemm_w8a8_acc(xq, wq))
+    assert np.abs(acc).max() == K * 127 * 127
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("M,N,K", [(16, 512, 512), (8, 11008, 4096), (100, 257, 4096), (3, 17, 48)])
+def test_w8a8_scaled(fmt, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    xq, wq = _codes(rng, (M, K)), _codes(rng, (N, K))
+    sx = (rng.random(M) * 0.05 + 1e-3).astype(np.float32)
+    sw = (rng.random(N) * 1e-3 + 1e-5).astype(np.float32)
+    y = qg.gemm_w8a8(to_dev(xq), to_dev(sx), to_dev(wq), to_dev(sw), out_dtype=TORCH_OUT[fmt])
+    assert_close(out_f64(y), oracle.gemm_w8a8(xq, sx, wq, sw), fmt, what=f"w8a8 {fmt}")
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 512, 512), (200, 300, 1024)])
+def test_w8a8_power_of_two_scales_bitwise(M, N, K):
+    rng = np.random.default_rng(5)
+    xq, wq = _codes(rng, (M, K)), _codes(rng, (N, K))
+    sx = (2.0 ** rng.integers(-10, -2, M)).astype(np.float32)
+    sw = (2.0 ** rng.integers(-14, -6, N)).astype(np.float32)
+    y = qg.gemm_w8a8(to_dev(xq), to_dev(sx), to_dev(wq), to_dev(sw), out_dtype=torch.float32)
+    np.testing.assert_array_equal(out_f64(y), oracle.gemm_w8a8(xq, sx, wq, sw))
+
+
+def test_w8a8_prefill_full_sampled():
+    """4096 x 11008 x 4096 in the launch configuration the benchmark times;
+    the oracle checks 48 sampled rows (all columns), including the last tile."""
+    M, N, K = 4096, 11008, 4096
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+    wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+    sx = torch.rand(M, device="cuda", generator=g) * 0.05 + 1e-3
+    sw = torch.rand(N, device="cuda", generator=g) * 1e-3 + 1e-5
+    acc = qg.gemm_w8a8(xq, None, wq, None, out_dtype=torch.int32)
+    y = qg.gemm_w8a8(xq, sx, wq, sw, out_dtype=torch.bfloat16)
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1, M - 2, 255, 256]]))
+    xq_n, wq_n = to_np(xq), to_np(wq)
+    ref = oracle.gemm_w8a8_acc(xq_n[rows], wq_n)
+    np.testing.assert_array_equal(to_np(acc)[rows], ref)
+    yref = oracle.gemm_w8a8(xq_n[rows], to_np(sx)[rows], wq_n, to_np(sw))
+    assert_close(out_f64(y)[rows], yref, "bf16", what="prefill bf16")
+    # run-to-run determinism
+    y2 = qg.gemm_w8a8(xq, sx, wq, sw, out_dtype=torch.bfloat16)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+# ---------------------------------------------------------------- W4A8 / W4A16
+
+def _u4_weights(rng, K, N):
+    w = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    return oracle.quantize_weight_u4_g128(w)
+
+
+def _w4_devs(packed, sc, zz):
+    return to_dev(packed), to_dev(sc), to_dev(zz)
+
+
+W4_SHAPES = [(16, 4096, 11008), (1, 16, 128), (5, 17, 256), (16, 300, 1024), (17, 64, 384),
+             (33, 40, 640), (1, 12288, 4096), (3, 100, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", W4_SHAPES)
+def test_w4a8_group_acc_bitwise(M, N, K):
+    rng = np.random.default_rng(M * 13 + N + K)
+    packed, sc, zz = _u4_weights(rng, K, N)
+    xq = _codes(rng, (M, K))
+    wqd, scd, zzd = _w4_devs(packed, sc, zz)
+    acc = qg.gemm_w4a8_g128(to_dev(xq), None, wqd, None, zzd, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(acc), oracle.gemm_w4a8_g128_acc(xq, packed, zz))
+
+
+def _w4a8_floor(xq, sx, packed, sc, zz):
+    acc = oracle.gemm_w4a8_g128_acc(xq, packed, zz).astype(np.float64)       # [M, G, N]
+    s = sc.astype(np.float64).T                                              # [G, N]
+    B = np.abs(sx.astype(np.float64))[:, None] * np.abs(acc * s[None]).sum(axis=1)
+    G = acc.shape[1]
+    return (G + 10) * 2.0 ** -24 * B
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 11008), (5, 17, 256), (33, 40, 640)])
+def test_w4a8_scaled(fmt, M, N, K):
+    rng = np.random.default_rng(M + 3 * N + K)
+    packed, sc, zz = _u4_weights(rng, K, N)
+    xq = _codes(rng, (M, K))
+    sx = (rng.random(M) * 0.05 + 1e-3).astype(np.float32)
+    wqd, scd, zzd = _w4_devs(packed, sc, zz)
+    y = qg.gemm_w4a8_g128(to_dev(xq), to_dev(sx), wqd, scd, zzd, out_dtype=TORCH_OUT[fmt])
+    yref = oracle.gemm_w4a8_g128(xq, sx, packed, sc, zz)
+    n = assert_close(out_f64(y), yref, fmt, floor=_w4a8_floor(xq, sx, packed, sc, zz),
+                     what=f"w4a8 {fmt}")
+    print(f"w4a8 {fmt} {M}x{N}x{K}: {n} of {yref.size} outputs within the cancellation floor only")
+
+
+def _w4a16_floor(x64, packed, sc, zz):
+    codes = oracle.unpack_u4(packed).astype(np.float64)                    # [N, K]
+    N, K = codes.shape
+    G = K // 128
+    wz = np.abs(codes.reshape(N, G, 128) - zz.astype(np.float64)[:, :, None])
+    B = np.zeros((x64.shape[0], N))
+    for g in range(G):
+        B += (np.abs(x64[:, 128 * g:128 * (g + 1)]) @ wz[:, g, :].T) * sc.astype(np.float64)[:, g]
+    return (128 + G + 10) * 2.0 ** -24 * B
+
+
+@pytest.mark.parametrize("xfmt", ["f16", "bf16"])
+@pytest.mark.parametrize("fmt", ["f16", "f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(1, 12288, 4096), (5, 17, 256), (16, 300, 1024), (33, 40, 640)])
+def test_w4a16(xfmt, fmt, M, N, K):
+    rng = np.random.default_rng(M * 5 + N + K)
+    packed, sc, zz = _u4_weights(rng, K, N)
+    x32 = rng.standard_normal((M, K)).astype(np.float32)
+    if xfmt == "f16":
+        xh = f32_to_f16(x32)
+        xd, x64 = to_dev(xh), xh.astype(np.float64)
+    else:
+        xb = f32_to_bf16_bits(x32)
+        xd, x64 = to_dev(xb, "bf16"), oracle.to_f32(xb, "bf16").astype(np.float64)
+    wqd, scd, zzd = _w4_devs(packed, sc, zz)
+    y = qg.gemm_w4a16_g128(xd, wqd, scd, zzd, out_dtype=TORCH_OUT[fmt])
+    yref = oracle.gemm_w4a16_g128(x64, packed, sc, zz)
+    n = assert_close(out_f64(y), yref, fmt, floor=_w4a16_floor(x64, packed, sc, zz),
+                     what=f"w4a16 x{xfmt} {fmt}")
+    print(f"w4a16 x{xfmt}->{fmt} {M}x{N}x{K}: {n} of {yref.size} within the floor only")
+
+
+def test_w4a16_exact_case_bitwise():
+    """Power-of-two scales and small-integer activations make every partial sum
+    exact in binary32, so the fp32 output must equal y_exact bit for bit."""
+    rng = np.random.default_rng(9)
+    M, N, K = 4, 48, 512
+    codes = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    packed = oracle.pack_u4(codes)
+    G = K // 128
+    zz = rng.integers(0, 16, (N, G)).astype(np.float16)
+    sc = (2.0 ** rng.integers(-8, -2, (N, G))).astype(np.float16)
+    xh = rng.integers(-8, 9, (M, K)).astype(np.float16)
+    y = qg.gemm_w4a16_g128(to_dev(xh), to_dev(packed), to_dev(sc), to_dev(zz),
+                           out_dtype=torch.float32)
+    np.testing.assert_array_equal(out_f64(y), oracle.gemm_w4a16_g128(xh.astype(np.float64),
+                                                                     packed, sc, zz))
+
+
+def test_gemm_empty_shapes():
+    xq = torch.zeros((0, 64), dtype=torch.int8, device="cuda")
+    wq = torch.zeros((32, 64), dtype=torch.int8, device="cuda")
+    y = qg.gemm_w8a8(xq, torch.zeros(0, device="cuda"), wq, torch.zeros(32, device="cuda"))
+    assert y.shape == (0, 32)

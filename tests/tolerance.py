@@ -1,0 +1,57 @@
+"""Output tolerances for comparing GPU results with the oracle's y_exact.
+
+Integer results (codes, scales, zero points, int32 accumulators) are compared
+bit for bit elsewhere; this module covers the floating-point epilogues.
+
+  fp32 outputs:       |y - y_exact| <= 1e-5 |y_exact|
+  bf16 / fp16 outputs:|y - y_exact| <= 1 ulp of the output format at y_exact
+A result that sums terms of both signs in binary32 (the group sums of W4A8
+and W4A16) may lose relative accuracy near zero; such an output also passes if
+  |y - y_exact| <= ulp_out(y_exact) + n * 2^-24 * B,
+with B the sum of the magnitudes of the terms and n the number of binary32
+roundings that can touch the sum (derived per kernel in the test).  The
+tests report how many outputs needed that floor.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_FMT = {"bf16": (8, -126), "f16": (11, -14)}
+
+
+def ulp(y_exact: np.ndarray, fmt: str) -> np.ndarray:
+    """Spacing of `fmt` values at |y_exact| (the subnormal spacing near 0)."""
+    p, emin = _FMT[fmt]
+    a = np.abs(np.asarray(y_exact, np.float64))
+    _, e = np.frexp(a)                    # a = m 2^e, m in [0.5, 1)
+    e = np.maximum(e - 1, emin)
+    return np.ldexp(1.0, e - (p - 1))
+
+
+def check(y, y_exact, fmt: str, floor=None):
+    """Return (ok mask, number of outputs that pass only through the floor)."""
+    y = np.asarray(y, np.float64)
+    ye = np.asarray(y_exact, np.float64)
+    d = np.abs(y - ye)
+    if fmt == "f32":
+        base = d <= 1e-5 * np.abs(ye)
+        bound = 1e-5 * np.abs(ye)
+    else:
+        bound = ulp(ye, fmt)
+        base = d <= bound
+    if floor is None:
+        return base, 0
+    ok = base | (d <= bound + floor)
+    return ok, int(np.count_nonzero(ok & ~base))
+
+
+def assert_close(y, y_exact, fmt: str, floor=None, what: str = ""):
+    ok, via_floor = check(y, y_exact, fmt, floor)
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        yy = np.asarray(y, np.float64)
+        ye = np.asarray(y_exact, np.float64)
+        rows = [(tuple(i), float(yy[tuple(i)]), float(ye[tuple(i)])) for i in idx]
+        raise AssertionError(f"{what}: {np.count_nonzero(~ok)} of {ok.size} outputs out of "
+                             f"tolerance ({fmt}); first: {rows}")
+    return via_floor
