@@ -55,10 +55,84 @@ __device__ __forceinline__ v4i unpack_bf16(u32 w, float zb /* 2^23 + z */) {
   return r;
 }
 
+template <int MT, int NT, int U>
+struct W4A16Batch {
+  v4i wv[U][NT], xa[U][MT][4];
+  uint16_t sbits[U][NT], zbits[U][NT];
+};
+
+template <int MT, int NT, int U>
+__device__ __forceinline__ void w4a16_load(W4A16Batch<MT, NT, U>& bt, int g0, int ge, rsrc_t wr,
+                                           const u32 (&woff)[NT], rsrc_t sr, rsrc_t zr,
+                                           const u32 (&soff)[NT], rsrc_t xr,
+                                           const u32 (&xoff)[MT]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int g = g0 + u;
+    const bool gin = g < ge;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      bt.wv[u][t] = bld16(wr, gin ? woff[t] + 64 * g : kOOB);
+      bt.sbits[u][t] = bld2(sr, gin ? soff[t] + 2 * g : kOOB);
+      bt.zbits[u][t] = bld2(zr, gin ? soff[t] + 2 * g : kOOB);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) bt.xa[u][mt][h] = bld16(xr, gin ? xoff[mt] + 256 * g + 16 * h : kOOB);
+  }
+  // keep the whole batch of loads ahead of the multiplies that follow
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MT, int NT, int U, int XDT>
+__device__ __forceinline__ void w4a16_mma(const W4A16Batch<MT, NT, U>& bt, int g0, int ge,
+                                          v4f (&yacc)[MT][NT]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {   // groups >= ge hold zeros and add zero
+    v4i a[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) a[mt][h] = shuffle_halves(bt.xa[u][mt][h]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float zf = f16_bits_to_f32(bt.zbits[u][t]);
+      const float s = f16_bits_to_f32(bt.sbits[u][t]);
+      v4i b[4];
+      if constexpr (XDT == F16) {
+        const u32 zh = f32_to_f16_bits(1024.f + zf);
+        const u32 zz = zh | (zh << 16);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) b[h] = unpack_f16((u32)bt.wv[u][t][h], zz);
+      } else {
+        const float zb = 8388608.f + zf;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) b[h] = unpack_bf16((u32)bt.wv[u][t][h], zb);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        v4f p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          if constexpr (XDT == F16)
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a[mt][h]),
+                                                       __builtin_bit_cast(v8h, b[h]), p, 0, 0, 0);
+          else
+            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[mt][h]),
+                                                        __builtin_bit_cast(v8bf, b[h]), p, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yacc[mt][t][i] = __builtin_fmaf(s, p[i], yacc[mt][t][i]);
+      }
+    }
+  }
+}
+
 // Workgroup = WAVES waves owning 16*NT columns and 16*MT rows; groups split
-// across waves.  Lane l: row/column (l & 15); in a group it loads words
-// 4j..4j+3 of its column (j = l >> 4), MFMA h (0..3) takes word 4j+h, i.e.
-// k = 32j + 8h + 0..7.
+// across waves, walked in double-buffered batches of U groups.  Lane l:
+// row/column (l & 15); in a group it loads words 4j..4j+3 of its column
+// (j = l >> 4), MFMA h (0..3) takes word 4j+h, i.e. k = 32j + 8h + 0..7.
 template <int MT, int NT, int WAVES, int U, int XDT, typename OutT>
 __global__ __launch_bounds__(64 * WAVES) void k_w4a16(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ wq,
@@ -79,14 +153,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16(
     ncol[t] = n_base + 16 * t + r;
     nok[t] = ncol[t] < N;
   }
-  bool mok[MT];
-  const uint16_t* xrow[MT];
+  // buffer resources cover this workgroup's weight columns and token rows;
+  // columns past N and rows past M read as zeros
+  const int rows_n = min(16 * NT, N - n_base), rows_m = min(16 * MT, M - m_base);
+  const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * Kw, (u32)(rows_n * Kw * 4));
+  const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  const rsrc_t xr = make_rsrc(x + (int64_t)m_base * K, (u32)(rows_m * K * 2));
+  u32 woff[NT], soff[NT], xoff[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = m_base + 16 * mt + r;
-    mok[mt] = m < M;
-    xrow[mt] = x + (int64_t)(mok[mt] ? m : 0) * K + 32 * j;
+  for (int t = 0; t < NT; ++t) {
+    woff[t] = (u32)(((16 * t + r) * Kw + 4 * j) * 4);
+    soff[t] = (u32)((16 * t + r) * G * 2);
   }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) xoff[mt] = (u32)(((16 * mt + r) * K + 32 * j) * 2);
 
   v4f yacc[MT][NT];
 #pragma unroll
@@ -94,70 +175,17 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16(
 #pragma unroll
     for (int t = 0; t < NT; ++t) yacc[mt][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int g0 = gb; g0 < ge; g0 += U) {
-    v4i wv[U][NT], xa[U][MT][4];
-    uint16_t sbits[U][NT], zbits[U][NT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int g = g0 + u;
-      const bool gin = g < ge;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bool ok = gin && nok[t];
-        const int64_t n = ok ? ncol[t] : 0;
-        wv[u][t] = ok ? ld16_stream(wq + n * Kw + 16 * g + 4 * j) : v4i{0, 0, 0, 0};
-        sbits[u][t] = ok ? wscale[n * G + g] : (uint16_t)0;
-        zbits[u][t] = ok ? wzero[n * G + g] : (uint16_t)0;
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bool ok = gin && mok[mt];
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          xa[u][mt][h] = ok ? ld16(xrow[mt] + 128 * g + 8 * h) : v4i{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (g0 + u >= ge) break;
-      v4i a[MT][4];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int h = 0; h < 4; ++h) a[mt][h] = shuffle_halves(xa[u][mt][h]);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float zf = f16_bits_to_f32(zbits[u][t]);
-        const float s = f16_bits_to_f32(sbits[u][t]);
-        v4i b[4];
-        if constexpr (XDT == F16) {
-          const u32 zh = f32_to_f16_bits(1024.f + zf);
-          const u32 zz = zh | (zh << 16);
-#pragma unroll
-          for (int h = 0; h < 4; ++h) b[h] = unpack_f16((u32)wv[u][t][h], zz);
-        } else {
-          const float zb = 8388608.f + zf;
-#pragma unroll
-          for (int h = 0; h < 4; ++h) b[h] = unpack_bf16((u32)wv[u][t][h], zb);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          v4f p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            if constexpr (XDT == F16)
-              p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a[mt][h]),
-                                                         __builtin_bit_cast(v8h, b[h]), p, 0, 0, 0);
-            else
-              p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[mt][h]),
-                                                          __builtin_bit_cast(v8bf, b[h]), p, 0, 0, 0);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) yacc[mt][t][i] = __builtin_fmaf(s, p[i], yacc[mt][t][i]);
-        }
-      }
-    }
+  W4A16Batch<MT, NT, U> p0, p1;
+  w4a16_load(p0, gb, ge, wr, woff, sr, zr, soff, xr, xoff);
+  // Branch-free software pipeline: groups past this wave's range read zeros
+  // (and add zero), so each batch waits only for its own loads.
+  for (int g0 = gb; g0 < ge; g0 += 2 * U) {
+    w4a16_load(p1, g0 + U, ge, wr, woff, sr, zr, soff, xr, xoff);
+    w4a16_mma<MT, NT, U, XDT>(p0, g0, ge, yacc);
+    w4a16_load(p0, g0 + 2 * U, ge, wr, woff, sr, zr, soff, xr, xoff);
+    w4a16_mma<MT, NT, U, XDT>(p1, g0 + U, ge, yacc);
   }
+
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -181,7 +209,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16(
 template <int XDT, typename OutT>
 static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
                                const uint16_t* wz, int M, int N, int K, OutT* y, hipStream_t st) {
-  constexpr int MT = 1, NT = 1, WAVES = 8, U = 4;
+  constexpr int MT = 1, NT = 1, WAVES = 8, U = 2;  // measured on MI355X
   dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
   k_w4a16<MT, NT, WAVES, U, XDT, OutT><<<grid, dim3(64 * WAVES), 0, st>>>(x, wq, ws, wz, M, N, K, y);
   return hipGetLastError();

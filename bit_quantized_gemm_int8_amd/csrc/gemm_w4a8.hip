@@ -47,9 +47,90 @@ __device__ __forceinline__ void store_out(OutT* y, int64_t idx, float v) {
   y[idx] = Out<OutT>::cvt(v);
 }
 
+template <int MT, int NT, int U>
+struct W4A8Batch {
+  v4i wv[U][NT], xa[U][MT][2];
+  uint16_t sbits[U][NT], zbits[U][NT];
+};
+
+// Issue the loads of groups [g0, g0 + U) (those below ge; the rest read zeros).
+template <int MT, int NT, int U>
+__device__ __forceinline__ void w4a8_load(W4A8Batch<MT, NT, U>& bt, int g0, int ge, rsrc_t wr,
+                                          const u32 (&woff)[NT], rsrc_t sr, rsrc_t zr,
+                                          const u32 (&soff)[NT], rsrc_t xr,
+                                          const u32 (&xoff)[MT]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int g = g0 + u;
+    const bool gin = g < ge;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      bt.wv[u][t] = bld16(wr, gin ? woff[t] + 64 * g : kOOB);
+      bt.sbits[u][t] = bld2(sr, gin ? soff[t] + 2 * g : kOOB);
+      bt.zbits[u][t] = bld2(zr, gin ? soff[t] + 2 * g : kOOB);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      bt.xa[u][mt][0] = bld16(xr, gin ? xoff[mt] + 128 * g : kOOB);
+      bt.xa[u][mt][1] = bld16(xr, gin ? xoff[mt] + 128 * g + 16 : kOOB);
+    }
+  }
+  // keep the whole batch of loads ahead of the multiplies that follow
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Multiply the groups of a batch; float mode accumulates s * acc into yacc,
+// int32 mode writes the per-group accumulators.
+template <int MT, int NT, int U, typename OutT>
+__device__ __forceinline__ void w4a8_mma(const W4A8Batch<MT, NT, U>& bt, int g0, int ge, int G,
+                                         int N, int M, int m_base, int j, const int (&ncol)[NT],
+                                         const bool (&nok)[NT], v4f (&yacc)[MT][NT],
+                                         OutT* __restrict__ y) {
+  constexpr bool kI32 = __is_same(OutT, int32_t);
+  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int g = g0 + u;          // g >= ge: zero operands, zero contribution
+    v4i a[MT][2], rs[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      a[mt][0] = shuffle_act16(bt.xa[u][mt][0]);
+      a[mt][1] = shuffle_act16(bt.xa[u][mt][1]);
+      rs[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][0], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+      rs[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][1], ones, rs[mt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const v4i b0 = unpack_u4_pair((u32)bt.wv[u][t][0], (u32)bt.wv[u][t][1]);
+      const v4i b1 = unpack_u4_pair((u32)bt.wv[u][t][2], (u32)bt.wv[u][t][3]);
+      const int z = (int)f16_bits_to_f32(bt.zbits[u][t]);
+      const float s = f16_bits_to_f32(bt.sbits[u][t]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        v4i acc = -z * rs[mt];
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][0], b0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][1], b1, acc, 0, 0, 0);
+        if constexpr (kI32) {
+          if (nok[t] && g < ge) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = m_base + 16 * mt + 4 * j + i;
+              if (m < M) y[((int64_t)m * G + g) * N + ncol[t]] = acc[i];
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) yacc[mt][t][i] = __builtin_fmaf(s, (float)acc[i], yacc[mt][t][i]);
+        }
+      }
+    }
+  }
+}
+
 // Workgroup = WAVES waves owning 16*NT output columns and 16*MT rows; the
-// groups of K are split across the waves (contiguous runs), U groups issued
-// per batch.  Lane l: MFMA row/column (l & 15); within a group, words
+// groups of K are split across the waves (contiguous runs), walked in batches
+// of U groups with the next batch's loads issued before the current batch is
+// multiplied.  Lane l: MFMA row/column (l & 15); within a group, words
 // 4j..4j+3 of its column with j = l >> 4 (one 16-byte load), of which MFMA h
 // takes words 4j+2h and 4j+2h+1 (k = 32j + 16h + 0..15).
 template <int MT, int NT, int WAVES, int U, typename OutT>
@@ -73,15 +154,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8(
     ncol[t] = n_base + 16 * t + r;
     nok[t] = ncol[t] < N;
   }
-  bool mok[MT];
-  const int8_t* xrow[MT];
+  // buffer resources cover this workgroup's weight columns and token rows;
+  // columns past N and rows past M read as zeros
+  const int rows_n = min(16 * NT, N - n_base), rows_m = min(16 * MT, M - m_base);
+  const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * Kw, (u32)(rows_n * Kw * 4));
+  const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  const rsrc_t xr = make_rsrc(xq + (int64_t)m_base * K, (u32)(rows_m * K));
+  u32 woff[NT], soff[NT], xoff[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = m_base + 16 * mt + r;
-    mok[mt] = m < M;
-    xrow[mt] = xq + (int64_t)(mok[mt] ? m : 0) * K + 32 * j;
+  for (int t = 0; t < NT; ++t) {
+    woff[t] = (u32)(((16 * t + r) * Kw + 4 * j) * 4);
+    soff[t] = (u32)((16 * t + r) * G * 2);
   }
-  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) xoff[mt] = (u32)((16 * mt + r) * K + 32 * j);
 
   v4f yacc[MT][NT];
 #pragma unroll
@@ -89,68 +176,17 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8(
 #pragma unroll
     for (int t = 0; t < NT; ++t) yacc[mt][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int g0 = gb; g0 < ge; g0 += U) {
-    v4i wv[U][NT], xa[U][MT][2];
-    uint16_t sbits[U][NT], zbits[U][NT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int g = g0 + u;
-      const bool gin = g < ge;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bool ok = gin && nok[t];
-        const int64_t n = ok ? ncol[t] : 0;
-        wv[u][t] = ok ? ld16_stream(wq + n * Kw + 16 * g + 4 * j) : v4i{0, 0, 0, 0};
-        sbits[u][t] = ok ? wscale[n * G + g] : (uint16_t)0;
-        zbits[u][t] = ok ? wzero[n * G + g] : (uint16_t)0;
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bool ok = gin && mok[mt];
-        xa[u][mt][0] = ok ? ld16(xrow[mt] + 128 * g) : v4i{0, 0, 0, 0};
-        xa[u][mt][1] = ok ? ld16(xrow[mt] + 128 * g + 16) : v4i{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int g = g0 + u;
-      if (g >= ge) break;
-      v4i a[MT][2], rs[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        a[mt][0] = shuffle_act16(xa[u][mt][0]);
-        a[mt][1] = shuffle_act16(xa[u][mt][1]);
-        rs[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][0], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
-        rs[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][1], ones, rs[mt], 0, 0, 0);
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const v4i b0 = unpack_u4_pair((u32)wv[u][t][0], (u32)wv[u][t][1]);
-        const v4i b1 = unpack_u4_pair((u32)wv[u][t][2], (u32)wv[u][t][3]);
-        const int z = (int)f16_bits_to_f32(zbits[u][t]);
-        const float s = f16_bits_to_f32(sbits[u][t]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          v4i acc = -z * rs[mt];
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][0], b0, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][1], b1, acc, 0, 0, 0);
-          if constexpr (kI32) {
-            // test output: per-group accumulators y[m][g][n]
-            if (nok[t]) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int m = m_base + 16 * mt + 4 * j + i;
-                if (m < M) y[((int64_t)m * G + g) * N + ncol[t]] = acc[i];
-              }
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) yacc[mt][t][i] = __builtin_fmaf(s, (float)acc[i], yacc[mt][t][i]);
-          }
-        }
-      }
-    }
+  W4A8Batch<MT, NT, U> p0, p1;
+  w4a8_load(p0, gb, ge, wr, woff, sr, zr, soff, xr, xoff);
+  // Branch-free software pipeline: groups past this wave's range read zeros
+  // (and add zero), so each batch waits only for its own loads.
+  for (int g0 = gb; g0 < ge; g0 += 2 * U) {
+    w4a8_load(p1, g0 + U, ge, wr, woff, sr, zr, soff, xr, xoff);
+    w4a8_mma(p0, g0, ge, G, N, M, m_base, j, ncol, nok, yacc, y);
+    w4a8_load(p0, g0 + 2 * U, ge, wr, woff, sr, zr, soff, xr, xoff);
+    w4a8_mma(p1, g0 + U, ge, G, N, M, m_base, j, ncol, nok, yacc, y);
   }
+
   if constexpr (!kI32) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -177,7 +213,7 @@ template <typename OutT>
 static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* wq,
                               const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
                               hipStream_t st) {
-  constexpr int MT = 1, NT = 1, WAVES = 8, U = 4;
+  constexpr int MT = 1, NT = 1, WAVES = 8, U = 2;  // measured on MI355X
   dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
   k_w4a8<MT, NT, WAVES, U, OutT><<<grid, dim3(64 * WAVES), 0, st>>>(xq, xs, wq, ws, wz, M, N, K, y);
   return hipGetLastError();

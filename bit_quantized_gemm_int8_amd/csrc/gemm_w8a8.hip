@@ -6,12 +6,13 @@
 // Two kernels:
 //  * small M (decode, M <= 64): the weight stream is the whole cost.  Every
 //    weight byte is used by at most 64 rows once, so weights go straight from
-//    HBM into MFMA operand registers (16-byte streaming loads, many in flight
-//    per lane); the K loop is split across the waves of a workgroup and the
-//    int32 partials meet in LDS (exact, order-free).
-//  * large M (prefill): 256x256 output tiles, K in 64-byte steps staged in LDS
-//    (double-buffered, XOR-swizzled 16-byte chunks), 4 waves each owning a
-//    128x128 sub-tile of 32x32x32 int8 MFMAs.
+//    HBM into MFMA operand registers (16-byte buffer loads, two batches in
+//    flight per lane); the K loop is split across the waves of a workgroup and
+//    the int32 partials meet in LDS (exact, order-free).
+//  * large M (prefill): 256x256 output tiles, K in 128-byte stages brought
+//    into LDS by buffer-to-LDS DMA (two alternating stage buffers, XOR-swizzled
+//    16-byte chunks), 4 waves each owning a 128x128 sub-tile of 32x32x32 int8
+//    MFMAs.
 #include "qg_device.hpp"
 #include "qg_launch.hpp"
 
@@ -31,8 +32,43 @@ __device__ __forceinline__ int32_t w8a8_epilogue<int32_t>(int acc, float, float)
 // 16*MT rows.  Lane l of a wave feeds MFMA row/column (l & 15) and the 16-byte
 // k-slice (l >> 4) of each 64-deep step, from memory in the same order for
 // both operands, so the int8 products pair up whatever order the matrix core
-// sums them in.
+// sums them in.  Each wave walks its share of K in batches of U steps and
+// keeps two batches of loads in flight (the next batch is issued before the
+// current one is multiplied).
 // ---------------------------------------------------------------------------
+template <int MT, int NT, int U>
+struct SmallMBatch {
+  v4i b[U][NT], a[U][MT];
+};
+
+template <int MT, int NT, int U>
+__device__ __forceinline__ void small_m_load(SmallMBatch<MT, NT, U>& bt, int s0, int se, int K,
+                                             int kq, rsrc_t wr, const u32 (&woff)[NT], rsrc_t xr,
+                                             const u32 (&xoff)[MT]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k = (s0 + u) * 64;
+    const bool kin = (s0 + u < se) && (k + kq < K);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) bt.b[u][t] = bld16(wr, kin ? woff[t] + k : kOOB);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) bt.a[u][mt] = bld16(xr, kin ? xoff[mt] + k : kOOB);
+  }
+  // keep the whole batch of loads ahead of the multiplies that follow
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MT, int NT, int U>
+__device__ __forceinline__ void small_m_mma(const SmallMBatch<MT, NT, U>& bt, v4i (&acc)[MT][NT]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[mt][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bt.a[u][mt], bt.b[u][t], acc[mt][t], 0, 0, 0);
+}
+
 template <int MT, int NT, int WAVES, int U, typename OutT>
 __global__ __launch_bounds__(64 * WAVES) void k_w8a8_small_m(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, const int8_t* __restrict__ wq,
@@ -46,22 +82,16 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_small_m(
   const int sb = (int)((int64_t)steps * wave / WAVES);
   const int se = (int)((int64_t)steps * (wave + 1) / WAVES);
 
-  const int8_t* wrow[NT];
-  bool nok[NT];
+  // buffer resources cover exactly this workgroup's weight rows and token
+  // rows; rows past N or M read as zeros
+  const int rows_n = min(16 * NT, N - n_base), rows_m = min(16 * MT, M - m_base);
+  const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * K, (u32)(rows_n * K));
+  const rsrc_t xr = make_rsrc(xq + (int64_t)m_base * K, (u32)(rows_m * K));
+  u32 woff[NT], xoff[MT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int n = n_base + 16 * t + r;
-    nok[t] = n < N;
-    wrow[t] = wq + (int64_t)(nok[t] ? n : 0) * K + kq;
-  }
-  const int8_t* xrow[MT];
-  bool mok[MT];
+  for (int t = 0; t < NT; ++t) woff[t] = (u32)((16 * t + r) * K + kq);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = m_base + 16 * mt + r;
-    mok[mt] = m < M;
-    xrow[mt] = xq + (int64_t)(mok[mt] ? m : 0) * K + kq;
-  }
+  for (int mt = 0; mt < MT; ++mt) xoff[mt] = (u32)((16 * mt + r) * K + kq);
 
   v4i acc[MT][NT];
 #pragma unroll
@@ -69,26 +99,16 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_small_m(
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[mt][t] = v4i{0, 0, 0, 0};
 
-  for (int s0 = sb; s0 < se; s0 += U) {
-    v4i b[U][NT], a[U][MT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = (s0 + u) * 64;
-      const bool kin = (s0 + u < se) && (k + kq < K);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        b[u][t] = (kin && nok[t]) ? ld16_stream(wrow[t] + k) : v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        a[u][mt] = (kin && mok[mt]) ? ld16(xrow[mt] + k) : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[mt][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][mt], b[u][t], acc[mt][t], 0, 0, 0);
+  // Branch-free software pipeline: loads past this wave's range read zeros
+  // (and multiply to zero), so the outstanding-load count is the same on
+  // every path and each batch waits only for its own loads.
+  SmallMBatch<MT, NT, U> p0, p1;
+  small_m_load(p0, sb, se, K, kq, wr, woff, xr, xoff);
+  for (int s0 = sb; s0 < se; s0 += 2 * U) {
+    small_m_load(p1, s0 + U, se, K, kq, wr, woff, xr, xoff);
+    small_m_mma(p0, acc);
+    small_m_load(p0, s0 + 2 * U, se, K, kq, wr, woff, xr, xoff);
+    small_m_mma(p1, acc);
   }
 
 #pragma unroll
@@ -115,24 +135,144 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_small_m(
 }
 
 // ---------------------------------------------------------------------------
-// Large-M kernel: 256x256x64 tiles, 4 waves (2x2), 32x32x32 int8 MFMAs.
-// LDS holds, per stage, the A tile [256 rows][64 k] then the B tile; row r's
-// 16-byte chunk c sits at r*64 + 16*(c ^ ((r >> 1) & 3)) so that the eight
-// rows a group of lanes reads at once land in eight different bank groups.
+// Large-M kernel: 256x256 output tiles, K in 128-byte stages, 4 waves (2x2),
+// each wave a 128x128 sub-tile of 32x32x32 int8 MFMAs (256 int32
+// accumulators per lane, held in the accumulation registers).
+//
+// Operands reach LDS by buffer-load-to-LDS DMA (no register staging): per
+// stage each wave issues 16 one-kilobyte DMA loads, each 8 rows x 128 bytes
+// (whole cache lines).  Two 64 KB stage buffers alternate: the DMA of stage
+// k+1 runs while stage k is multiplied.  Rows past M/N and bytes past K come
+// back as zeros from the buffer resources' range check.
+// LDS layout of a stage: A tile [256 rows][128 B] then B tile; row r's
+// 16-byte chunk c sits at r*128 + 16*(c ^ f(r)), f(r) = (r >> 1) & 7, so 16
+// consecutive rows reading the same chunk hit 16 different 16-byte bank
+// groups.  The DMA writes lane l's 16 bytes to slot l of the kilobyte, so the
+// swizzle is applied by choosing which chunk each lane fetches.
 // ---------------------------------------------------------------------------
-constexpr int TBM = 256, TBN = 256, TBK = 64;
+constexpr int TBM = 256, TBN = 256, TBK = 128;
+constexpr int kStageBytes = (TBM + TBN) * TBK;   // 64 KB
 
-__device__ __forceinline__ int swz(int row, int ch) { return row * TBK + ((ch ^ ((row >> 1) & 3)) << 4); }
+__shared__ __attribute__((aligned(16))) int8_t g_stage0[kStageBytes];
+__shared__ __attribute__((aligned(16))) int8_t g_stage1[kStageBytes];
 
-template <typename OutT>
-__global__ __launch_bounds__(256) void k_w8a8_tiled(const int8_t* __restrict__ xq,
-                                                    const float* __restrict__ xs,
-                                                    const int8_t* __restrict__ wq,
-                                                    const float* __restrict__ ws, int M, int N,
-                                                    int K, OutT* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) int8_t smem[2][(TBM + TBN) * TBK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+// gfx950 LDS: 64 banks x 4 bytes; a 16-byte-per-lane read serves 16 lanes
+// per cycle.  With 128-byte rows, rows r and r+1 share a 256-byte bank row, so
+// 16 consecutive rows reading the same chunk are conflict-free when the 8 rows
+// of each parity get 8 different chunk slots: f(r) = (r >> 1) & 7.
+__device__ __forceinline__ int swz_f(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int ch) { return row * TBK + ((ch ^ swz_f(row)) << 4); }
+
+#define QG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// DMA of one stage, spread over the multiply of the previous stage.  The
+// stage is 64 one-kilobyte loads; with NW waves each issues 64/NW of them.
+// Load q covers rows 8q..8q+7 of A (q < 32) or B (q >= 32); lane l fetches row
+// 8q + (l >> 3), chunk (l & 7) ^ f(row).  f(row) takes bits 1-2 from the row
+// within the 8-row block and bit 3 from the block's parity, so each lane
+// needs two byte offsets (even and odd blocks); the row step is a scalar
+// offset.
+template <int NW>
+struct PrefillDma {
+  int8_t* buf;
+  rsrc_t ar, br;
+  u32 voff[2];
+  int wave;
+  __device__ __forceinline__ void issue(int i, int K) const {
+    const int q = wave * (64 / NW) + i;
+    int8_t* dst = buf + (q < 32 ? 0 : TBM * TBK) + (q & 31) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 32 ? ar : br, QG_LDS(dst), 16, voff[q & 1],
+                                             (u32)(8 * (q & 31) * K), 0, 0);
+  }
+};
+
+template <int NW>
+__device__ __forceinline__ PrefillDma<NW> prefill_dma_setup(int8_t* buf, int kt, int K, rsrc_t ar,
+                                                            rsrc_t br, int wave, int lane) {
+  const int row_local = lane >> 3, slot = lane & 7;
+  PrefillDma<NW> d{buf, ar, br, {0u, 0u}, wave};
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int k = kt * TBK + 16 * (slot ^ swz_f(8 * par + row_local));
+    d.voff[par] = k < K ? (u32)(row_local * K + k) : kOOB;
+  }
+  return d;
+}
+
+template <int NW>
+__device__ __forceinline__ void prefill_dma(int8_t* buf, int kt, int K, rsrc_t ar, rsrc_t br,
+                                            int wave, int lane) {
+  const PrefillDma<NW> d = prefill_dma_setup<NW>(buf, kt, K, ar, br, wave, lane);
+#pragma unroll
+  for (int i = 0; i < 64 / NW; ++i) d.issue(i, K);
+}
+
+// Wave tile: 4 row tiles (128 rows) x WJ column tiles (32*WJ columns) of
+// 32x32 MFMAs; WJ = 4 with 4 waves (2x2), WJ = 2 with 8 waves (2x4).
+template <int WJ>
+__device__ __forceinline__ void prefill_frag(const int8_t* buf, int ks, int row_a, int row_b,
+                                             int lane, v4i (&af)[4], v4i (&bf)[WJ]) {
+  const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    af[i] = *reinterpret_cast<const v4i*>(&buf[swz(row_a + i * 32 + (lane & 31), ch)]);
+#pragma unroll
+  for (int j = 0; j < WJ; ++j)
+    bf[j] = *reinterpret_cast<const v4i*>(&buf[TBM * TBK + swz(row_b + j * 32 + (lane & 31), ch)]);
+}
+
+// Multiply one stage: 4 sub-steps of 32 k; the fragments of sub-step ks+1 are
+// read from LDS while the MFMAs of sub-step ks run (two fragment sets).  The
+// wave's DMA loads of the next stage are slotted in between MFMAs over the
+// first half of the stage, so the wave never stalls on a burst of loads and
+// the second half covers their latency.
+template <int NW, int WJ>
+__device__ __forceinline__ void prefill_mma(const int8_t* buf, int row_a, int row_b, int lane,
+                                            v16i (&acc)[4][WJ], const PrefillDma<NW>& next,
+                                            int K) {
+  constexpr int kLoads = 64 / NW;              // DMA loads per wave per stage
+  constexpr int kSlots = 2 * 4 * WJ;           // MFMAs in the first two sub-steps
+  constexpr int kEvery = kSlots / kLoads;
+  v4i af[2][4], bf[2][WJ];
+  prefill_frag<WJ>(buf, 0, row_a, row_b, lane, af[0], bf[0]);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks < 3) prefill_frag<WJ>(buf, ks + 1, row_a, row_b, lane, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < WJ; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks & 1][i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
+        const int slot = (ks * 4 + i) * WJ + j;
+        if (slot < kSlots && (slot % kEvery) == kEvery - 1) next.issue(slot / kEvery, K);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Wait until this wave's DMA loads have landed, then meet the other waves:
+// after the barrier the whole stage is in LDS and every wave has finished
+// reading the other buffer, which the next DMA overwrites.  One asm statement
+// with a memory clobber, so no LDS access moves across it.
+__device__ __forceinline__ void prefill_stage_sync() {
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int NW, typename OutT>
+__global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict__ xq,
+                                                        const float* __restrict__ xs,
+                                                        const int8_t* __restrict__ wq,
+                                                        const float* __restrict__ ws, int M,
+                                                        int N, int K, OutT* __restrict__ y) {
+  constexpr int WJ = NW == 4 ? 4 : 2;           // column tiles per wave
+  constexpr int WAVES_N = NW / 2;               // waves across the 256 columns
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: the DMA's LDS address (M0) and buffer resource
+  // must be wave-uniform values
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int row_a = wm * 128, row_b = wn * 32 * WJ;
 
   // Tile order: the hardware hands consecutive workgroups to the 8 XCDs in
   // turn; renumber so each XCD walks a contiguous run of tiles, and walk
@@ -144,8 +284,7 @@ __global__ __launch_bounds__(256) void k_w8a8_tiled(const int8_t* __restrict__ x
   {
     const int per = total / 8, rem = total % 8;   // xcd x gets per + (x < rem) tiles
     const int xcd = bid % 8, idx = bid / 8;
-    if (idx < per + (xcd < rem ? 1 : 0))
-      bid = xcd * per + (xcd < rem ? xcd : rem) + idx;
+    bid = xcd * per + (xcd < rem ? xcd : rem) + idx;
   }
   constexpr int GROUP = 4;
   const int group = bid / (GROUP * tiles_n);
@@ -155,97 +294,66 @@ __global__ __launch_bounds__(256) void k_w8a8_tiled(const int8_t* __restrict__ x
   const int tn = (bid % (GROUP * tiles_n)) / gsize;
   const int m0 = tm * TBM, n0 = tn * TBN;
 
-  v4i ra[4], rb[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c >> 2, k = k0 + (c & 3) * 16;
-      const int m = m0 + row, n = n0 + row;
-      ra[i] = (m < M && k < K) ? ld16(xq + (int64_t)m * K + k) : v4i{0, 0, 0, 0};
-      rb[i] = (n < N && k < K) ? ld16(wq + (int64_t)n * K + k) : v4i{0, 0, 0, 0};
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c >> 2, off = swz(row, c & 3);
-      *reinterpret_cast<v4i*>(&smem[buf][off]) = ra[i];
-      *reinterpret_cast<v4i*>(&smem[buf][TBM * TBK + off]) = rb[i];
-    }
-  };
+  const rsrc_t ar = make_rsrc(xq + (int64_t)m0 * K, (u32)(min(TBM, M - m0) * K));
+  const rsrc_t br = make_rsrc(wq + (int64_t)n0 * K, (u32)(min(TBN, N - n0) * K));
 
-  v16i acc[4][4];
+  v16i acc[4][WJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+    for (int j = 0; j < WJ; ++j) acc[i][j] = v16i{};
 
   const int nk = (K + TBK - 1) / TBK;
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * TBK);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = ks * 2 + (lane >> 5);
-      v4i af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const v4i*>(&smem[buf][swz(row, ch)]);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wn * 128 + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const v4i*>(&smem[buf][TBM * TBK + swz(row, ch)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) swrite(buf ^ 1);
-    __syncthreads();
+  prefill_dma<NW>(g_stage0, 0, K, ar, br, wave, lane);
+  for (int kt = 0; kt < nk; kt += 2) {
+    // stages past nk are loaded as zeros and add nothing; multiplying them
+    // (at most one extra stage, when nk is odd) keeps the loop branch-free
+    prefill_stage_sync();
+    prefill_mma<NW, WJ>(g_stage0, row_a, row_b, lane, acc,
+                        prefill_dma_setup<NW>(g_stage1, kt + 1, K, ar, br, wave, lane), K);
+    prefill_stage_sync();
+    prefill_mma<NW, WJ>(g_stage1, row_a, row_b, lane, acc,
+                        prefill_dma_setup<NW>(g_stage0, kt + 2, K, ar, br, wave, lane), K);
   }
 
   // 32x32 accumulator layout: lane l holds column (l & 31); register e holds
   // row 8*(e >> 2) + 4*(l >> 5) + (e & 3).
   const int col_in = lane & 31, rsub = 4 * (lane >> 5);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 128 + j * 32 + col_in;
+  for (int j = 0; j < WJ; ++j) {
+    const int n = n0 + row_b + j * 32 + col_in;
     if (n >= N) continue;
     const float sw = ws ? ws[n] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + rsub + (e & 3);
+        const int m = m0 + row_a + i * 32 + 8 * (e >> 2) + rsub + (e & 3);
         if (m < M) y[(int64_t)m * N + n] = w8a8_epilogue<OutT>(acc[i][j][e], xs ? xs[m] : 0.f, sw);
       }
     }
   }
 }
 
+constexpr int kPrefillWaves = 8;
+
 template <typename OutT>
 static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* wq,
                               const float* ws, int M, int N, int K, OutT* y, hipStream_t st) {
   if (M <= 64) {
-    constexpr int WAVES = 8, NT = 1, U = 4;
+    // shapes picked by measurement on MI355X (decode, K = 4096, N = 11008)
+    constexpr int WAVES = 4, NT = 1;
     dim3 block(64 * WAVES);
     const unsigned gx = (unsigned)((N + 16 * NT - 1) / (16 * NT));
     if (M <= 16)
-      k_w8a8_small_m<1, NT, WAVES, U, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
+      k_w8a8_small_m<1, NT, WAVES, 8, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
     else if (M <= 32)
-      k_w8a8_small_m<2, NT, WAVES, U, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
+      k_w8a8_small_m<2, NT, WAVES, 4, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
     else
-      k_w8a8_small_m<4, NT, WAVES, U, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
+      k_w8a8_small_m<4, NT, WAVES, 2, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
   } else {
     const int tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
-    k_w8a8_tiled<OutT><<<dim3((unsigned)tiles), dim3(256), 0, st>>>(xq, xs, wq, ws, M, N, K, y);
+    k_w8a8_tiled<kPrefillWaves, OutT><<<dim3((unsigned)tiles), dim3(64 * kPrefillWaves), 0, st>>>(xq, xs, wq, ws, M, N, K, y);
   }
   return hipGetLastError();
 }

@@ -27,6 +27,24 @@ __device__ __forceinline__ v4i ld16_stream(const void* p) {
 
 __device__ __forceinline__ void st16(void* p, v4i v) { *reinterpret_cast<v4i*>(p) = v; }
 
+// ---- raw buffer loads --------------------------------------------------------
+// A buffer resource covers [base, base + bytes); a load whose offset lies past
+// the end returns zeros instead of touching memory, so edge tiles and masked
+// lanes need no branch: they pass kOOB (or any offset >= bytes).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr u32 kOOB = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ v4i bld16(rsrc_t r, u32 off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint16_t bld2(rsrc_t r, u32 off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
 // ---- number formats ----------------------------------------------------------
 
 __device__ __forceinline__ float bf16_bits_to_f32(u32 h) { return __uint_as_float(h << 16); }
