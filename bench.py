@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain device copy of 512 MiB (counter calibration)")
+    ap.add_argument("--ingest-counters", metavar="DIR",
+                    help="summarise rocprofv3 output in DIR/{stats,fetch,write} into profiles/")
     return ap.parse_args()
 
 
@@ -231,15 +233,15 @@ def run_workload(wl, steps, warmup, traffic_db):
 
 
 def copy_calibration():
+    """A plain elementwise kernel that reads and writes COPY_BYTES each: the
+    known-size reference that HBM byte counters are scaled by."""
     import torch
-    n = 512 * 2 ** 20
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
-    a.fill_(1)
     for _ in range(3):
-        b.copy_(a)
+        torch.add(a, 1, out=b)
     torch.cuda.synchronize()
-    print(f"[bench] copy calibration: 3 copies of {n} bytes", file=sys.stderr, flush=True)
+    print(f"[bench] copy calibration: 3 passes over {COPY_BYTES} bytes", file=sys.stderr, flush=True)
 
 
 def cpu_baseline(wl, seconds):
@@ -275,8 +277,138 @@ def cpu_baseline(wl, seconds):
             "ms_per_step": round(el / n * 1e3, 2)}
 
 
+# ------------------------------------------------------------ counter ingest
+
+# demangled-name patterns of each workload's dominant kernel as bench.py runs it
+# (rocprofv3 leaves names with _Float16 mangled, hence the alternatives)
+KERNEL_OF = {
+    "w8a8_decode_ffn_up": [("k_w8a8_small_m<1,", "unsigned short>")],
+    "w8a8_tiny": [("k_w8a8_small_m<1,", "float>")],
+    "w4a8_ffn_down": [("k_w4a8<", "unsigned short>")],
+    "w4a16_qkv": [("k_w4a16<", "_Float16>"), ("k_w4a16ILi", "ELi1EDF16_E")],
+    "w8a8_prefill": [("k_w8a8_tiled<", "unsigned short>")],
+}
+COPY_BYTES = 512 * 2 ** 20
+PROFILE_COMMANDS = """\
+cd /tmp && export TMPDIR=/tmp
+rocprofv3 --kernel-trace --stats -d $OUT/pmc/stats -o run --output-format csv -- python3 $REPO/bench.py --steps 50 --warmup 5 --no-cpu
+rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc/fetch -o run --output-format csv -- python3 $REPO/bench.py --steps 10 --warmup 2 --no-cpu --copy-calib
+rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc/write -o run --output-format csv -- python3 $REPO/bench.py --steps 10 --warmup 2 --no-cpu --copy-calib
+python3 $REPO/bench.py --ingest-counters $OUT/pmc"""
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _match(name, alternatives):
+    return any(all(p in name for p in pats) for pats in alternatives)
+
+
+def ingest_counters(d):
+    """rocprofv3 CSVs -> profiles/traffic.json + per-kernel summaries.
+
+    d/stats: --kernel-trace --stats run; d/fetch: --pmc FETCH_SIZE run;
+    d/write: --pmc WRITE_SIZE run (both with --copy-calib).  FETCH_SIZE and
+    WRITE_SIZE are KiB per dispatch; each is scaled by known copy bytes over
+    what the same counter reads for the 512 MiB device copy.
+    """
+    import glob
+    from workloads import by_name
+    stats = _csv_rows(glob.glob(os.path.join(d, "stats", "*kernel_stats.csv"))[0])
+    per = {}
+    for ctr, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        rows = _csv_rows(glob.glob(os.path.join(d, sub, "*counter_collection.csv"))[0])
+        vals = {}
+        for r in rows:
+            if r["Counter_Name"] != ctr:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        # the calibration copy is the only dispatch of that size in the run
+        copy = [v for vs in vals.values() for v in vs if 0.5 < v * 1024 / COPY_BYTES < 2.0]
+        factor = (COPY_BYTES / (sum(copy) / len(copy) * 1024)) if copy else None
+        per[ctr] = (vals, factor, len(copy))
+    out, lines = {}, []
+    for wl_name, pats in KERNEL_OF.items():
+        wl = by_name(wl_name)
+        gemm_b, quant_b, ops = algorithmic(wl)
+        srow = next((r for r in stats if _match(r["Name"], pats)), None)
+        rec = {"kernel": srow["Name"].split("(")[0] if srow else None,
+               "calls": int(srow["Calls"]) if srow else 0,
+               "avg_ns": float(srow["AverageNs"]) if srow else None,
+               "algorithmic_bytes": gemm_b, "ops": ops}
+        total = 0.0
+        ok = True
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals, factor, ncopy = per[ctr]
+            v = [x for k, xs in vals.items() if _match(k, pats) for x in xs]
+            if not v or factor is None:
+                ok = False
+                continue
+            mean_kib = sum(v) / len(v)
+            rec[ctr.lower() + "_kib_mean"] = round(mean_kib, 1)
+            rec[ctr.lower() + "_copy_factor"] = round(factor, 4)
+            total += mean_kib * 1024 * factor
+        rec["bytes_per_launch"] = round(total) if ok else None
+        rec["source_sha"] = source_sha(wl.path)
+        out[wl.path + ":" + wl_name] = rec
+        lines.append(rec)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    for key, rec in out.items():
+        path, wl_name = key.split(":")
+        wl = by_name(wl_name)
+        kname = {"w8a8": "gemm_w8a8_small_m" if wl.M <= 64 else "gemm_w8a8_tiled",
+                 "w4a8": "gemm_w4a8_g128", "w4a16": "gemm_w4a16_g128"}[path]
+        fn = os.path.join(ROOT, "profiles", f"{kname}.{wl_name}.md")
+        avg = rec["avg_ns"]
+        lines = [f"# {kname} on {wl_name} (M={wl.M}, K={wl.K}, N={wl.N})", "",
+                 "rocprofv3 summary of the benchmark's dominant kernel for this workload.", "",
+                 "Commands (repository root as $REPO, an output directory as $OUT, one MI355X):", "", "```",
+                 PROFILE_COMMANDS, "```", "",
+                 "| quantity | value |", "|---|---|",
+                 f"| kernel | `{rec['kernel']}` |",
+                 f"| dispatches traced | {rec['calls']} |",
+                 f"| average duration (kernel trace) | {avg / 1e3:.3f} us |" if avg else "| average duration | n/a |",
+                 f"| algorithmic bytes per launch | {rec['algorithmic_bytes']} |",
+                 f"| algorithmic ops per launch | {rec['ops']} |"]
+        if avg:
+            lines.append(f"| algorithmic GB/s at that duration | {rec['algorithmic_bytes'] / avg:.1f} |")
+            lines.append(f"| algorithmic TOP/s at that duration | {rec['ops'] / avg / 1e3:.1f} |")
+        for ctr in ("fetch_size", "write_size"):
+            if ctr + "_kib_mean" in rec:
+                lines.append(f"| {ctr.upper()} mean (KiB per dispatch) | {rec[ctr + '_kib_mean']} |")
+                lines.append(f"| {ctr.upper()} copy-kernel scale factor | {rec[ctr + '_copy_factor']} |")
+        lines.append(f"| HBM traffic per launch (scaled FETCH + WRITE) | {rec['bytes_per_launch']} |")
+        if rec["bytes_per_launch"]:
+            lines.append(f"| traffic / algorithmic bytes | {rec['bytes_per_launch'] / rec['algorithmic_bytes']:.3f} |")
+        lines.append(f"| kernel source hash | {rec['source_sha']} |")
+        lines += ["", "The scale factor is the 512 MiB known-size elementwise copy's true bytes over",
+                  "what the same counter reported for it in the same run."]
+        with open(fn, "w") as f:
+            f.write("\n".join(lines) + "\n")
+    # every library kernel the benchmark ran, from the kernel trace
+    rows = [r for r in stats if "qg::" in r["Name"] or "_ZN2qg" in r["Name"]]
+    lines = ["# Kernel trace of the benchmark (all workloads)", "",
+             "Commands (repository root as $REPO, an output directory as $OUT, one MI355X):",
+             "", "```", PROFILE_COMMANDS.splitlines()[0], PROFILE_COMMANDS.splitlines()[1], "```", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} "
+                     f"| {float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} |")
+    with open(os.path.join(ROOT, "profiles", "kernel_trace.bench_all_workloads.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the layer shards column-parallel without collectives; see the design notes)",
