@@ -14,6 +14,7 @@
 // (1024 + q_i, 1024 + q_{i+4}); a packed fp16 subtract of (1024 + z) leaves
 // (q - z) exactly.  The activation halves are shuffled into the matching
 // [0,4,1,5,2,6,3,7] order.
+#include "qg_decode.hpp"
 #include "qg_device.hpp"
 #include "qg_launch.hpp"
 
@@ -72,7 +73,7 @@ __device__ __forceinline__ void w4a16_load(W4A16Batch<MT, NT, U>& bt, int g0, in
     const bool gin = g < ge;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      bt.wv[u][t] = bld16(wr, gin ? woff[t] + 64 * g : kOOB);
+      bt.wv[u][t] = bld16_nt(wr, gin ? woff[t] + 64 * g : kOOB);
       bt.sbits[u][t] = bld2(sr, gin ? soff[t] + 2 * g : kOOB);
       bt.zbits[u][t] = bld2(zr, gin ? soff[t] + 2 * g : kOOB);
     }
@@ -206,9 +207,148 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode kernel (M <= 16) on whole-line weight units (see qg_decode.hpp): a
+// unit is two g=128 groups of 16 weight rows.  The token rows are staged whole
+// in LDS, each 16-byte chunk already in the [0,4,1,5,2,6,3,7] order of the
+// unpacked codes, and the rows' scales and zero points next to them; wave w
+// streams its contiguous run of units in batches of UB, two batches in
+// flight.  Rows r >= MR of the MFMA read token row 0 (never stored): with one
+// token row every lane reads the same bytes, an LDS broadcast.
+// ---------------------------------------------------------------------------
+template <int MR, int WAVES, int UB, int XDT, typename OutT>
+__global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ wq,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
+    OutT* __restrict__ y) {
+  constexpr int kThreads = 64 * WAVES;
+  // LDS: MR token rows (pitch stage_pitch(2K)), then 16 x sz_pitch(G) words
+  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+  __shared__ __attribute__((aligned(16))) int8_t tiles[WAVES][kTileBytes];
+  __shared__ v4f red[WAVES][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int n_base = blockIdx.x * 16;
+  const int G = K >> 7, Kw = K >> 3, RB = Kw * 4;   // RB: packed bytes per weight row
+  const int units = (RB + kUnitBytes - 1) / kUnitBytes;
+  const int ub = (int)((int64_t)units * wave / WAVES), ue = (int)((int64_t)units * (wave + 1) / WAVES);
+  const int xpitch = stage_pitch(2 * K);
+  int8_t* xl = smem;
+  u32* szl = reinterpret_cast<u32*>(smem + MR * xpitch);
+
+  const int rows_n = min(16, N - n_base);
+  const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * Kw, (u32)(rows_n * RB));
+  const UnitLanes ul = unit_lanes(lane, RB);
+
+  v4i b0[UB][2], b1[UB][2];
+  auto load = [&](v4i (&b)[UB][2], int q0) {
+#pragma unroll
+    for (int v = 0; v < UB; ++v) unit_load(b[v], wr, ul, q0 + v, q0 + v < ue, RB);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // scales and zero points, token rows, and behind them the first weight batch
+  ScaleZeroStage<kThreads, 4> sz;
+  const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  sz.load(sr, zr, G, 0);
+  stage_rows<MR, kThreads>(xl, make_rsrc(x, (u32)(M * K * 2)), 2 * K,
+                           [](v4i v) { return shuffle_halves(v); },
+                           [&]() { load(b0, ub); });
+  sz.store(szl, G);
+  for (int c0 = 4 * kThreads; c0 < 16 * G; c0 += 4 * kThreads) {
+    sz.load(sr, zr, G, c0);
+    sz.store(szl, G);
+  }
+  lds_barrier();
+
+  const int8_t* xrow = xl + (r < MR ? r : 0) * xpitch + 64 * j;
+  const u32* szrow = szl + r * sz_pitch(G);
+  int8_t* tile = tiles[wave];
+  v4f yacc = {0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const v4i (&b)[UB][2], int q0) {
+#pragma unroll
+    for (int v = 0; v < UB; ++v) {
+      v4i f[2];
+      unit_transpose(tile, b[v], ul, f);
+      // units past this wave's run: zero codes; their scale is taken as zero
+      const bool qin = q0 + v < ue;
+      const int q = qin ? q0 + v : 0;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int g = 2 * q + s;
+        const u32 szw = qin && g < G ? szrow[g] : 0u;
+        const float sc = f16_bits_to_f32((uint16_t)(szw & 0xFFFFu));
+        const float zf = f16_bits_to_f32((uint16_t)(szw >> 16));
+        v4i bw[4];
+        if constexpr (XDT == F16) {
+          const u32 zh = f32_to_f16_bits(1024.f + zf);
+          const u32 zz = zh | (zh << 16);
+#pragma unroll
+          for (int h = 0; h < 4; ++h) bw[h] = unpack_f16((u32)f[s][h], zz);
+        } else {
+          const float zb = 8388608.f + zf;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) bw[h] = unpack_bf16((u32)f[s][h], zb);
+        }
+        const int8_t* xf = xrow + 256 * (g < G ? g : 0);
+        v4f pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const v4i a = ld16(xf + 16 * h);
+          if constexpr (XDT == F16)
+            pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
+                                                          __builtin_bit_cast(v8h, bw[h]), pacc, 0, 0, 0);
+          else
+            pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                           __builtin_bit_cast(v8bf, bw[h]), pacc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yacc[i] = __builtin_fmaf(sc, pacc[i], yacc[i]);
+      }
+    }
+  };
+  for (int q0 = ub; q0 < ue; q0 += 2 * UB) {
+    load(b1, q0 + UB);
+    mma(b0, q0);
+    load(b0, q0 + 2 * UB);
+    mma(b1, q0 + UB);
+  }
+
+  red[wave][lane] = yacc;
+  __syncthreads();
+  if (tid < 64) {
+    v4f sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+    const int n = n_base + r;
+    if (n < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * j + i;
+        if (m < M) y[(int64_t)m * N + n] = Out<OutT>::cvt(sum[i]);
+      }
+    }
+  }
+}
+
 template <int XDT, typename OutT>
 static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
                                const uint16_t* wz, int M, int N, int K, OutT* y, hipStream_t st) {
+  const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+  const size_t lds = (size_t)mr * stage_pitch(2 * K) + (size_t)16 * sz_pitch(K / 128) * 4;
+  if (M <= 16 && lds <= kDecLdsMaxBytes) {
+    constexpr int WAVES = 4, UB = 1;  // measured on MI355X
+    const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
+    switch (mr) {
+      case 1: k_w4a16_dec<1, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+      case 2: k_w4a16_dec<2, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+      case 4: k_w4a16_dec<4, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+      case 8: k_w4a16_dec<8, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+      default: k_w4a16_dec<16, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    }
+    return hipGetLastError();
+  }
   constexpr int MT = 1, NT = 1, WAVES = 8, U = 2;  // measured on MI355X
   dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
   k_w4a16<MT, NT, WAVES, U, XDT, OutT><<<grid, dim3(64 * WAVES), 0, st>>>(x, wq, ws, wz, M, N, K, y);

@@ -14,6 +14,7 @@
 // pairs every code with its own activation.  The zero point enters once per
 // group through the token sums sum_k xq[m,k], which one extra MFMA against an
 // all-ones operand produces in the accumulator layout.
+#include "qg_decode.hpp"
 #include "qg_device.hpp"
 #include "qg_launch.hpp"
 
@@ -65,7 +66,7 @@ __device__ __forceinline__ void w4a8_load(W4A8Batch<MT, NT, U>& bt, int g0, int 
     const bool gin = g < ge;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      bt.wv[u][t] = bld16(wr, gin ? woff[t] + 64 * g : kOOB);
+      bt.wv[u][t] = bld16_nt(wr, gin ? woff[t] + 64 * g : kOOB);
       bt.sbits[u][t] = bld2(sr, gin ? soff[t] + 2 * g : kOOB);
       bt.zbits[u][t] = bld2(zr, gin ? soff[t] + 2 * g : kOOB);
     }
@@ -209,10 +210,169 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode kernel (M <= 16) on whole-line weight units (see qg_decode.hpp): a
+// unit is two g=128 groups of 16 weight rows.  Scales and zero points are
+// staged in LDS; the token rows (up to 16 x K bytes, too many to stage whole
+// for long K) come straight from the L2 into the MFMA operand registers with
+// the unit they belong to.  Wave w streams its contiguous run of units in
+// batches of UB, two batches in flight.
+// ---------------------------------------------------------------------------
+template <int UB>
+struct W4A8DecBatch {
+  v4i w[UB][2], xa[UB][2][2];   // unit v: weight loads; group s, MFMA h token fragment
+};
+
+template <int MR, int WAVES, int UB, typename OutT>
+__global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, const int32_t* __restrict__ wq,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
+    OutT* __restrict__ y) {
+  constexpr bool kI32 = __is_same(OutT, int32_t);
+  constexpr int kThreads = 64 * WAVES;
+  extern __shared__ __attribute__((aligned(16))) u32 szl[];   // 16 x sz_pitch(G) words
+  __shared__ __attribute__((aligned(16))) int8_t tiles[WAVES][kTileBytes];
+  __shared__ v4f red[kI32 ? 1 : WAVES][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int n_base = blockIdx.x * 16;
+  const int G = K >> 7, Kw = K >> 3, RB = Kw * 4;
+  const int units = (RB + kUnitBytes - 1) / kUnitBytes;
+  const int ub = (int)((int64_t)units * wave / WAVES), ue = (int)((int64_t)units * (wave + 1) / WAVES);
+
+  const int rows_n = min(16, N - n_base);
+  const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * Kw, (u32)(rows_n * RB));
+  const UnitLanes ul = unit_lanes(lane, RB);
+  // token row r (rows >= M past the resource's end read zeros), k = 32j + 16h
+  const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
+  const u32 xoff = (u32)((r < MR ? r : MR) * K + 32 * j);
+
+  using Batch = W4A8DecBatch<UB>;
+  auto load = [&](Batch& bt, int q0) {
+#pragma unroll
+    for (int v = 0; v < UB; ++v) {
+      const int q = q0 + v;
+      unit_load(bt.w[v], wr, ul, q, q < ue, RB);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int g = 2 * q + s;
+        const bool gin = q < ue && g < G;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) bt.xa[v][s][h] = bld16(xr, gin ? xoff + 128 * g + 16 * h : kOOB);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  Batch b0, b1;
+  ScaleZeroStage<kThreads, 4> sz;
+  const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  sz.load(sr, zr, G, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(b0, ub);
+  float sx[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!kI32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * j + i;
+      sx[i] = xs[m < M ? m : M - 1];
+    }
+  }
+  sz.store(szl, G);
+  for (int c0 = 4 * kThreads; c0 < 16 * G; c0 += 4 * kThreads) {
+    sz.load(sr, zr, G, c0);
+    sz.store(szl, G);
+  }
+  lds_barrier();
+
+  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  const u32* szrow = szl + r * sz_pitch(G);
+  int8_t* tile = tiles[wave];
+  v4f yacc = {0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const Batch& bt, int q0) {
+#pragma unroll
+    for (int v = 0; v < UB; ++v) {
+      v4i f[2];
+      unit_transpose(tile, bt.w[v], ul, f);
+      const int q = q0 + v;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        // groups past this wave's run or past G: zero codes, zero point and scale
+        const int g = 2 * q + s;
+        const bool gin = q < ue && g < G;
+        const u32 szw = gin ? szrow[g] : 0u;
+        const v4i a0 = shuffle_act16(bt.xa[v][s][0]), a1 = shuffle_act16(bt.xa[v][s][1]);
+        v4i rs = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+        rs = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, ones, rs, 0, 0, 0);
+        const int z = (int)f16_bits_to_f32((uint16_t)(szw >> 16));
+        v4i acc = -z * rs;
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_u4_pair((u32)f[s][0], (u32)f[s][1]),
+                                                    acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_u4_pair((u32)f[s][2], (u32)f[s][3]),
+                                                    acc, 0, 0, 0);
+        if constexpr (kI32) {
+          const int n = n_base + r;
+          if (gin && n < N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = 4 * j + i;
+              if (m < M) y[((int64_t)m * G + g) * N + n] = acc[i];
+            }
+          }
+        } else {
+          const float sc = f16_bits_to_f32((uint16_t)(szw & 0xFFFFu));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) yacc[i] = __builtin_fmaf(sc, (float)acc[i], yacc[i]);
+        }
+      }
+    }
+  };
+  for (int q0 = ub; q0 < ue; q0 += 2 * UB) {
+    load(b1, q0 + UB);
+    mma(b0, q0);
+    load(b0, q0 + 2 * UB);
+    mma(b1, q0 + UB);
+  }
+
+  if constexpr (!kI32) {
+    red[wave][lane] = yacc;
+    __syncthreads();
+    if (tid < 64) {
+      v4f sum = red[0][lane];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+      const int n = n_base + r;
+      if (n < N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * j + i;
+          if (m < M) store_out<OutT>(y, (int64_t)m * N + n, sum[i] * sx[i]);
+        }
+      }
+    }
+  }
+}
+
 template <typename OutT>
 static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* wq,
                               const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
                               hipStream_t st) {
+  const size_t lds = (size_t)16 * sz_pitch(K / 128) * 4;
+  if (M <= 16 && lds <= kDecLdsMaxBytes) {
+    constexpr int WAVES = 8, UB = 1;  // measured on MI355X
+    const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
+    const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+    switch (mr) {
+      case 1: k_w4a8_dec<1, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
+      case 2: k_w4a8_dec<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
+      case 4: k_w4a8_dec<4, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
+      case 8: k_w4a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
+      default: k_w4a8_dec<16, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
+    }
+    return hipGetLastError();
+  }
   constexpr int MT = 1, NT = 1, WAVES = 8, U = 2;  // measured on MI355X
   dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
   k_w4a8<MT, NT, WAVES, U, OutT><<<grid, dim3(64 * WAVES), 0, st>>>(xq, xs, wq, ws, wz, M, N, K, y);

@@ -3,16 +3,21 @@
 // 「第4章：量化」 §2.3 (W8A8: the GEMM runs on int8 units), §1.1 (x_hat = x_int s);
 // 「LLM推理降本五要素」 §2.1 (at decode the layer waits on weight bandwidth).
 //
-// Two kernels:
-//  * small M (decode, M <= 64): the weight stream is the whole cost.  Every
-//    weight byte is used by at most 64 rows once, so weights go straight from
-//    HBM into MFMA operand registers (16-byte buffer loads, two batches in
-//    flight per lane); the K loop is split across the waves of a workgroup and
-//    the int32 partials meet in LDS (exact, order-free).
+// Three kernels:
+//  * decode (M <= 16, token rows fit LDS): the weight stream is the whole
+//    cost.  Whole-line weight units transposed through LDS into MFMA
+//    operands, token rows staged once per workgroup (qg_decode.hpp).
+//  * small M (other M <= 64): weights go straight from HBM into MFMA operand
+//    registers (16-byte buffer loads, two batches in flight per lane); the K
+//    loop is split across the waves of a workgroup and the int32 partials
+//    meet in LDS (exact, order-free).
 //  * large M (prefill): 256x256 output tiles, K in 128-byte stages brought
 //    into LDS by buffer-to-LDS DMA (two alternating stage buffers, XOR-swizzled
 //    16-byte chunks), 4 waves each owning a 128x128 sub-tile of 32x32x32 int8
 //    MFMAs.
+#include <type_traits>
+
+#include "qg_decode.hpp"
 #include "qg_device.hpp"
 #include "qg_launch.hpp"
 
@@ -50,7 +55,7 @@ __device__ __forceinline__ void small_m_load(SmallMBatch<MT, NT, U>& bt, int s0,
     const int k = (s0 + u) * 64;
     const bool kin = (s0 + u < se) && (k + kq < K);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) bt.b[u][t] = bld16(wr, kin ? woff[t] + k : kOOB);
+    for (int t = 0; t < NT; ++t) bt.b[u][t] = bld16_nt(wr, kin ? woff[t] + k : kOOB);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) bt.a[u][mt] = bld16(xr, kin ? xoff[mt] + k : kOOB);
   }
@@ -67,6 +72,100 @@ __device__ __forceinline__ void small_m_mma(const SmallMBatch<MT, NT, U>& bt, v4
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         acc[mt][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bt.a[u][mt], bt.b[u][t], acc[mt][t], 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel (M <= 16) on whole-line weight units (see qg_decode.hpp): a
+// unit is two 64-deep int8 MFMA steps of 16 weight rows.  The token rows are
+// staged whole in LDS first (MR rows, MR >= M, rows past M as zeros); wave w
+// then streams its contiguous run of units in batches of UB, two batches in
+// flight, each unit transposed through the wave's tile and multiplied against
+// the matching token fragments.  The int32 partials of the waves meet in LDS.
+// ---------------------------------------------------------------------------
+template <int MR, int WAVES, int UB, typename OutT>
+__global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, const int8_t* __restrict__ wq,
+    const float* __restrict__ ws, int M, int N, int K, OutT* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) int8_t xl[];   // MR rows, pitch stage_pitch(K)
+  __shared__ __attribute__((aligned(16))) int8_t tiles[WAVES][kTileBytes];
+  __shared__ v4i red[WAVES][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int n_base = blockIdx.x * 16;
+  const int units = (K + kUnitBytes - 1) / kUnitBytes;
+  const int ub = (int)((int64_t)units * wave / WAVES), ue = (int)((int64_t)units * (wave + 1) / WAVES);
+  const int pitch = stage_pitch(K);
+
+  const int rows_n = min(16, N - n_base);
+  const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * K, (u32)(rows_n * K));
+  const UnitLanes ul = unit_lanes(lane, K);
+
+  v4i b0[UB][2], b1[UB][2];
+  auto load = [&](v4i (&b)[UB][2], int q0) {
+#pragma unroll
+    for (int v = 0; v < UB; ++v) unit_load(b[v], wr, ul, q0 + v, q0 + v < ue, K);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // token rows into LDS; the first weight batch is issued behind the first
+  // round of their loads
+  stage_rows<MR, 64 * WAVES>(xl, make_rsrc(xq, (u32)(M * K)), K, [](v4i v) { return v; },
+                             [&]() { load(b0, ub); });
+  // epilogue scales, fetched early so the tail of the kernel waits on nothing
+  // (int32 output takes no scales, and its scale pointers may be null)
+  const int n_out = n_base + r;
+  float sw = 0.f, sx[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!std::is_same<OutT, int32_t>::value) {
+    sw = ws[n_out < N ? n_out : N - 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * j + i;
+      sx[i] = xs[m < M ? m : M - 1];
+    }
+  }
+  lds_barrier();
+
+  // Rows r >= MR, units past this wave's run and fragments past K read valid
+  // LDS (row 0, k 0): their weight operand is zero, and rows >= M are never
+  // stored.
+  const int8_t* xrow = xl + (r < MR ? r : 0) * pitch;
+  int8_t* tile = tiles[wave];
+  v4i acc = {0, 0, 0, 0};
+  auto mma = [&](const v4i (&b)[UB][2], int q0) {
+#pragma unroll
+    for (int v = 0; v < UB; ++v) {
+      v4i f[2];
+      unit_transpose(tile, b[v], ul, f);
+      const bool qin = q0 + v < ue;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int ka = kUnitBytes * (q0 + v) + 64 * s + 16 * j;
+        const v4i a = ld16(xrow + (qin && ka < K ? ka : 0));
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, f[s], acc, 0, 0, 0);
+      }
+    }
+  };
+  for (int q0 = ub; q0 < ue; q0 += 2 * UB) {
+    load(b1, q0 + UB);
+    mma(b0, q0);
+    load(b0, q0 + 2 * UB);
+    mma(b1, q0 + UB);
+  }
+
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (tid < 64) {
+    v4i sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+    if (n_out < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * j + i;
+        if (m < M) y[(int64_t)m * N + n_out] = w8a8_epilogue<OutT>(sum[i], sx[i], sw);
+      }
+    }
+  }
 }
 
 template <int MT, int NT, int WAVES, int U, typename OutT>
@@ -336,7 +435,6 @@ __global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict
 }
 
 constexpr int kPrefillWaves = 8;
-
 template <typename OutT>
 static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* wq,
                               const float* ws, int M, int N, int K, OutT* y, hipStream_t st) {
@@ -345,7 +443,19 @@ static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* w
     constexpr int WAVES = 4, NT = 1;
     dim3 block(64 * WAVES);
     const unsigned gx = (unsigned)((N + 16 * NT - 1) / (16 * NT));
-    if (M <= 16)
+    const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+    const size_t lds = (size_t)mr * stage_pitch(K);
+    if (M <= 16 && lds <= kDecLdsMaxBytes) {
+      constexpr int UB = 2;
+      const dim3 grid(gx, 1);
+      switch (mr) {
+        case 1: k_w8a8_dec<1, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+        case 2: k_w8a8_dec<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+        case 4: k_w8a8_dec<4, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+        case 8: k_w8a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+        default: k_w8a8_dec<16, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+      }
+    } else if (M <= 16)
       k_w8a8_small_m<1, NT, WAVES, 8, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
     else if (M <= 32)
       k_w8a8_small_m<2, NT, WAVES, 4, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);

@@ -1,0 +1,171 @@
+// Building blocks of the decode-shaped (M <= 16) GEMM kernels.
+//
+// At decode the layer is a stream of weight bytes, each used by at most 16
+// token rows, so the kernels are shaped around reading the weights at full
+// HBM efficiency.  A workgroup owns 16 weight rows (16 output columns) and the
+// whole K.  The rows are read in units of 128 bytes per row (one cache line):
+// two MFMA steps of int8 codes, or two g=128 groups of packed uint4 codes.
+//
+// Whole-line loads.  An MFMA operand wants lane l to hold row l & 15, so a
+// direct fragment load touches 16 rows x 64 bytes -- half lines -- and
+// measured 25-50% slower on MI355X than loads whose lanes cover whole 128-byte
+// lines.  A unit is therefore fetched as two loads of 8 rows x 128 bytes
+// (lane l: row 8h + (l >> 3), 16-byte chunk l & 7) and turned into MFMA
+// fragments through a 2 KB wave-private LDS tile: written with the lane's
+// chunk at an XOR-swizzled slot, read back as fragment s = chunk 4s + (l >> 4)
+// of row l & 15.  Both directions are free of LDS bank conflicts (64 banks x
+// 4 bytes): a write covers rows 2i, 2i+1 with all 16 chunk slots, a read the
+// 16 rows of one chunk at 16 different slots.
+//
+// Work split.  The waves of a workgroup split the units into contiguous
+// runs: a wave streaming its own stretch of every row measured faster than
+// waves interleaving units of a shared stretch (DRAM page locality).
+#pragma once
+
+#include "qg_device.hpp"
+
+namespace qg {
+
+constexpr int kUnitBytes = 128;   // per weight row
+constexpr int kTileBytes = 16 * kUnitBytes;
+// Largest dynamic LDS a decode launch stages (token rows, scales): 80 KB, so
+// that two workgroups still share the 160 KB of a CU.
+constexpr size_t kDecLdsMaxBytes = 80 * 1024;
+
+__device__ __forceinline__ int unit_slot(int row, int chunk) {
+  return row * kUnitBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// Per-lane constants of the unit fetch and transpose.
+struct UnitLanes {
+  u32 goff[2];    // byte offset of the lane's chunk of unit 0 (load h) in the 16-row block
+  int wslot[2];   // LDS slot the lane writes (load h)
+  int rslot[2];   // LDS slot of the lane's fragment s
+  int kchunk;     // byte offset of the lane's chunk within a unit
+};
+
+__device__ __forceinline__ UnitLanes unit_lanes(int lane, int row_bytes) {
+  UnitLanes u;
+  const int ch = lane & 7;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * h + (lane >> 3);
+    u.goff[h] = (u32)(row * row_bytes + 16 * ch);
+    u.wslot[h] = unit_slot(row, ch);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) u.rslot[s] = unit_slot(lane & 15, 4 * s + (lane >> 4));
+  u.kchunk = 16 * ch;
+  return u;
+}
+
+// Issue the two whole-line loads of unit q (bytes 128q .. 128q + 127 of each
+// row) if `valid`.  Chunks past the row end, rows past the buffer resource's
+// end and invalid units read zeros.
+__device__ __forceinline__ void unit_load(v4i (&d)[2], rsrc_t wr, const UnitLanes& ul, int q,
+                                          bool valid, int row_bytes) {
+  const bool in = valid && kUnitBytes * q + ul.kchunk < row_bytes;
+  const u32 o = (u32)(kUnitBytes * q);
+  d[0] = bld16_nt(wr, in ? ul.goff[0] + o : kOOB);
+  d[1] = bld16_nt(wr, in ? ul.goff[1] + o : kOOB);
+}
+
+// Write a fetched unit into the wave's tile and read back its two MFMA
+// fragments.  One wave's LDS accesses execute in issue order, so the reads
+// see the writes and the next unit's writes follow these reads; the asm
+// statement keeps the compiler from reordering them.
+__device__ __forceinline__ void unit_transpose(int8_t* tile, const v4i (&d)[2], const UnitLanes& ul,
+                                               v4i (&f)[2]) {
+  st16(tile + ul.wslot[0], d[0]);
+  st16(tile + ul.wslot[1], d[1]);
+  asm volatile("" ::: "memory");
+  f[0] = ld16(tile + ul.rslot[0]);
+  f[1] = ld16(tile + ul.rslot[1]);
+  asm volatile("" ::: "memory");
+}
+
+// Row pitch (bytes) of token rows staged whole in LDS: an odd number of
+// 16-byte chunks, so the 16 rows of a fragment read hit 16 different bank
+// groups.
+__host__ __device__ constexpr int stage_pitch(int row_bytes) {
+  return ((row_bytes >> 4) & 1) ? row_bytes + 32 : row_bytes + 16;
+}
+
+// Copy ROWS token rows of `row_bytes` bytes (a multiple of 16) from global
+// memory into LDS at pitch stage_pitch(row_bytes), every 16-byte chunk passed
+// through `f`.  A round moves CPR chunks of every row per thread (at most 8
+// or ROWS loads per thread), all loads before their stores; `after` runs between the
+// first round's loads and stores, so that loads the caller issues there
+// overlap the staging.  Rows past the resource's end are staged as zeros.
+template <int ROWS, int THREADS, typename F, typename A>
+__device__ __forceinline__ void stage_rows(int8_t* dst, rsrc_t src, int row_bytes, F f, A after) {
+  constexpr int CPR = ROWS >= 8 ? 1 : 8 / ROWS;
+  const int kc = row_bytes >> 4, pitch = stage_pitch(row_bytes);
+  v4i v[ROWS][CPR];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < CPR; ++i) {
+      const int c = c0 + (int)threadIdx.x + i * THREADS;
+#pragma unroll
+      for (int m = 0; m < ROWS; ++m)
+        v[m][i] = bld16(src, c < kc ? (u32)(m * row_bytes + 16 * c) : kOOB);
+    }
+  };
+  auto store = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < CPR; ++i) {
+      // a chunk past the row end is written (as zeros) into the row's padding
+      const int c = c0 + (int)threadIdx.x + i * THREADS, cc = c < kc ? c : kc;
+#pragma unroll
+      for (int m = 0; m < ROWS; ++m) st16(dst + m * pitch + 16 * cc, f(v[m][i]));
+    }
+  };
+  load(0);
+  __builtin_amdgcn_sched_barrier(0);
+  after();
+  store(0);
+  for (int c0 = CPR * THREADS; c0 < kc; c0 += CPR * THREADS) {
+    load(c0);
+    store(c0);
+  }
+}
+
+// Scale and zero point of the 16 weight rows of a workgroup (G groups, fp16
+// bits) staged in LDS as words s | z << 16 at pitch G + 1, an odd number of
+// words, so that the 16 rows of one group read hit 16 different banks.
+// EPT elements per thread are loaded per round, all before their stores.
+__host__ __device__ constexpr int sz_pitch(int G) { return G + 1; }
+
+template <int THREADS, int EPT>
+struct ScaleZeroStage {
+  uint16_t s[EPT], z[EPT];
+  int e0;
+  __device__ __forceinline__ void load(rsrc_t sr, rsrc_t zr, int G, int c0) {
+    e0 = c0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = c0 + (int)threadIdx.x + i * THREADS;
+      const bool in = e < 16 * G;   // rows past the resource's end read zeros
+      s[i] = bld2(sr, in ? (u32)(2 * e) : kOOB);
+      z[i] = bld2(zr, in ? (u32)(2 * e) : kOOB);
+    }
+  }
+  __device__ __forceinline__ void store(u32* dst, int G) const {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = e0 + (int)threadIdx.x + i * THREADS;
+      if (e < 16 * G) {
+        const int row = e / G;
+        dst[row * sz_pitch(G) + (e - row * G)] = (u32)s[i] | ((u32)z[i] << 16);
+      }
+    }
+  }
+};
+
+// Barrier for LDS data written by the workgroup: waits for this wave's LDS
+// accesses only, leaving its global loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace qg

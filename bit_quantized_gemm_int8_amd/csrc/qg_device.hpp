@@ -41,6 +41,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ v4i bld16(rsrc_t r, u32 off) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Streaming variant (non-temporal cache policy) for data read exactly once per
+// call, i.e. the weight stream; measured ~6% faster than the default policy
+// for a 45 MB stream on MI355X.
+constexpr int kAuxNonTemporal = 2;
+__device__ __forceinline__ v4i bld16_nt(rsrc_t r, u32 off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNonTemporal));
+}
 __device__ __forceinline__ uint16_t bld2(rsrc_t r, u32 off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }

@@ -21,7 +21,10 @@ TORCH_OUT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 W8A8_SHAPES = [(16, 512, 512), (1, 16, 16), (3, 17, 48), (8, 11008, 4096), (17, 40, 528),
                (33, 100, 1024), (64, 64, 64), (65, 300, 272), (100, 257, 4096),
-               (300, 520, 1040), (257, 1000, 1936)]
+               (300, 520, 1040), (257, 1000, 1936),
+               # decode kernel: odd 16-byte chunk count per row (LDS pitch), several
+               # token-row staging rounds, and a K whose rows overflow the LDS budget
+               (5, 33, 4112), (12, 100, 9008), (16, 40, 8192)]
 
 
 def _codes(rng, shape):
@@ -104,7 +107,7 @@ def _w4_devs(packed, sc, zz):
 
 
 W4_SHAPES = [(16, 4096, 11008), (1, 16, 128), (5, 17, 256), (16, 300, 1024), (17, 64, 384),
-             (33, 40, 640), (1, 12288, 4096), (3, 100, 2048)]
+             (33, 40, 640), (1, 12288, 4096), (3, 100, 2048), (2, 48, 14336)]
 
 
 @pytest.mark.parametrize("M,N,K", W4_SHAPES)
@@ -127,7 +130,7 @@ def _w4a8_floor(xq, sx, packed, sc, zz):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f32", "f16"])
-@pytest.mark.parametrize("M,N,K", [(16, 4096, 11008), (5, 17, 256), (33, 40, 640)])
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 11008), (5, 17, 256), (33, 40, 640), (2, 48, 14336)])
 def test_w4a8_scaled(fmt, M, N, K):
     rng = np.random.default_rng(M + 3 * N + K)
     packed, sc, zz = _u4_weights(rng, K, N)
@@ -154,7 +157,8 @@ def _w4a16_floor(x64, packed, sc, zz):
 
 @pytest.mark.parametrize("xfmt", ["f16", "bf16"])
 @pytest.mark.parametrize("fmt", ["f16", "f32", "bf16"])
-@pytest.mark.parametrize("M,N,K", [(1, 12288, 4096), (5, 17, 256), (16, 300, 1024), (33, 40, 640)])
+@pytest.mark.parametrize("M,N,K", [(1, 12288, 4096), (5, 17, 256), (16, 300, 1024), (33, 40, 640),
+                                   (2, 48, 14336)])
 def test_w4a16(xfmt, fmt, M, N, K):
     rng = np.random.default_rng(M * 5 + N + K)
     packed, sc, zz = _u4_weights(rng, K, N)
