@@ -15,6 +15,7 @@
 //    into LDS by buffer-to-LDS DMA (two alternating stage buffers, XOR-swizzled
 //    16-byte chunks), 4 waves each owning a 128x128 sub-tile of 32x32x32 int8
 //    MFMAs.
+#include <array>
 #include <type_traits>
 
 #include "qg_decode.hpp"
@@ -341,7 +342,9 @@ __device__ __forceinline__ void prefill_mma(const int8_t* buf, int row_a, int ro
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j < WJ; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks & 1][i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
+        // weight fragment as the first operand: the accumulator comes out
+        // transposed (lane = token row), see the epilogue
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[ks & 1][j], af[ks & 1][i], acc[i][j], 0, 0, 0);
         const int slot = (ks * 4 + i) * WJ + j;
         if (slot < kSlots && (slot % kEvery) == kEvery - 1) next.issue(slot / kEvery, K);
       }
@@ -358,12 +361,16 @@ __device__ __forceinline__ void prefill_stage_sync() {
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Scales of the tile's 256 token rows and 256 weight rows, staged in LDS.
+__shared__ __attribute__((aligned(16))) float g_tile_scale[TBM + TBN];
+
 template <int NW, typename OutT>
 __global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict__ xq,
                                                         const float* __restrict__ xs,
                                                         const int8_t* __restrict__ wq,
                                                         const float* __restrict__ ws, int M,
-                                                        int N, int K, OutT* __restrict__ y) {
+                                                        int N, int K, OutT* __restrict__ y,
+                                                        int vec_store) {
   constexpr int WJ = NW == 4 ? 4 : 2;           // column tiles per wave
   constexpr int WAVES_N = NW / 2;               // waves across the 256 columns
   const int tid = threadIdx.x, lane = tid & 63;
@@ -402,6 +409,14 @@ __global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict
 #pragma unroll
     for (int j = 0; j < WJ; ++j) acc[i][j] = v16i{};
 
+  constexpr bool kI32 = std::is_same<OutT, int32_t>::value;
+  if constexpr (!kI32) {   // (int32 output takes no scales; its pointers may be null)
+    for (int t = tid; t < TBM + TBN; t += 64 * NW) {
+      const int m = m0 + t, n = n0 + t - TBM;
+      g_tile_scale[t] = t < TBM ? (m < M ? xs[m] : 0.f) : (n < N ? ws[n] : 0.f);
+    }
+  }
+
   const int nk = (K + TBK - 1) / TBK;
   prefill_dma<NW>(g_stage0, 0, K, ar, br, wave, lane);
   for (int kt = 0; kt < nk; kt += 2) {
@@ -415,22 +430,91 @@ __global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict
                         prefill_dma_setup<NW>(g_stage0, kt + 2, K, ar, br, wave, lane), K);
   }
 
-  // 32x32 accumulator layout: lane l holds column (l & 31); register e holds
-  // row 8*(e >> 2) + 4*(l >> 5) + (e & 3).
-  const int col_in = lane & 31, rsub = 4 * (lane >> 5);
+  // The MFMAs ran with the weight fragment first, so accumulator (i, j) holds
+  // the transposed 32x32 block: lane l has token row 32i + (l & 31) of the
+  // wave tile, and register e the weight row (output column) 32j + 8(e >> 2)
+  // + 4(l >> 5) + (e & 3) -- four consecutive output columns per e >> 2.
+  //
+  // Epilogue: the last (zero) DMA has landed and every wave is done with the
+  // stage buffers, which now serve as wave-private 16 KB staging regions: a
+  // pass writes 128 token rows x 128 bytes of output (two column tiles of
+  // 2-byte outputs, one of 4-byte outputs) into the region, then reads it
+  // back as whole 16-byte chunks and stores whole 128-byte lines of y.  Tiles
+  // that cross the edge of y, or a y that is not 16-byte aligned per row,
+  // take element stores instead.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  constexpr int E = (int)sizeof(OutT);
+  constexpr int JP = E == 2 ? 2 : 1;               // column tiles per pass
+  const int lr = lane & 31, lc = 4 * (lane >> 5);
+  float sx[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!kI32) {
 #pragma unroll
-  for (int j = 0; j < WJ; ++j) {
-    const int n = n0 + row_b + j * 32 + col_in;
-    if (n >= N) continue;
-    const float sw = ws ? ws[n] : 0.f;
+    for (int i = 0; i < 4; ++i) sx[i] = g_tile_scale[row_a + 32 * i + lr];
+  }
+  auto scaled4 = [&](int i, int j, int eb) {      // 4 consecutive outputs
+    v4f sw = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!kI32) sw = *reinterpret_cast<const v4f*>(&g_tile_scale[TBM + row_b + 32 * j + 8 * eb + lc]);
+    OutT o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int t = 0; t < 4; ++t) o[t] = w8a8_epilogue<OutT>(acc[i][j][4 * eb + t], sx[i], sw[t]);
+    return std::array<OutT, 4>{o[0], o[1], o[2], o[3]};
+  };
+  const bool full = vec_store && m0 + TBM <= M && n0 + TBN <= N;
+  if (full) {
+    int8_t* reg = (wave < 4 ? g_stage0 : g_stage1) + (wave & 3) * 16384;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + row_a + i * 32 + 8 * (e >> 2) + rsub + (e & 3);
-        if (m < M) y[(int64_t)m * N + n] = w8a8_epilogue<OutT>(acc[i][j][e], xs ? xs[m] : 0.f, sw);
+    for (int jp = 0; jp < WJ; jp += JP) {
+#pragma unroll
+      for (int jj = 0; jj < JP; ++jj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int eb = 0; eb < 4; ++eb) {
+            const std::array<OutT, 4> o = scaled4(i, jp + jj, eb);
+            const int row = 32 * i + lr, byte = E * (32 * jj + 8 * eb + lc);
+            int8_t* d = reg + row * 128 + (((byte >> 4) ^ (row & 7)) << 4) + (byte & 15);
+            if constexpr (E == 2) {
+              uint16_t h[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) h[t] = __builtin_bit_cast(uint16_t, o[t]);
+              *reinterpret_cast<uint2*>(d) = uint2{(u32)h[0] | ((u32)h[1] << 16), (u32)h[2] | ((u32)h[3] << 16)};
+            } else {
+              u32 w[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) w[t] = __builtin_bit_cast(u32, o[t]);
+              st16(d, v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
+            }
+          }
+      // one wave's LDS accesses execute in order: the reads below see the
+      // writes above, and the next pass's writes follow these reads
+      asm volatile("" ::: "memory");
+      int8_t* ybase = reinterpret_cast<int8_t*>(y) +
+                      ((int64_t)(m0 + row_a) * N + n0 + row_b + 32 * jp) * E;
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int row = 8 * it + (lane >> 3), ch = lane & 7;
+        const v4i v = ld16(reg + row * 128 + ((ch ^ (row & 7)) << 4));
+        st16(ybase + (int64_t)row * N * E + 16 * ch, v);
       }
+      asm volatile("" ::: "memory");
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + row_a + 32 * i + lr;
+        if (m >= M) continue;
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) {
+          const std::array<OutT, 4> o = scaled4(i, j, eb);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int n = n0 + row_b + 32 * j + 8 * eb + lc + t;
+            if (n < N) y[(int64_t)m * N + n] = o[t];
+          }
+        }
+      }
   }
 }
 
@@ -463,7 +547,10 @@ static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* w
       k_w8a8_small_m<4, NT, WAVES, 2, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
   } else {
     const int tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
-    k_w8a8_tiled<kPrefillWaves, OutT><<<dim3((unsigned)tiles), dim3(64 * kPrefillWaves), 0, st>>>(xq, xs, wq, ws, M, N, K, y);
+    // whole-line stores need every row of y to start on a 16-byte boundary
+    const int vec = ((uintptr_t)y % 16 == 0) && ((size_t)N * sizeof(OutT)) % 16 == 0;
+    k_w8a8_tiled<kPrefillWaves, OutT><<<dim3((unsigned)tiles), dim3(64 * kPrefillWaves), 0, st>>>(
+        xq, xs, wq, ws, M, N, K, y, vec);
   }
   return hipGetLastError();
 }
