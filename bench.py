@@ -40,9 +40,9 @@ INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA
 F16_PEAK_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
 ROTATE_BYTES = 600 * 2 ** 20    # weight copies per rotation: > 2x the 256 MB MALL
 KERNEL_SOURCES = {
-    "w8a8": ["gemm_w8a8.hip", "qg_device.hpp"],
-    "w4a8": ["gemm_w4a8.hip", "qg_device.hpp"],
-    "w4a16": ["gemm_w4a16.hip", "qg_device.hpp"],
+    "w8a8": ["gemm_w8a8.hip", "qg_decode.hpp", "qg_device.hpp"],
+    "w4a8": ["gemm_w4a8.hip", "qg_decode.hpp", "qg_device.hpp"],
+    "w4a16": ["gemm_w4a16.hip", "qg_decode.hpp", "qg_device.hpp"],
     "quant": ["quant.hip", "qg_device.hpp"],
 }
 
@@ -282,10 +282,10 @@ def cpu_baseline(wl, seconds):
 # demangled-name patterns of each workload's dominant kernel as bench.py runs it
 # (rocprofv3 leaves names with _Float16 mangled, hence the alternatives)
 KERNEL_OF = {
-    "w8a8_decode_ffn_up": [("k_w8a8_small_m<1,", "unsigned short>")],
-    "w8a8_tiny": [("k_w8a8_small_m<1,", "float>")],
-    "w4a8_ffn_down": [("k_w4a8<", "unsigned short>")],
-    "w4a16_qkv": [("k_w4a16<", "_Float16>"), ("k_w4a16ILi", "ELi1EDF16_E")],
+    "w8a8_decode_ffn_up": [("k_w8a8_dec<8,", "unsigned short>")],
+    "w8a8_tiny": [("k_w8a8_dec<16,", "float>")],
+    "w4a8_ffn_down": [("k_w4a8_dec<16,", "unsigned short>")],
+    "w4a16_qkv": [("k_w4a16_dec<1,", "_Float16>"), ("k_w4a16_decILi1E", "DF16_E")],
     "w8a8_prefill": [("k_w8a8_tiled<", "unsigned short>")],
 }
 COPY_BYTES = 512 * 2 ** 20
@@ -361,7 +361,7 @@ def ingest_counters(d):
     for key, rec in out.items():
         path, wl_name = key.split(":")
         wl = by_name(wl_name)
-        kname = {"w8a8": "gemm_w8a8_small_m" if wl.M <= 64 else "gemm_w8a8_tiled",
+        kname = {"w8a8": "gemm_w8a8_dec" if wl.M <= 16 else "gemm_w8a8_tiled",
                  "w4a8": "gemm_w4a8_g128", "w4a16": "gemm_w4a16_g128"}[path]
         fn = os.path.join(ROOT, "profiles", f"{kname}.{wl_name}.md")
         avg = rec["avg_ns"]
