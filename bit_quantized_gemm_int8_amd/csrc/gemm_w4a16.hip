@@ -31,12 +31,21 @@ __device__ __forceinline__ v4i shuffle_halves(v4i x) {
              (int)__builtin_amdgcn_perm(d3, d1, 0x07060302u)};
 }
 
+// (x & mask) | bits in one VALU instruction (the compiler otherwise emits an
+// AND and an OR).  The mask comes from an SGPR and the bits from a VGPR: a
+// gfx9 VOP3 instruction reads at most one scalar operand.
+__device__ __forceinline__ u32 and_or(u32 x, u32 mask, u32 bits) {
+  u32 r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(bits));
+  return r;
+}
+
 // 8 codes of word w -> (q - z) as fp16 halves in order [q0 q4 q1 q5 q2 q6 q3 q7]
 __device__ __forceinline__ v4i unpack_f16(u32 w, u32 zz /* fp16 pair of 1024 + z */) {
   v4i r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32 t = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+    const u32 t = and_or(w >> (4 * i), 0x000F000Fu, 0x64006400u);
     const h2 d = __builtin_bit_cast(h2, t) - __builtin_bit_cast(h2, zz);
     r[i] = __builtin_bit_cast(int, d);
   }

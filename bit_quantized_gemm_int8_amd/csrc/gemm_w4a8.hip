@@ -108,7 +108,9 @@ __device__ __forceinline__ void w4a8_mma(const W4A8Batch<MT, NT, U>& bt, int g0,
       const float s = f16_bits_to_f32(bt.sbits[u][t]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        v4i acc = -z * rs[mt];
+        v4i acc;   // |z| <= 15, |token sum| <= 128 * 127: 24-bit multiplies are exact
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __mul24(-z, rs[mt][i]);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][0], b0, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][1], b1, acc, 0, 0, 0);
         if constexpr (kI32) {
@@ -307,7 +309,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec(
         v4i rs = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, ones, v4i{0, 0, 0, 0}, 0, 0, 0);
         rs = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, ones, rs, 0, 0, 0);
         const int z = (int)f16_bits_to_f32((uint16_t)(szw >> 16));
-        v4i acc = -z * rs;
+        // |z| <= 15 and |token sum| <= 128 * 127: the 24-bit multiply is exact
+        v4i acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __mul24(-z, rs[i]);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_u4_pair((u32)f[s][0], (u32)f[s][1]),
                                                     acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_u4_pair((u32)f[s][2], (u32)f[s][3]),

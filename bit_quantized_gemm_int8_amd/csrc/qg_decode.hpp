@@ -93,13 +93,13 @@ __host__ __device__ constexpr int stage_pitch(int row_bytes) {
 
 // Copy ROWS token rows of `row_bytes` bytes (a multiple of 16) from global
 // memory into LDS at pitch stage_pitch(row_bytes), every 16-byte chunk passed
-// through `f`.  A round moves CPR chunks of every row per thread (at most 8
-// or ROWS loads per thread), all loads before their stores; `after` runs between the
+// through `f`.  A round moves CPR chunks of every row per thread (2 for up to
+// 4 rows, else 1: a 4096-element fp16 row, or 4096 int8 codes, in one round), all loads before their stores; `after` runs between the
 // first round's loads and stores, so that loads the caller issues there
 // overlap the staging.  Rows past the resource's end are staged as zeros.
 template <int ROWS, int THREADS, typename F, typename A>
 __device__ __forceinline__ void stage_rows(int8_t* dst, rsrc_t src, int row_bytes, F f, A after) {
-  constexpr int CPR = ROWS >= 8 ? 1 : 8 / ROWS;
+  constexpr int CPR = ROWS <= 4 ? 2 : 1;
   const int kc = row_bytes >> 4, pitch = stage_pitch(row_bytes);
   v4i v[ROWS][CPR];
   auto load = [&](int c0) {
