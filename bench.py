@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain device copy of 512 MiB (counter calibration)")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="instead of the benchmark line: time every path at M = 1..64 next to "
+                         "an fp16 dense GEMM of the same layer, one JSON record per (path, M)")
     ap.add_argument("--ingest-counters", metavar="DIR",
                     help="summarise rocprofv3 output in DIR/{stats,fetch,write} into profiles/")
     return ap.parse_args()
@@ -277,6 +280,88 @@ def cpu_baseline(wl, seconds):
             "ms_per_step": round(el / n * 1e3, 2)}
 
 
+# ------------------------------------------------------------ batch sweep
+
+SWEEP_LAYERS = (("w8a8", 4096, 11008, "bf16"), ("w4a8", 11008, 4096, "bf16"),
+                ("w4a16", 4096, 12288, "f16"))
+SWEEP_M = (1, 2, 4, 8, 16, 32, 64)
+
+
+def batch_sweep(steps):
+    """Decode-to-prefill crossover: each path's linear layer (activation
+    quantization + GEMM; W4A16 the GEMM alone) at M = 1..64 tokens, next to an
+    fp16 dense GEMM of the same K x N layer (torch.matmul, i.e. the vendor
+    BLAS) on fp16 weights.  Seeded random inputs; weights rotate over more
+    than 600 MB of copies in both cases so they stream from HBM."""
+    import torch
+    import bit_quantized_gemm_int8_amd as qg
+
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+    def graph_us(fn, n):
+        fn(0)   # eager first: the vendor BLAS sets itself up outside capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    for path, K, N, xd in SWEEP_LAYERS:
+        w = torch.randn((K, N), generator=gen, device=dev) * 0.02
+        if path == "w8a8":
+            weights = qg.quantize_weight_i8_per_channel(w)
+        else:
+            weights = qg.quantize_weight_u4_g128(w)
+        wbytes = sum(t.numel() * t.element_size() for t in weights)
+        R = max(2, math.ceil(ROTATE_BYTES / wbytes))
+        copies = [weights] + [tuple(t.clone() for t in weights) for _ in range(R - 1)]
+        w16 = w.to(torch.float16)
+        R16 = max(2, math.ceil(ROTATE_BYTES / (2 * K * N)))
+        copies16 = [w16] + [w16.clone() for _ in range(R16 - 1)]
+        del w
+        for M in SWEEP_M:
+            x = torch.randn((M, K), generator=gen, device=dev).to(tdt[xd])
+            xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+            xs = torch.empty((M,), dtype=torch.float32, device=dev)
+            y = torch.empty((M, N), dtype=tdt[xd], device=dev)
+            y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
+            x16 = x.to(torch.float16)
+
+            def layer(i):
+                c = copies[i % R]
+                if path == "w4a16":
+                    qg.gemm_w4a16_g128(x, c[0], c[1], c[2], out_dtype=y.dtype, out=y)
+                    return
+                qg.quantize_per_token_i8(x, out=(xq, xs))
+                if path == "w8a8":
+                    qg.gemm_w8a8(xq, xs, c[0], c[1], out_dtype=y.dtype, out=y)
+                else:
+                    qg.gemm_w4a8_g128(xq, xs, c[0], c[1], c[2], out_dtype=y.dtype, out=y)
+
+            def dense(i):
+                torch.matmul(x16, copies16[i % R16], out=y16)
+
+            us = graph_us(layer, steps)
+            us16 = graph_us(dense, steps)
+            rec = {"path": path, "M": M, "K": K, "N": N, "layer_us": round(us, 3),
+                   "fp16_dense_us": round(us16, 3), "speedup_vs_fp16": round(us16 / us, 3),
+                   "weight_bytes": wbytes, "weight_TBps": round(wbytes / us / 1e6, 3)}
+            print(json.dumps(rec), flush=True)
+        del copies, copies16
+        torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------ counter ingest
 
 # demangled-name patterns of each workload's dominant kernel as bench.py runs it
@@ -406,6 +491,9 @@ def ingest_counters(d):
 
 def main():
     args = parse()
+    if args.batch_sweep:
+        batch_sweep(args.steps)
+        return
     if args.ingest_counters:
         ingest_counters(args.ingest_counters)
         return
