@@ -260,15 +260,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
   ScaleZeroStage<kThreads, 4> sz;
   const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
   const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
-  sz.load(sr, zr, G, 0);
+  sz.load(sr, zr, 16 * G, 0);
   stage_rows<MR, kThreads>(xl, make_rsrc(x, (u32)(M * K * 2)), 2 * K,
                            [](v4i v) { return shuffle_halves(v); },
                            [&]() { load(b0, ub); });
-  sz.store(szl, G);
-  for (int c0 = 4 * kThreads; c0 < 16 * G; c0 += 4 * kThreads) {
-    sz.load(sr, zr, G, c0);
-    sz.store(szl, G);
-  }
+  sz.finish(sr, zr, szl, G, 16 * G);
   lds_barrier();
 
   const int8_t* xrow = xl + (r < MR ? r : 0) * xpitch + 64 * j;
@@ -341,21 +337,184 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide decode kernel (up to 64 token rows, MT m-tiles of 16): a workgroup of
+// NB waves owns NB x 16 weight rows, one 16-row block per wave over the whole
+// K, the waves moving through K in phases of PU units (2 PU groups).  A
+// phase's panel of token rows (16 MT rows x 256 PU halves, chunks already in
+// the unpack order) is staged in LDS once for all NB waves (two-deep ring,
+// one barrier per phase), and each unpacked weight fragment feeds the MFMAs
+// of all MT m-tiles.  Scales and zero points of the workgroup's rows are
+// staged in LDS at the start.
+// ---------------------------------------------------------------------------
+template <int MT, int NB, int PU, int XDT, typename OutT>
+__global__ __launch_bounds__(64 * NB) void k_w4a16_wide(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ wq,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
+    OutT* __restrict__ y) {
+  constexpr int MR = 16 * MT, PB = 512 * PU, kThreads = 64 * NB;   // PB: panel bytes per row
+  constexpr int kPitch = PB + 16;                                   // odd number of 16-byte chunks
+  constexpr int kRowChunks = PB / 16, kChunks = MR * kRowChunks;
+  constexpr int CPT = (kChunks + kThreads - 1) / kThreads;
+  constexpr bool kFull = CPT * kThreads == kChunks;
+  extern __shared__ __attribute__((aligned(16))) u32 szl[];          // 16 NB x sz_pitch(G) words
+  __shared__ __attribute__((aligned(16))) int8_t xbuf[2][MR * kPitch];
+  __shared__ __attribute__((aligned(16))) int8_t tiles[NB][kTileBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int G = K >> 7, Kw = K >> 3, RB = Kw * 4;
+  const int wg_row0 = blockIdx.x * NB * 16, n_base = wg_row0 + wave * 16;
+  const int units = (RB + kUnitBytes - 1) / kUnitBytes;
+  const int phases = (units + PU - 1) / PU;
+
+  const int rows_n = max(0, min(16, N - n_base));
+  const rsrc_t wr = make_rsrc(wq + (int64_t)min(n_base, N - 1) * Kw, (u32)(rows_n * RB));
+  const rsrc_t xr = make_rsrc(x, (u32)(M * K * 2));
+  const UnitLanes ul = unit_lanes(lane, RB);
+
+  struct Batch {
+    v4i w[PU][2], x[CPT];
+  };
+  auto load = [&](Batch& bt, int p) {
+#pragma unroll
+    for (int v = 0; v < PU; ++v) unit_load(bt.w[v], wr, ul, p * PU + v, true, RB);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int chunk = tid + c * kThreads;
+      const int row = chunk / kRowChunks, kb = p * PB + (chunk % kRowChunks) * 16;
+      bt.x[c] = bld16(xr, kb < 2 * K ? (u32)(row * 2 * K + kb) : kOOB);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // scales and zero points of the workgroup's 16 NB rows, with the first
+  // weight batch issued behind their loads
+  const int wg_rows = max(0, min(16 * NB, N - wg_row0));
+  const rsrc_t sr = make_rsrc(wscale + (int64_t)min(wg_row0, N - 1) * G, (u32)(wg_rows * G * 2));
+  const rsrc_t zr = make_rsrc(wzero + (int64_t)min(wg_row0, N - 1) * G, (u32)(wg_rows * G * 2));
+  ScaleZeroStage<kThreads, 4> sz;
+  sz.load(sr, zr, 16 * NB * G, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  Batch b0, b1;
+  load(b0, 0);
+  sz.finish(sr, zr, szl, G, 16 * NB * G);
+
+  const u32* szrow = szl + (wave * 16 + r) * sz_pitch(G);
+  int8_t* tile = tiles[wave];
+  v4f yacc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) yacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto process = [&](const Batch& bt, int p) {
+    int8_t* buf = xbuf[p & 1];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int chunk = tid + c * kThreads;
+      if (kFull || chunk < kChunks)
+        st16(buf + (chunk / kRowChunks) * kPitch + (chunk % kRowChunks) * 16, shuffle_halves(bt.x[c]));
+    }
+    // Panel p (and, at p = 0, the scales) complete once every wave is here;
+    // the buffer phase p + 1 overwrites was last read at phase p - 1.
+    lds_barrier();
+#pragma unroll
+    for (int v = 0; v < PU; ++v) {
+      v4i f[2];
+      unit_transpose(tile, bt.w[v], ul, f);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int g = 2 * (p * PU + v) + s2;
+        const u32 szw = g < G ? szrow[g] : 0u;     // past G: zero codes and scale
+        const float zf = f16_bits_to_f32((uint16_t)(szw >> 16));
+        v4i bw[4];
+        if constexpr (XDT == F16) {
+          const u32 zh = f32_to_f16_bits(1024.f + zf);
+          const u32 zz = zh | (zh << 16);
+#pragma unroll
+          for (int h = 0; h < 4; ++h) bw[h] = unpack_f16((u32)f[s2][h], zz);
+        } else {
+          const float zb = 8388608.f + zf;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) bw[h] = unpack_bf16((u32)f[s2][h], zb);
+        }
+        const float sc = f16_bits_to_f32((uint16_t)(szw & 0xFFFFu));
+        const int kin = 512 * v + 256 * s2 + 64 * j;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int8_t* xf = buf + (16 * mt + r) * kPitch + kin;
+          v4f pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const v4i a = ld16(xf + 16 * h);
+            if constexpr (XDT == F16)
+              pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
+                                                            __builtin_bit_cast(v8h, bw[h]), pacc, 0, 0, 0);
+            else
+              pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                             __builtin_bit_cast(v8bf, bw[h]), pacc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) yacc[mt][i] = __builtin_fmaf(sc, pacc[i], yacc[mt][i]);
+        }
+      }
+    }
+  };
+  for (int p = 0; p < phases; p += 2) {
+    load(b1, p + 1);
+    process(b0, p);
+    load(b0, p + 2);
+    process(b1, p + 1);
+  }
+
+  const int n = n_base + r;
+  if (n < N) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * j + i;
+        if (m < M) y[(int64_t)m * N + n] = Out<OutT>::cvt(yacc[mt][i]);
+      }
+  }
+}
+
+template <int MT, int XDT, typename OutT>
+static void launch_w4a16_wide(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
+                              const uint16_t* wz, int M, int N, int K, OutT* y, size_t lds,
+                              hipStream_t st) {
+  constexpr int PU = MT == 1 ? 2 : 1;   // measured on MI355X (K = 4096, N = 12288)
+  const int nb = wide_waves(N), nblocks = (N + 15) / 16;
+  const dim3 grid((unsigned)((nblocks + nb - 1) / nb));
+  switch (nb) {
+    case 1: k_w4a16_wide<MT, 1, PU, XDT, OutT><<<grid, dim3(64), lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    case 2: k_w4a16_wide<MT, 2, PU, XDT, OutT><<<grid, dim3(128), lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    case 3: k_w4a16_wide<MT, 3, PU, XDT, OutT><<<grid, dim3(192), lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    default: k_w4a16_wide<MT, 4, PU, XDT, OutT><<<grid, dim3(256), lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+  }
+}
+
 template <int XDT, typename OutT>
 static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
                                const uint16_t* wz, int M, int N, int K, OutT* y, hipStream_t st) {
-  const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
-  const size_t lds = (size_t)mr * stage_pitch(2 * K) + (size_t)16 * sz_pitch(K / 128) * 4;
-  if (M <= 16 && lds <= kDecLdsMaxBytes) {
+  const int G = K / 128;
+  const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+  const size_t lds = (size_t)mr * stage_pitch(2 * K) + (size_t)16 * sz_pitch(G) * 4;
+  if (M <= 8 && lds <= kDecLdsMaxBytes) {
     constexpr int WAVES = 4, UB = 1;  // measured on MI355X
     const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
     switch (mr) {
       case 1: k_w4a16_dec<1, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
       case 2: k_w4a16_dec<2, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
       case 4: k_w4a16_dec<4, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-      case 8: k_w4a16_dec<8, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-      default: k_w4a16_dec<16, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+      default: k_w4a16_dec<8, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
     }
+    return hipGetLastError();
+  }
+  const size_t lds_wide = (size_t)16 * wide_waves(N) * sz_pitch(G) * 4;
+  if (M <= 64 && lds_wide <= kDecLdsMaxBytes) {
+    if (M <= 16) launch_w4a16_wide<1, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
+    else if (M <= 32) launch_w4a16_wide<2, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
+    else if (M <= 48) launch_w4a16_wide<3, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
+    else launch_w4a16_wide<4, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
     return hipGetLastError();
   }
   constexpr int MT = 1, NT = 1, WAVES = 8, U = 2;  // measured on MI355X

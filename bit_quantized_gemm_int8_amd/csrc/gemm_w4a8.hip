@@ -271,7 +271,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec(
   ScaleZeroStage<kThreads, 4> sz;
   const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
   const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
-  sz.load(sr, zr, G, 0);
+  sz.load(sr, zr, 16 * G, 0);
   __builtin_amdgcn_sched_barrier(0);
   load(b0, ub);
   float sx[4] = {0.f, 0.f, 0.f, 0.f};
@@ -282,11 +282,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec(
       sx[i] = xs[m < M ? m : M - 1];
     }
   }
-  sz.store(szl, G);
-  for (int c0 = 4 * kThreads; c0 < 16 * G; c0 += 4 * kThreads) {
-    sz.load(sr, zr, G, c0);
-    sz.store(szl, G);
-  }
+  sz.finish(sr, zr, szl, G, 16 * G);
   lds_barrier();
 
   const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};

@@ -4,17 +4,17 @@
 // 「LLM推理降本五要素」 §2.1 (at decode the layer waits on weight bandwidth).
 //
 // Three kernels:
-//  * decode (M <= 16, token rows fit LDS): the weight stream is the whole
+//  * decode (M <= 8, token rows fit LDS): the weight stream is the whole
 //    cost.  Whole-line weight units transposed through LDS into MFMA
-//    operands, token rows staged once per workgroup (qg_decode.hpp).
-//  * small M (other M <= 64): weights go straight from HBM into MFMA operand
-//    registers (16-byte buffer loads, two batches in flight per lane); the K
-//    loop is split across the waves of a workgroup and the int32 partials
-//    meet in LDS (exact, order-free).
+//    operands, token rows staged once per workgroup (qg_decode.hpp); the K
+//    loop is split across the waves and the int32 partials meet in LDS.
+//  * wide decode (M <= 64): one 16-row weight block per wave over the whole
+//    K, several blocks per workgroup sharing each phase's token-row panel.
 //  * large M (prefill): 256x256 output tiles, K in 128-byte stages brought
 //    into LDS by buffer-to-LDS DMA (two alternating stage buffers, XOR-swizzled
 //    16-byte chunks), 4 waves each owning a 128x128 sub-tile of 32x32x32 int8
 //    MFMAs.
+#include <algorithm>
 #include <array>
 #include <type_traits>
 
@@ -31,48 +31,6 @@ __device__ __forceinline__ OutT w8a8_epilogue(int acc, float sx, float sw) {
 template <>
 __device__ __forceinline__ int32_t w8a8_epilogue<int32_t>(int acc, float, float) {
   return acc;
-}
-
-// ---------------------------------------------------------------------------
-// Small-M kernel.  Workgroup = WAVES waves; it owns 16*NT output columns and
-// 16*MT rows.  Lane l of a wave feeds MFMA row/column (l & 15) and the 16-byte
-// k-slice (l >> 4) of each 64-deep step, from memory in the same order for
-// both operands, so the int8 products pair up whatever order the matrix core
-// sums them in.  Each wave walks its share of K in batches of U steps and
-// keeps two batches of loads in flight (the next batch is issued before the
-// current one is multiplied).
-// ---------------------------------------------------------------------------
-template <int MT, int NT, int U>
-struct SmallMBatch {
-  v4i b[U][NT], a[U][MT];
-};
-
-template <int MT, int NT, int U>
-__device__ __forceinline__ void small_m_load(SmallMBatch<MT, NT, U>& bt, int s0, int se, int K,
-                                             int kq, rsrc_t wr, const u32 (&woff)[NT], rsrc_t xr,
-                                             const u32 (&xoff)[MT]) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int k = (s0 + u) * 64;
-    const bool kin = (s0 + u < se) && (k + kq < K);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) bt.b[u][t] = bld16_nt(wr, kin ? woff[t] + k : kOOB);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) bt.a[u][mt] = bld16(xr, kin ? xoff[mt] + k : kOOB);
-  }
-  // keep the whole batch of loads ahead of the multiplies that follow
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-template <int MT, int NT, int U>
-__device__ __forceinline__ void small_m_mma(const SmallMBatch<MT, NT, U>& bt, v4i (&acc)[MT][NT]) {
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[mt][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bt.a[u][mt], bt.b[u][t], acc[mt][t], 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -169,68 +127,112 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
   }
 }
 
-template <int MT, int NT, int WAVES, int U, typename OutT>
-__global__ __launch_bounds__(64 * WAVES) void k_w8a8_small_m(
+// ---------------------------------------------------------------------------
+// Wide decode kernel (up to 64 token rows, MT m-tiles of 16): a workgroup of
+// NB waves owns NB x 16 weight rows; wave w streams its own 16 rows over the
+// whole K as whole-line units, and the waves move through K in phases of PU
+// units.  A phase's panel of token rows (16 MT rows x 128 PU bytes) is staged
+// in LDS once for all NB waves (two-deep ring, one barrier per phase), so one
+// token-row byte read from L2 serves 16 NB weight rows.  Every wave owns its
+// outputs whole: no cross-wave reduction.
+// ---------------------------------------------------------------------------
+template <int MT, int NB, int PU, typename OutT>
+__global__ __launch_bounds__(64 * NB) void k_w8a8_wide(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, const int8_t* __restrict__ wq,
     const float* __restrict__ ws, int M, int N, int K, OutT* __restrict__ y) {
-  __shared__ v4i red[WAVES][MT][NT][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, kq = (lane >> 4) * 16;
-  const int n_base = blockIdx.x * 16 * NT;
-  const int m_base = blockIdx.y * 16 * MT;
-  const int steps = (K + 63) >> 6;
-  const int sb = (int)((int64_t)steps * wave / WAVES);
-  const int se = (int)((int64_t)steps * (wave + 1) / WAVES);
+  constexpr int MR = 16 * MT, PB = kUnitBytes * PU, kThreads = 64 * NB;
+  constexpr int kPitch = PB + 16;                      // odd number of 16-byte chunks
+  constexpr int kRowChunks = PB / 16, kChunks = MR * kRowChunks;
+  constexpr int CPT = (kChunks + kThreads - 1) / kThreads;
+  constexpr bool kFull = CPT * kThreads == kChunks;
+  __shared__ __attribute__((aligned(16))) int8_t xbuf[2][MR * kPitch];
+  __shared__ __attribute__((aligned(16))) int8_t tiles[NB][kTileBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int n_base = (blockIdx.x * NB + wave) * 16;
+  const int units = (K + kUnitBytes - 1) / kUnitBytes;
+  const int phases = (units + PU - 1) / PU;
 
-  // buffer resources cover exactly this workgroup's weight rows and token
-  // rows; rows past N or M read as zeros
-  const int rows_n = min(16 * NT, N - n_base), rows_m = min(16 * MT, M - m_base);
-  const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * K, (u32)(rows_n * K));
-  const rsrc_t xr = make_rsrc(xq + (int64_t)m_base * K, (u32)(rows_m * K));
-  u32 woff[NT], xoff[MT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) woff[t] = (u32)((16 * t + r) * K + kq);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) xoff[mt] = (u32)((16 * mt + r) * K + kq);
+  // rows past N (including a whole wave's block past N) read zeros
+  const int rows_n = max(0, min(16, N - n_base));
+  const rsrc_t wr = make_rsrc(wq + (int64_t)min(n_base, N - 1) * K, (u32)(rows_n * K));
+  const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
+  const UnitLanes ul = unit_lanes(lane, K);
 
-  v4i acc[MT][NT];
+  struct Batch {
+    v4i w[PU][2], x[CPT];
+  };
+  auto load = [&](Batch& bt, int p) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int v = 0; v < PU; ++v) unit_load(bt.w[v], wr, ul, p * PU + v, true, K);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[mt][t] = v4i{0, 0, 0, 0};
+    for (int c = 0; c < CPT; ++c) {
+      const int chunk = tid + c * kThreads;
+      const int row = chunk / kRowChunks, kb = p * PB + (chunk % kRowChunks) * 16;
+      // rows >= M fall past the end of the resource and read zeros
+      bt.x[c] = bld16(xr, kb < K ? (u32)(row * K + kb) : kOOB);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // Branch-free software pipeline: loads past this wave's range read zeros
-  // (and multiply to zero), so the outstanding-load count is the same on
-  // every path and each batch waits only for its own loads.
-  SmallMBatch<MT, NT, U> p0, p1;
-  small_m_load(p0, sb, se, K, kq, wr, woff, xr, xoff);
-  for (int s0 = sb; s0 < se; s0 += 2 * U) {
-    small_m_load(p1, s0 + U, se, K, kq, wr, woff, xr, xoff);
-    small_m_mma(p0, acc);
-    small_m_load(p0, s0 + 2 * U, se, K, kq, wr, woff, xr, xoff);
-    small_m_mma(p1, acc);
+  int8_t* tile = tiles[wave];
+  v4i acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4i{0, 0, 0, 0};
+  auto process = [&](const Batch& bt, int p) {
+    int8_t* buf = xbuf[p & 1];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int chunk = tid + c * kThreads;
+      if (kFull || chunk < kChunks)
+        st16(buf + (chunk / kRowChunks) * kPitch + (chunk % kRowChunks) * 16, bt.x[c]);
+    }
+    // Panel p is complete once every wave is here; the buffer phase p + 1
+    // overwrites was last read at phase p - 1, before this barrier.
+    lds_barrier();
+#pragma unroll
+    for (int v = 0; v < PU; ++v) {
+      v4i f[2];
+      unit_transpose(tile, bt.w[v], ul, f);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        // past K the weight operand is zero; keep the panel read in range
+        const int kin = kUnitBytes * v + 64 * s2 + 16 * j;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const v4i a = ld16(buf + (16 * mt + r) * kPitch + kin);
+          acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, f[s2], acc[mt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  Batch b0, b1;
+  load(b0, 0);
+  const int n_out = n_base + r;
+  float sw = 0.f;
+  if constexpr (!std::is_same<OutT, int32_t>::value) sw = ws[n_out < N ? n_out : N - 1];
+  // every wave runs the same number of phases, so all reach every barrier
+  for (int p = 0; p < phases; p += 2) {
+    load(b1, p + 1);
+    process(b0, p);
+    load(b0, p + 2);
+    process(b1, p + 1);
   }
 
+  if (n_out < N) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) red[wave][mt][t][lane] = acc[mt][t];
-  __syncthreads();
-
-  // 16x16 accumulator layout: lane l holds column (l & 15), rows 4*(l >> 4) + i.
-  for (int it = threadIdx.x; it < MT * NT * 64; it += 64 * WAVES) {
-    const int l = it & 63, t = (it >> 6) % NT, mt = (it >> 6) / NT;
-    v4i sum = red[0][mt][t][l];
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) sum += red[w][mt][t][l];
-    const int n = n_base + 16 * t + (l & 15);
-    if (n >= N) continue;
-    const float sw = ws ? ws[n] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m_base + 16 * mt + 4 * (l >> 4) + i;
-      if (m < M) y[(int64_t)m * N + n] = w8a8_epilogue<OutT>(sum[i], xs ? xs[m] : 0.f, sw);
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * j + i;
+        if (m < M) {
+          float sx = 0.f;
+          if constexpr (!std::is_same<OutT, int32_t>::value) sx = xs[m];
+          y[(int64_t)m * N + n_out] = w8a8_epilogue<OutT>(acc[mt][i], sx, sw);
+        }
+      }
   }
 }
 
@@ -519,32 +521,46 @@ __global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict
 }
 
 constexpr int kPrefillWaves = 8;
+template <int MT, typename OutT>
+static void launch_w8a8_wide(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
+                             int M, int N, int K, OutT* y, hipStream_t st) {
+  constexpr int PU = MT <= 2 ? 4 : 2;   // measured on MI355X (K = 4096, N = 11008)
+  const int nb = wide_waves(N), nblocks = (N + 15) / 16;
+  const dim3 grid((unsigned)((nblocks + nb - 1) / nb));
+  switch (nb) {
+    case 1: k_w8a8_wide<MT, 1, PU, OutT><<<grid, dim3(64), 0, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+    case 2: k_w8a8_wide<MT, 2, PU, OutT><<<grid, dim3(128), 0, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+    case 3: k_w8a8_wide<MT, 3, PU, OutT><<<grid, dim3(192), 0, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+    default: k_w8a8_wide<MT, 4, PU, OutT><<<grid, dim3(256), 0, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+  }
+}
+
 template <typename OutT>
 static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* wq,
                               const float* ws, int M, int N, int K, OutT* y, hipStream_t st) {
   if (M <= 64) {
     // shapes picked by measurement on MI355X (decode, K = 4096, N = 11008)
-    constexpr int WAVES = 4, NT = 1;
-    dim3 block(64 * WAVES);
-    const unsigned gx = (unsigned)((N + 16 * NT - 1) / (16 * NT));
-    const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+    constexpr int WAVES = 4;
+    const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
     const size_t lds = (size_t)mr * stage_pitch(K);
-    if (M <= 16 && lds <= kDecLdsMaxBytes) {
+    if (M <= 8 && lds <= kDecLdsMaxBytes) {
       constexpr int UB = 2;
-      const dim3 grid(gx, 1);
+      const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
       switch (mr) {
         case 1: k_w8a8_dec<1, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
         case 2: k_w8a8_dec<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
         case 4: k_w8a8_dec<4, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-        case 8: k_w8a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-        default: k_w8a8_dec<16, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+        default: k_w8a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
       }
-    } else if (M <= 16)
-      k_w8a8_small_m<1, NT, WAVES, 8, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
-    else if (M <= 32)
-      k_w8a8_small_m<2, NT, WAVES, 4, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
-    else
-      k_w8a8_small_m<4, NT, WAVES, 2, OutT><<<dim3(gx, 1), block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
+    } else if (M <= 16) {
+      launch_w8a8_wide<1, OutT>(xq, xs, wq, ws, M, N, K, y, st);
+    } else if (M <= 32) {
+      launch_w8a8_wide<2, OutT>(xq, xs, wq, ws, M, N, K, y, st);
+    } else if (M <= 48) {
+      launch_w8a8_wide<3, OutT>(xq, xs, wq, ws, M, N, K, y, st);
+    } else {
+      launch_w8a8_wide<4, OutT>(xq, xs, wq, ws, M, N, K, y, st);
+    }
   } else {
     const int tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
     // whole-line stores need every row of y to start on a 16-byte boundary

@@ -130,37 +130,56 @@ __device__ __forceinline__ void stage_rows(int8_t* dst, rsrc_t src, int row_byte
   }
 }
 
-// Scale and zero point of the 16 weight rows of a workgroup (G groups, fp16
-// bits) staged in LDS as words s | z << 16 at pitch G + 1, an odd number of
-// words, so that the 16 rows of one group read hit 16 different banks.
-// EPT elements per thread are loaded per round, all before their stores.
+// Scale and zero point of the weight rows of a workgroup (`rows` rows of G
+// groups, fp16 bits, contiguous in global memory) staged in LDS as words
+// s | z << 16 at pitch G + 1, an odd number of words, so that the 16 rows of
+// one group read hit 16 different banks.  EPT elements per thread are loaded
+// per round, all before their stores.  Elements past the buffer resources'
+// ends read as zeros.
 __host__ __device__ constexpr int sz_pitch(int G) { return G + 1; }
 
 template <int THREADS, int EPT>
 struct ScaleZeroStage {
   uint16_t s[EPT], z[EPT];
   int e0;
-  __device__ __forceinline__ void load(rsrc_t sr, rsrc_t zr, int G, int c0) {
+  __device__ __forceinline__ void load(rsrc_t sr, rsrc_t zr, int total, int c0) {
     e0 = c0;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       const int e = c0 + (int)threadIdx.x + i * THREADS;
-      const bool in = e < 16 * G;   // rows past the resource's end read zeros
-      s[i] = bld2(sr, in ? (u32)(2 * e) : kOOB);
-      z[i] = bld2(zr, in ? (u32)(2 * e) : kOOB);
+      s[i] = bld2(sr, e < total ? (u32)(2 * e) : kOOB);
+      z[i] = bld2(zr, e < total ? (u32)(2 * e) : kOOB);
     }
   }
-  __device__ __forceinline__ void store(u32* dst, int G) const {
+  __device__ __forceinline__ void store(u32* dst, int G, int total) const {
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       const int e = e0 + (int)threadIdx.x + i * THREADS;
-      if (e < 16 * G) {
+      if (e < total) {
         const int row = e / G;
         dst[row * sz_pitch(G) + (e - row * G)] = (u32)s[i] | ((u32)z[i] << 16);
       }
     }
   }
+  // all rows: first round issued by the caller (so it can overlap other
+  // loads), the rest here
+  __device__ __forceinline__ void finish(rsrc_t sr, rsrc_t zr, u32* dst, int G, int total) {
+    store(dst, G, total);
+    for (int c0 = EPT * THREADS; c0 < total; c0 += EPT * THREADS) {
+      load(sr, zr, total, c0);
+      store(dst, G, total);
+    }
+  }
 };
+
+// Waves (16-row weight blocks) per workgroup of the wide decode kernels: the
+// grid should come out near one workgroup per CU (256 on MI355X), so that the
+// token rows are read by as few workgroups as the weight stream allows.
+inline int wide_waves(int N) {
+  const int nblocks = (N + 15) / 16;
+  const int nb = (nblocks + 128) / 256;
+  return nb < 1 ? 1 : nb > 4 ? 4 : nb;
+}
 
 // Barrier for LDS data written by the workgroup: waits for this wave's LDS
 // accesses only, leaving its global loads in flight.

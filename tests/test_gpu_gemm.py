@@ -24,7 +24,10 @@ W8A8_SHAPES = [(16, 512, 512), (1, 16, 16), (3, 17, 48), (8, 11008, 4096), (17, 
                (300, 520, 1040), (257, 1000, 1936),
                # decode kernel: odd 16-byte chunk count per row (LDS pitch), several
                # token-row staging rounds, and a K whose rows overflow the LDS budget
-               (5, 33, 4112), (12, 100, 9008), (16, 40, 8192)]
+               (5, 33, 4112), (12, 100, 9008), (16, 40, 8192),
+               # wide decode kernel: three weight blocks per workgroup with the last
+               # workgroup partly past N, and the full 64-token FFN-up shape
+               (40, 10256, 512), (64, 11008, 4096)]
 
 
 def _codes(rng, shape):
@@ -158,7 +161,7 @@ def _w4a16_floor(x64, packed, sc, zz):
 @pytest.mark.parametrize("xfmt", ["f16", "bf16"])
 @pytest.mark.parametrize("fmt", ["f16", "f32", "bf16"])
 @pytest.mark.parametrize("M,N,K", [(1, 12288, 4096), (5, 17, 256), (16, 300, 1024), (33, 40, 640),
-                                   (2, 48, 14336)])
+                                   (2, 48, 14336), (48, 10256, 512), (64, 512, 4096)])
 def test_w4a16(xfmt, fmt, M, N, K):
     rng = np.random.default_rng(M * 5 + N + K)
     packed, sc, zz = _u4_weights(rng, K, N)
