@@ -368,10 +368,15 @@ def batch_sweep(steps):
 # (rocprofv3 leaves names with _Float16 mangled, hence the alternatives)
 KERNEL_OF = {
     "w8a8_decode_ffn_up": [("k_w8a8_dec<8,", "unsigned short>")],
-    "w8a8_tiny": [("k_w8a8_dec<16,", "float>")],
+    "w8a8_tiny": [("k_w8a8_wide<1,", "float>")],
     "w4a8_ffn_down": [("k_w4a8_dec<16,", "unsigned short>")],
     "w4a16_qkv": [("k_w4a16_dec<1,", "_Float16>"), ("k_w4a16_decILi1E", "DF16_E")],
     "w8a8_prefill": [("k_w8a8_tiled<", "unsigned short>")],
+}
+# profile file label of each workload's dominant kernel
+KERNEL_LABEL = {
+    "w8a8_decode_ffn_up": "gemm_w8a8_dec", "w8a8_tiny": "gemm_w8a8_wide",
+    "w4a8_ffn_down": "gemm_w4a8_dec", "w4a16_qkv": "gemm_w4a16_dec", "w8a8_prefill": "gemm_w8a8_tiled",
 }
 COPY_BYTES = 512 * 2 ** 20
 PROFILE_COMMANDS = """\
@@ -446,8 +451,7 @@ def ingest_counters(d):
     for key, rec in out.items():
         path, wl_name = key.split(":")
         wl = by_name(wl_name)
-        kname = {"w8a8": "gemm_w8a8_dec" if wl.M <= 16 else "gemm_w8a8_tiled",
-                 "w4a8": "gemm_w4a8_g128", "w4a16": "gemm_w4a16_g128"}[path]
+        kname = KERNEL_LABEL[wl_name]
         fn = os.path.join(ROOT, "profiles", f"{kname}.{wl_name}.md")
         avg = rec["avg_ns"]
         lines = [f"# {kname} on {wl_name} (M={wl.M}, K={wl.K}, N={wl.N})", "",
