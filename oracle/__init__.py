@@ -19,7 +19,8 @@ Sources (cited by page title and section):
   §2.2 (SmoothQuant fold), §3.2-3.3 (4-bit, group 128, zero point configs);
   「Quantization & Flash Attention」 §2.2-2.3 (AWQ per-channel fold);
   「LLM推理降本五要素」 §2.2 (group-wise W4A8 with per-group scale and zero),
-  §5.2 (round-then-clamp to int8).
+  §5.2 (round-then-clamp to int8; KV-cache position segments of 128 tokens
+  with per-channel scales).
 
 Parity status: every function here is pinned by tests/test_oracle_*.py
 against closed forms, invariants, brute force on tiny inputs and the
@@ -40,3 +41,4 @@ __all__ = [
     "gemm_w4a16_g128_partials", "gemm_w4a16_g128",
     "smoothquant_scales", "awq_scales", "fold_weight", "fold_activation",
 ]
+from .kv import quantize_kv_segments, dequantize_kv_segments
