@@ -13,7 +13,8 @@ rather than from the 256 MB last-level cache.
 
 The JSON line reports the headline workload (W8A8 decode FFN-up, M=8,
 K=4096, N=11008) in HBM TB/s, with a "workloads" list holding every workload
-(including the M=4096 prefill in INT8 TOP/s), each with the roofline of its
+(including the M=4096 prefill in INT8 TOP/s, and the KV-cache INT8 quantizer
+on one layer's 4096-position Llama-2-7B cache), each with the roofline of its
 dominant kernel.  `roofline.traffic` is taken from profiles/traffic.json
 (rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a copy-kernel calibration) when
 it was measured on the current kernel sources, else null.
@@ -35,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantized GEMM: HBM TB/s at M≤16, INT8 TOPS at M=4096, % of roofline"
 HEADLINE = "w8a8_decode_ffn_up"
+BENCH_KV = ("kv_llama2_7b_4k",)   # KV-cache workloads in the default run
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA
 F16_PEAK_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
@@ -44,6 +46,7 @@ KERNEL_SOURCES = {
     "w4a8": ["gemm_w4a8.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a16": ["gemm_w4a16.hip", "qg_decode.hpp", "qg_device.hpp"],
     "quant": ["quant.hip", "qg_device.hpp"],
+    "kv": ["kv.hip", "qg_device.hpp"],
 }
 
 
@@ -99,6 +102,104 @@ def algorithmic(wl):
     quant = x_b * M * K + M * K + 4 * M if wl.path != "w4a16" else 0
     ops = 2 * M * N * K
     return gemm, quant, ops
+
+
+def kv_algorithmic(wl):
+    """Bytes the KV-cache quantizer and dequantizer must move per call: the
+    cache in its storage format, the int8 codes and the fp32 scales, each
+    once."""
+    el = wl.T * wl.H * wl.D
+    x_b = {"f32": 4, "bf16": 2, "f16": 2}[wl.dtype]
+    scales = 4 * wl.H * ((wl.T + 127) // 128) * wl.D
+    return x_b * el + el + scales, el + scales + x_b * el
+
+
+def run_kv(wl, steps, warmup, traffic_db):
+    """KV-cache INT8 quantization of one layer's [T][H][D] cache (and its
+    dequantization), each timed as a captured graph of `steps` calls rotating
+    over more than 600 MB of cache copies."""
+    import numpy as np
+    import torch
+    import bit_quantized_gemm_int8_amd as qg
+    from workloads import draw_kv, f32_to_bf16_bits, f32_to_f16
+
+    dev = "cuda"
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+    print(f"[bench] {wl.name}: T={wl.T} H={wl.H} D={wl.D} preparing", file=sys.stderr, flush=True)
+    x = draw_kv(wl)
+    if wl.dtype == "bf16":
+        kv = torch.from_numpy(f32_to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    elif wl.dtype == "f16":
+        kv = torch.from_numpy(f32_to_f16(x)).to(dev)
+    else:
+        kv = torch.from_numpy(x).to(dev)
+    del x
+    q_b, dq_b = kv_algorithmic(wl)
+    R = max(2, math.ceil(ROTATE_BYTES / q_b))
+    S = (wl.T + 127) // 128
+    ins = [kv] + [kv.clone() for _ in range(R - 1)]
+    codes = [torch.empty((wl.T, wl.H, wl.D), dtype=torch.int8, device=dev) for _ in range(R)]
+    scales = [torch.empty((wl.H, S, wl.D), dtype=torch.float32, device=dev) for _ in range(R)]
+    outs = [torch.empty_like(kv) for _ in range(R)]
+
+    def quant(i):
+        qg.quantize_kv_i8_segments(ins[i % R], out=(codes[i % R], scales[i % R]))
+
+    def dequant(i):
+        qg.dequantize_kv_i8_segments(codes[i % R], scales[i % R], out_dtype=kv.dtype,
+                                     out=outs[i % R])
+
+    for i in range(R):
+        quant(i)
+    torch.cuda.synchronize()
+    c_ref, s_ref = codes[0].clone(), scales[0].clone()
+
+    def capture(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        return g
+
+    def timed(g):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    g_warm = capture(quant, max(warmup, 1))
+    g_q = capture(quant, steps)
+    g_dq = capture(dequant, steps)
+    g_warm.replay()
+    q_s = timed(g_q)
+    dq_s = timed(g_dq)
+    for i in range(R):
+        if not (torch.equal(codes[i], c_ref) and torch.equal(scales[i], s_ref)):
+            raise RuntimeError(f"{wl.name}: replayed codes differ from the eager result")
+    q_us, dq_us = q_s / steps * 1e6, dq_s / steps * 1e6
+    achieved = q_b / (q_us * 1e-6) / 1e9
+    tr = traffic_db.get("kv:" + wl.name)
+    traffic = tr["bytes_per_launch"] if tr and tr.get("source_sha") == source_sha("kv") else None
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    res = {
+        "workload": wl.name, "path": "kv_i8_segments", "T": wl.T, "H": wl.H, "D": wl.D,
+        "x_dtype": wl.dtype, "value": round(q_b / (q_us * 1e-6) / 1e12, 4), "unit": "TB/s",
+        "ms_per_step": round(q_us / 1e3, 5),
+        "quant_us": round(q_us, 3), "dequant_us": round(dq_us, 3),
+        "quant_bytes": q_b, "dequant_bytes": dq_b,
+        "dequant_TBps": round(dq_b / (dq_us * 1e-6) / 1e12, 4),
+        "copies": R, "roofline": roof,
+    }
+    print(f"[bench] {wl.name}: quant {q_us:.2f} us ({roof['achieved']} GB/s, "
+          f"{100 * roof['frac']:.1f}% of peak), dequant {dq_us:.2f} us "
+          f"({res['dequant_TBps']} TB/s)", file=sys.stderr, flush=True)
+    del ins, codes, scales, outs, g_warm, g_q, g_dq
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_workload(wl, steps, warmup, traffic_db):
@@ -372,11 +473,13 @@ KERNEL_OF = {
     "w4a8_ffn_down": [("k_w4a8_dec<16,", "unsigned short>")],
     "w4a16_qkv": [("k_w4a16_dec<1,", "_Float16>"), ("k_w4a16_decILi1E", "DF16_E")],
     "w8a8_prefill": [("k_w8a8_tiled<", "unsigned short>")],
+    "kv_llama2_7b_4k": [("k_kv_quant_seg<2, 8>",)],
 }
 # profile file label of each workload's dominant kernel
 KERNEL_LABEL = {
     "w8a8_decode_ffn_up": "gemm_w8a8_dec", "w8a8_tiny": "gemm_w8a8_wide",
     "w4a8_ffn_down": "gemm_w4a8_dec", "w4a16_qkv": "gemm_w4a16_dec", "w8a8_prefill": "gemm_w8a8_tiled",
+    "kv_llama2_7b_4k": "kv_quant_seg",
 }
 COPY_BYTES = 512 * 2 ** 20
 PROFILE_COMMANDS = """\
@@ -397,6 +500,18 @@ def _match(name, alternatives):
     return any(all(p in name for p in pats) for pats in alternatives)
 
 
+def _profiled(name):
+    """(algorithmic bytes, ops, source key, shape text) of a profiled workload."""
+    from workloads import KV_WORKLOADS, by_name
+    kv = {w.name: w for w in KV_WORKLOADS}
+    if name in kv:
+        wl = kv[name]
+        return kv_algorithmic(wl)[0], 0, "kv", f"T={wl.T}, H={wl.H}, D={wl.D}, {wl.dtype}"
+    wl = by_name(name)
+    gemm_b, _, ops = algorithmic(wl)
+    return gemm_b, ops, wl.path, f"M={wl.M}, K={wl.K}, N={wl.N}"
+
+
 def ingest_counters(d):
     """rocprofv3 CSVs -> profiles/traffic.json + per-kernel summaries.
 
@@ -406,7 +521,6 @@ def ingest_counters(d):
     what the same counter reads for the 512 MiB device copy.
     """
     import glob
-    from workloads import by_name
     stats = _csv_rows(glob.glob(os.path.join(d, "stats", "*kernel_stats.csv"))[0])
     per = {}
     for ctr, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
@@ -422,8 +536,7 @@ def ingest_counters(d):
         per[ctr] = (vals, factor, len(copy))
     out, lines = {}, []
     for wl_name, pats in KERNEL_OF.items():
-        wl = by_name(wl_name)
-        gemm_b, quant_b, ops = algorithmic(wl)
+        gemm_b, ops, key, _ = _profiled(wl_name)
         srow = next((r for r in stats if _match(r["Name"], pats)), None)
         rec = {"kernel": srow["Name"].split("(")[0] if srow else None,
                "calls": int(srow["Calls"]) if srow else 0,
@@ -442,19 +555,19 @@ def ingest_counters(d):
             rec[ctr.lower() + "_copy_factor"] = round(factor, 4)
             total += mean_kib * 1024 * factor
         rec["bytes_per_launch"] = round(total) if ok else None
-        rec["source_sha"] = source_sha(wl.path)
-        out[wl.path + ":" + wl_name] = rec
+        rec["source_sha"] = source_sha(key)
+        out[key + ":" + wl_name] = rec
         lines.append(rec)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
     for key, rec in out.items():
         path, wl_name = key.split(":")
-        wl = by_name(wl_name)
+        shape = _profiled(wl_name)[3]
         kname = KERNEL_LABEL[wl_name]
         fn = os.path.join(ROOT, "profiles", f"{kname}.{wl_name}.md")
         avg = rec["avg_ns"]
-        lines = [f"# {kname} on {wl_name} (M={wl.M}, K={wl.K}, N={wl.N})", "",
+        lines = [f"# {kname} on {wl_name} ({shape})", "",
                  "rocprofv3 summary of the benchmark's dominant kernel for this workload.", "",
                  "Commands (repository root as $REPO, an output directory as $OUT, one MI355X):", "", "```",
                  PROFILE_COMMANDS, "```", "",
@@ -493,6 +606,19 @@ def ingest_counters(d):
     print(json.dumps(out, indent=1))
 
 
+def _config(head):
+    if "T" in head:   # a KV-cache workload run on its own
+        return {"workload": head["workload"], "T": head["T"], "H": head["H"], "D": head["D"],
+                "x_dtype": head["x_dtype"],
+                "step": "quantize_kv_i8_segments (captured HIP graph)",
+                "parallelism": "single GPU"}
+    return {"workload": head["workload"], "M": head["M"], "K": head["K"], "N": head["N"],
+            "x_dtype": head["x_dtype"], "out_dtype": head["out_dtype"],
+            "step": ("quantize_per_token_i8 + gemm_w8a8" if head["path"] != "w4a16"
+                     else "gemm_w4a16_g128") + " (captured HIP graph)",
+            "parallelism": "single GPU"}
+
+
 def main():
     args = parse()
     if args.batch_sweep:
@@ -507,16 +633,19 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
-    from workloads import WORKLOADS, by_name
+    from workloads import KV_WORKLOADS, WORKLOADS, by_name
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import bit_quantized_gemm_int8_amd as qg
     qg.load()
-    names = [w.name for w in WORKLOADS] if args.workloads == "all" else args.workloads.split(",")
+    kv_wls = {w.name: w for w in KV_WORKLOADS if w.name in BENCH_KV}
+    names = [w.name for w in WORKLOADS] + list(kv_wls) if args.workloads == "all" \
+        else args.workloads.split(",")
     names = sorted(names, key=lambda n: n != HEADLINE)
     traffic_db = load_traffic()
-    results = [run_workload(by_name(n), args.steps, args.warmup, traffic_db) for n in names]
+    results = [run_kv(kv_wls[n], args.steps, args.warmup, traffic_db) if n in kv_wls
+               else run_workload(by_name(n), args.steps, args.warmup, traffic_db) for n in names]
     if args.copy_calib:
         copy_calibration()
     head = next((r for r in results if r["workload"] == HEADLINE), results[0])
@@ -529,10 +658,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic (seeded; Llama-2-7B-shaped layers, no trained weights)",
-        "config": {"workload": head["workload"], "M": head["M"], "K": head["K"], "N": head["N"],
-                   "x_dtype": head["x_dtype"], "out_dtype": head["out_dtype"],
-                   "step": "quantize_per_token_i8 + gemm_w8a8 (captured HIP graph)",
-                   "parallelism": "single GPU"},
+        "config": _config(head),
         "roofline": head["roofline"], "cpu_baseline": cpu,
         "workloads": results,
     }

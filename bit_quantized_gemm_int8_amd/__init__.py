@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
   gemm_w4a16_g128(x, wq, w_scale, w_zero, out_dtype)
   smoothquant_fold(x_cal, w) / awq_fold(x_cal, w) -> (s f32 [K], w_folded f32 [K,N])
   apply_smoothing(x, s, out_dtype)
+  quantize_kv_i8_segments(kv)                   -> (kv_q int8 [T,H,D], kv_scale f32 [H,ceil(T/128),D])
+  dequantize_kv_i8_segments(kv_q, kv_scale, out_dtype) -> [T,H,D]
 """
 from __future__ import annotations
 
@@ -29,6 +31,7 @@ __all__ = [
     "quantize_per_token_i8", "quantize_weight_i8_per_channel", "quantize_weight_u4_g128",
     "gemm_w8a8", "gemm_w4a8_g128", "gemm_w4a16_g128",
     "smoothquant_fold", "awq_fold", "apply_smoothing", "status_string",
+    "quantize_kv_i8_segments", "dequantize_kv_i8_segments", "KV_SEGMENT",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemm.so")
@@ -48,6 +51,8 @@ _SIGNATURES = {
     "smoothquant_fold": [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp],
     "awq_fold": [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp],
     "apply_smoothing": [_vp, _i64, _i64, _vp, _vp, _int, _vp],
+    "quantize_kv_i8_segments": [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp],
+    "dequantize_kv_i8_segments": [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -223,4 +228,41 @@ def apply_smoothing(x: torch.Tensor, s: torch.Tensor, out_dtype=torch.bfloat16):
     M, K = x.shape
     y = torch.empty((M, K), dtype=out_dtype, device=x.device)
     _call("apply_smoothing", px, M, K, ps, y.data_ptr(), _DTYPE_CODE[out_dtype], _stream())
+    return y
+
+
+KV_SEGMENT = 128   # positions per KV-cache scale segment
+
+
+def quantize_kv_i8_segments(kv: torch.Tensor, out=None):
+    """kv [T, H, D] (f32/f16/bf16) -> (kv_q int8 [T, H, D],
+    kv_scale f32 [H, ceil(T/128), D]): one scale per head, 128-position
+    segment and channel."""
+    pk = _dev(kv, "kv", _FLOATS)
+    if kv.dim() != 3:
+        raise ValueError("kv must be [T, H, D]")
+    T, H, D = kv.shape
+    S = (T + KV_SEGMENT - 1) // KV_SEGMENT
+    kq, ks = out if out is not None else (None, None)
+    kq = _out(kq, (T, H, D), torch.int8, kv.device)
+    ks = _out(ks, (H, S, D), torch.float32, kv.device)
+    _call("quantize_kv_i8_segments", pk, _DTYPE_CODE[kv.dtype], T, H, D, kq.data_ptr(),
+          ks.data_ptr(), _stream())
+    return kq, ks
+
+
+def dequantize_kv_i8_segments(kv_q: torch.Tensor, kv_scale: torch.Tensor,
+                              out_dtype=torch.bfloat16, out=None):
+    """kv_q int8 [T, H, D] * kv_scale [H, t // 128, D] -> [T, H, D] of out_dtype."""
+    pq = _dev(kv_q, "kv_q", (torch.int8,))
+    ps = _dev(kv_scale, "kv_scale", (torch.float32,))
+    if kv_q.dim() != 3:
+        raise ValueError("kv_q must be [T, H, D]")
+    T, H, D = kv_q.shape
+    S = (T + KV_SEGMENT - 1) // KV_SEGMENT
+    if tuple(kv_scale.shape) != (H, S, D):
+        raise ValueError(f"kv_scale must be [{H}, {S}, {D}]")
+    y = _out(out, (T, H, D), out_dtype, kv_q.device)
+    _call("dequantize_kv_i8_segments", pq, ps, T, H, D, y.data_ptr(), _DTYPE_CODE[out_dtype],
+          _stream())
     return y

@@ -24,6 +24,15 @@ qg_status_t check_dims(int64_t M, int64_t N, int64_t K) {
   return QG_OK;
 }
 
+// KV cache [T][H][D]: T >= 0 positions, H >= 1 heads, D a multiple of 16 in
+// [16, 256], H * D <= 2^22 (a 128-position segment then spans less than
+// 2^31 bytes, the reach of the kernels' 32-bit buffer offsets).
+qg_status_t check_kv_dims(int64_t T, int64_t H, int64_t D) {
+  if (T < 0 || T > kMaxDim || H < 1 || D < 16 || D > 256 || D % 16) return QG_ERR_SHAPE;
+  if (H * D > ((int64_t)1 << 22)) return QG_ERR_SHAPE;
+  return QG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,6 +156,29 @@ qg_status_t apply_smoothing(const float* x, int64_t M, int64_t K, const float* s
   if (!x || !s || !x_out) return QG_ERR_NULL;
   return hip_status(qg::launch_apply_smoothing(x, M, K, s, x_out, out_dtype,
                                                static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t quantize_kv_i8_segments(const void* kv, int kv_dtype, int64_t T, int64_t H, int64_t D,
+                                    int8_t* kv_q, float* kv_scale, void* stream) {
+  if (qg_status_t s = check_kv_dims(T, H, D)) return s;
+  if (!is_float_dtype(kv_dtype)) return QG_ERR_DTYPE;
+  if (T == 0) return QG_OK;
+  if (!kv || !kv_q || !kv_scale) return QG_ERR_NULL;
+  if (!aligned16(kv) || !aligned16(kv_q) || !aligned16(kv_scale)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_kv_quant_seg(kv, kv_dtype, T, H, D, kv_q, kv_scale,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t dequantize_kv_i8_segments(const int8_t* kv_q, const float* kv_scale, int64_t T,
+                                      int64_t H, int64_t D, void* out, int out_dtype,
+                                      void* stream) {
+  if (qg_status_t s = check_kv_dims(T, H, D)) return s;
+  if (!is_float_dtype(out_dtype)) return QG_ERR_DTYPE;
+  if (T == 0) return QG_OK;
+  if (!kv_q || !kv_scale || !out) return QG_ERR_NULL;
+  if (!aligned16(kv_q) || !aligned16(kv_scale) || !aligned16(out)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_kv_dequant_seg(kv_q, kv_scale, T, H, D, out, out_dtype,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

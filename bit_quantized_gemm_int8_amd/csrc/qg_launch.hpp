@@ -30,5 +30,9 @@ hipError_t launch_awq_fold(const float* x_cal, int64_t T, const float* w, int64_
                            float* s, float* w_out, hipStream_t st);
 hipError_t launch_apply_smoothing(const float* x, int64_t M, int64_t K, const float* s,
                                   void* x_out, int out_dtype, hipStream_t st);
+hipError_t launch_kv_quant_seg(const void* kv, int kv_dtype, int64_t T, int64_t H, int64_t D,
+                               int8_t* kv_q, float* kv_scale, hipStream_t st);
+hipError_t launch_kv_dequant_seg(const int8_t* kv_q, const float* kv_scale, int64_t T, int64_t H,
+                                 int64_t D, void* out, int out_dtype, hipStream_t st);
 
 }  // namespace qg

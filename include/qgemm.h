@@ -205,6 +205,41 @@ qg_status_t awq_fold(const float* x_cal, int64_t T, const float* w, int64_t K, i
 qg_status_t apply_smoothing(const float* x, int64_t M, int64_t K, const float* s,
                             void* x_out, int out_dtype, void* stream);
 
+/*
+ * KV-cache INT8 quantization in position segments of 128 with one scale per
+ * (kv head, segment, head-dim channel).
+ * 「LLM推理降本五要素」 §5.2 (segments of 128 positions, per-channel scales,
+ * round then clamp to int8); 「第4章：量化」 §1.2 (symmetric s = max|x|/127),
+ * §1.1; 「现代AI加速技术全景解析」 §5.2 (the cache grouped in blocks of 128
+ * positions, [L/G][G][H][D]).
+ *   For each head h, segment g (positions [128g, min(T, 128g + 128))) and
+ *   channel d:  a = max_t |kv[t,h,d]|;  s = a / 127;
+ *               kv_q[t,h,d] = clamp(rne(kv[t,h,d] / s), -127, 127);
+ *   a channel with a == 0 in a segment gets s = 0 and zero codes.  A last,
+ *   partial segment is quantized over the positions it has.
+ * kv:       [T][H][D] of kv_dtype (QG_F32, QG_F16 or QG_BF16), read only;
+ *           position-major, the layout in which a cache grows.
+ * kv_q:     [T][H][D] int8 codes, written.
+ * kv_scale: [H][ceil(T/128)][D] float scales, written.
+ * T >= 0 (T == 0: nothing is launched); H >= 1; D a multiple of 16 in
+ * [16, 256]; H * D <= 2^22.  One layer of one sequence per call.
+ * The per-token variant (one scale per position and head) is
+ * quantize_per_token_i8 on kv viewed as [T*H][D].
+ */
+qg_status_t quantize_kv_i8_segments(const void* kv, int kv_dtype, int64_t T, int64_t H,
+                                    int64_t D, int8_t* kv_q, float* kv_scale, void* stream);
+
+/*
+ * Dequantization of a segment-quantized KV cache (「第4章：量化」 §1.1,
+ * x_hat = x_int * s):  out[t,h,d] = kv_q[t,h,d] * kv_scale[h, t/128, d],
+ * the product rounded to binary32, then to out_dtype (QG_F32, QG_F16 or
+ * QG_BF16, round to nearest even).  Shapes and rules as for
+ * quantize_kv_i8_segments; out is [T][H][D], written.
+ */
+qg_status_t dequantize_kv_i8_segments(const int8_t* kv_q, const float* kv_scale, int64_t T,
+                                      int64_t H, int64_t D, void* out, int out_dtype,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

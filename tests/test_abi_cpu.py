@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     for n in ["quantize_per_token_i8", "quantize_weight_i8_per_channel",
               "quantize_weight_u4_g128", "gemm_w8a8", "gemm_w4a8_g128", "gemm_w4a16_g128",
               "smoothquant_fold", "awq_fold", "apply_smoothing", "qg_status_string",
-              "qg_abi_version"]:
+              "qg_abi_version", "quantize_kv_i8_segments", "dequantize_kv_i8_segments"]:
         assert n in names, n
 
 
@@ -84,6 +84,21 @@ def test_validation_codes():
     assert lib.smoothquant_fold(A, 0, A, 16, 4, A, A, None) == SHAPE
     assert lib.awq_fold(A, 4, A, 18, 4, A, A, None) == SHAPE
     assert lib.apply_smoothing(A, 4, 16, A, A, 3, None) == DTYPE
+    kq = lib.quantize_kv_i8_segments
+    assert kq(None, 2, 256, 8, 128, A, A, None) == NULL
+    assert kq(A, 2, 256, 8, 120, A, A, None) == SHAPE     # D not a multiple of 16
+    assert kq(A, 2, 256, 8, 272, A, A, None) == SHAPE     # D > 256
+    assert kq(A, 2, 256, 0, 128, A, A, None) == SHAPE     # no heads
+    assert kq(A, 2, 256, 2 ** 15 + 1, 128, A, A, None) == SHAPE   # H * D > 2^22
+    assert kq(A, 2, -1, 8, 128, A, A, None) == SHAPE
+    assert kq(A, 3, 256, 8, 128, A, A, None) == DTYPE
+    assert kq(A, 2, 256, 8, 128, A, MIS, None) == ALIGN
+    assert kq(None, 2, 0, 8, 128, None, None, None) == OK   # empty cache
+    kd = lib.dequantize_kv_i8_segments
+    assert kd(A, A, 256, 8, 128, None, 2, None) == NULL
+    assert kd(A, A, 256, 8, 8, A, 2, None) == SHAPE
+    assert kd(A, A, 256, 8, 128, A, 3, None) == DTYPE
+    assert kd(MIS, A, 256, 8, 128, A, 2, None) == ALIGN
     assert "SHAPE" in lib.qg_status_string(2).decode()
 
 

@@ -29,7 +29,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "by_name", "draw", "f32_to_bf16_bits",
-           "f32_to_f16", "bf16_bits_to_f32", "ragged"]
+           "f32_to_f16", "bf16_bits_to_f32", "ragged", "KVWorkload", "KV_WORKLOADS",
+           "draw_kv"]
 
 
 @dataclass(frozen=True)
@@ -110,6 +111,48 @@ def draw(wl: Workload, seed_offset: int = 0, rows: Optional[int] = None) -> dict
         xc[:, idx] *= wl.outlier_scale
         out["x_cal"] = xc.astype(np.float32)
     return out
+
+
+# --- KV cache ------------------------------------------------------------------
+# One layer of one sequence's key (or value) cache, [T][H][D] position-major.
+# 「LLM推理降本五要素」 §5.2 quantizes a Llama-2-7B cache (32 heads of 128
+# dims; 4096 positions is that model's context length).  Value recipe (a
+# reading: the pages give none): N(0, 1) per element, times a per-(head,
+# channel) magnitude exp(N(0, 0.5^2)), and 2 outlier channels per head
+# (seeded choice) times 10 -- keys vary by channel, the reason for per-channel
+# scales.  Seeds: values 7000 + i, magnitudes 7000 + i + 100, outliers
+# 7000 + i + 200.
+
+
+@dataclass(frozen=True)
+class KVWorkload:
+    index: int
+    name: str
+    T: int
+    H: int
+    D: int
+    dtype: str           # "f32" | "bf16" | "f16"
+
+
+KV_WORKLOADS = (
+    KVWorkload(1, "kv_small", 300, 4, 128, "bf16"),
+    KVWorkload(2, "kv_llama2_7b_4k", 4096, 32, 128, "bf16"),
+)
+
+
+def draw_kv(wl: KVWorkload, T: Optional[int] = None, H: Optional[int] = None,
+            D: Optional[int] = None) -> np.ndarray:
+    """float32 [T, H, D] cache values (before the cast to wl.dtype)."""
+    T = wl.T if T is None else T
+    H = wl.H if H is None else H
+    D = wl.D if D is None else D
+    base = 7000 + wl.index
+    x = _normal(base, (T, H, D), 1.0)
+    mag = np.exp(_normal(base + 100, (H, D), 0.5))
+    rng = np.random.Generator(np.random.PCG64(base + 200))
+    for h in range(H):
+        mag[h, rng.permutation(D)[:2]] *= 10.0
+    return (x * mag[None]).astype(np.float32)
 
 
 # --- plain storage-format casts (inputs are handed over in these formats) ----
