@@ -473,7 +473,7 @@ KERNEL_OF = {
     "w4a8_ffn_down": [("k_w4a8_dec<16,", "unsigned short>")],
     "w4a16_qkv": [("k_w4a16_dec<1,", "_Float16>"), ("k_w4a16_decILi1E", "DF16_E")],
     "w8a8_prefill": [("k_w8a8_tiled<", "unsigned short>")],
-    "kv_llama2_7b_4k": [("k_kv_quant_seg<2, 8>",)],
+    "kv_llama2_7b_4k": [("k_kv_quant_seg<2, 4>",)],
 }
 # profile file label of each workload's dominant kernel
 KERNEL_LABEL = {
