@@ -123,20 +123,11 @@ struct KvQuant {
     }
   }
 
-  // Finish an item: per-channel maxima, scales, codes.  The code of x is
-  // rint(fl32(x / s)), which for finite x lies in [-127, 127] (the clamp
-  // of the definition never binds).  It is formed from
-  // a = fl32(x * r), r = fl32(1 / s), computed once per channel.  With q = x / s
-  // exact and |q| <= 127 (1 + 2^-21) (s is the rounded max / 127, and r finite
-  // means s >= 2^-128), fl32(q) lies within 2^-24 |q| of q and a within
-  // (2^-23 + 2^-48) |q|, so |a - fl32(q)| < 2.3e-5 < 2^-15.  When a is at least
-  // 2^-15 away from every half-integer, a and fl32(q) lie strictly between
-  // the same two half-integers and round to the same integer (the margin also
-  // covers a - k evaluated from the unrounded product, as a fused multiply-add
-  // does).  A value nearer a tie, or any value when r is infinite, takes the
-  // correctly rounded division instead.  (With bf16 caches about 0.3% of the
-  // values do -- the quotients of 8-bit mantissas often fall on or near half
-  // integers -- so the fallback is decided per value, not per chunk.)
+  // Finish an item: per-channel maxima, scales and their reciprocals, codes
+  // (sym_code_t: the correctly rounded quotient's integer, reached through
+  // the reciprocal).  With bf16 caches about 0.3% of the values fall near a
+  // tie and take the division -- quotients of 8-bit mantissas often land on
+  // or near half-integers -- so the fallback is decided per value.
   __device__ __forceinline__ void process(const KvItem& w, const KvRaw<DT> (&raw)[KC],
                                           float* part, float* chs, float* chr) const {
     const int cw = 8 * cpw;
@@ -162,7 +153,7 @@ struct KvQuant {
       for (int r = 0; r < rp; ++r) a = fmaxf(a, part[r * cw + tid]);
       sc = a > 0.f ? a / 127.f : 0.f;
       chs[tid] = sc;
-      chr[tid] = a > 0.f ? 1.f / sc : 0.f;
+      chr[tid] = sym_code_r(a, sc);
     }
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(sc), w.s, tid < cw ? 4u * tid : kOOB, 0,
                                           0);
@@ -173,29 +164,15 @@ struct KvQuant {
       s[e] = chs[8 * cc + e];
       rc[e] = chr[8 * cc + e];   // 0 for an all-zero channel: its codes come out 0
     }
-    // t = a + 1.5 * 2^23 rounds a to an integer (half to even) and leaves it,
-    // two's complement, in the low bits of t: the code's byte is t's low byte
-    constexpr float kTie = 0.5f - 1.f / 32768.f;
-    constexpr float kMagic = 12582912.f;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
-      float t[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float a = v[i][e] * rc[e];
-        t[e] = a + kMagic;
-        // near a tie (or NaN: r infinite): the correctly rounded quotient
-        if (!(fabsf(a - (t[e] - kMagic)) <= kTie))
-          t[e] = (s[e] > 0.f ? v[i][e] / s[e] : 0.f) + kMagic;
-      }
       u32 c[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32 b0 = __float_as_uint(t[4 * h]), b1 = __float_as_uint(t[4 * h + 1]);
-        const u32 b2 = __float_as_uint(t[4 * h + 2]), b3 = __float_as_uint(t[4 * h + 3]);
-        // byte j of the word = low byte of b_j (selector 0x0c: zero byte)
-        c[h] = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);
-      }
+      for (int h = 0; h < 2; ++h)
+        c[h] = pack_code_bytes(sym_code_t(v[i][4 * h], s[4 * h], rc[4 * h]),
+                               sym_code_t(v[i][4 * h + 1], s[4 * h + 1], rc[4 * h + 1]),
+                               sym_code_t(v[i][4 * h + 2], s[4 * h + 2], rc[4 * h + 2]),
+                               sym_code_t(v[i][4 * h + 3], s[4 * h + 3], rc[4 * h + 3]));
       // rows past the segment's end fall outside the resource: dropped
       __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)c[0], (int)c[1]}, w.q, qo[i], 0, 0);
     }

@@ -105,13 +105,43 @@ __device__ __forceinline__ float block_max(float v, float* red /* LDS, NT/64 flo
   return r;
 }
 
-// ---- symmetric int8 code of x given the scale s > 0 ------------------------
-// x / s is the correctly rounded binary32 quotient (hipcc's default fp32
-// division); rintf rounds half to even.
-__device__ __forceinline__ int sym_code_i8(float x, float s) {
-  float q = __builtin_rintf(x / s);
-  q = fminf(fmaxf(q, -127.f), 127.f);
-  return (int)q;
+// ---- symmetric int8 codes ---------------------------------------------------
+// The code of x under the scale s = fl32(max|x| / 127) > 0 of its slice (row,
+// column, channel) is rint(fl32(x / s)), with x / s the correctly rounded
+// binary32 quotient and rint half to even; for finite x it lies in
+// [-127, 127], so the clamp of the definition never binds.
+//
+// sym_code_t forms it from the reciprocal r = fl32(1 / s), computed once per
+// slice.  With q = x / s exact, |q| <= 127 (1 + 2^-21) (a finite r means
+// s >= 2^-128), fl32(q) lies within 2^-24 |q| of q and x * r, rounded once or
+// not at all, within (2^-23 + 2^-48) |q|: the two differ by less than
+// 2.3e-5 < 2^-15.  When x * r is at least 2^-15 away from every
+// half-integer, both round to the same integer; otherwise (and for any x when
+// r is infinite) the correctly rounded division decides.  Adding 1.5 * 2^23
+// rounds to an integer (half to even) and leaves it, two's complement, in the
+// low bits: the returned float's low byte is the code.  r = 0 (an all-zero
+// slice) gives code 0.
+constexpr float kCodeTie = 0.5f - 1.f / 32768.f;
+constexpr float kRoundMagic = 12582912.f;   // 1.5 * 2^23
+
+__device__ __forceinline__ float sym_code_t(float x, float s, float r) {
+  const float a = x * r;
+  float t = a + kRoundMagic;
+  // near a tie (or NaN: r infinite): the correctly rounded quotient
+  if (!(fabsf(a - (t - kRoundMagic)) <= kCodeTie)) t = (s > 0.f ? x / s : 0.f) + kRoundMagic;
+  return t;
+}
+
+// Reciprocal of a slice's scale for sym_code_t: 0 for an all-zero slice.
+__device__ __forceinline__ float sym_code_r(float amax, float s) {
+  return amax > 0.f ? 1.f / s : 0.f;
+}
+
+// The low bytes of four sym_code_t results as one word (byte j from t_j).
+__device__ __forceinline__ u32 pack_code_bytes(float t0, float t1, float t2, float t3) {
+  // v_perm selector 0x0c yields a zero byte
+  return __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x0c0c0400u) |
+         __builtin_amdgcn_perm(__float_as_uint(t3), __float_as_uint(t2), 0x04000c0cu);
 }
 
 }  // namespace qg

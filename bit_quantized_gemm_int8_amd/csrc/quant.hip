@@ -17,6 +17,41 @@ namespace qg {
 // from HBM once; codes leave as one 16-byte store per chunk.
 // ---------------------------------------------------------------------------
 
+// Chunk c of a row through a buffer resource over the row: a chunk past the
+// row's end reads zeros, so a thread's loads need no branch and all of them
+// are in flight together.
+template <int DT>
+__device__ __forceinline__ void load_chunk16_rs(rsrc_t row, bool valid, int c, v4i (&raw)[4]) {
+  constexpr int kBytes = DT == F32 ? 64 : 32;
+#pragma unroll
+  for (int i = 0; i < kBytes / 16; ++i)
+    raw[i] = bld16(row, valid ? (u32)(c * kBytes + 16 * i) : kOOB);
+}
+
+template <int DT>
+__device__ __forceinline__ void widen16(const v4i (&raw)[4], float (&v)[16]) {
+  if constexpr (DT == F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * i + e] = __int_as_float(raw[i][e]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const u32 u = (u32)raw[i][e];
+        if constexpr (DT == BF16) {
+          v[8 * i + 2 * e] = bf16_bits_to_f32(u & 0xFFFFu);
+          v[8 * i + 2 * e + 1] = bf16_bits_to_f32(u >> 16);
+        } else {
+          v[8 * i + 2 * e] = f16_bits_to_f32((uint16_t)(u & 0xFFFFu));
+          v[8 * i + 2 * e + 1] = f16_bits_to_f32((uint16_t)(u >> 16));
+        }
+      }
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void load_chunk16(const void* row, int c, float (&v)[16]) {
   if constexpr (DT == F32) {
@@ -47,18 +82,13 @@ __device__ __forceinline__ void load_chunk16(const void* row, int c, float (&v)[
   }
 }
 
-__device__ __forceinline__ v4i codes16(const float (&v)[16], float s, bool nz) {
+// codes of 16 values of one slice with scale s and reciprocal r (sym_code_r)
+__device__ __forceinline__ v4i codes16(const float (&v)[16], float s, float r) {
   v4i out;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    u32 word = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      int q = nz ? sym_code_i8(v[4 * w + b], s) : 0;
-      word |= ((u32)q & 0xFFu) << (8 * b);
-    }
-    out[w] = (int)word;
-  }
+  for (int w = 0; w < 4; ++w)
+    out[w] = (int)pack_code_bytes(sym_code_t(v[4 * w], s, r), sym_code_t(v[4 * w + 1], s, r),
+                                  sym_code_t(v[4 * w + 2], s, r), sym_code_t(v[4 * w + 3], s, r));
   return out;
 }
 
@@ -78,23 +108,28 @@ __global__ __launch_bounds__(256) void k_quant_per_token(const void* __restrict_
   const int nch = (int)(K >> 4);
   float amax = 0.f;
   if constexpr (CH > 0) {
-    float v[CH][16];
+    // K <= 1024 * 16 here, so the row's bytes fit a buffer resource
+    const rsrc_t rr = make_rsrc(xr, (uint32_t)(K * esize<DT>()));
+    v4i raw[CH][4];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int idx = threadIdx.x + c * 256;
-      if (idx < nch) {
-        load_chunk16<DT>(xr, idx, v[c]);
+      load_chunk16_rs<DT>(rr, idx < nch, idx, raw[c]);
+    }
+    float v[CH][16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[c][e]));
-      }
+    for (int c = 0; c < CH; ++c) {
+      widen16<DT>(raw[c], v[c]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[c][e]));   // zeros past the end
     }
     amax = block_max<256>(amax, red);
-    const float s = amax / 127.f;
+    const float s = amax / 127.f, r = sym_code_r(amax, s);
     if (threadIdx.x == 0) xs[row] = amax > 0.f ? s : 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int idx = threadIdx.x + c * 256;
-      if (idx < nch) st16(qr + (int64_t)idx * 16, codes16(v[c], s, amax > 0.f));
+      if (idx < nch) st16(qr + (int64_t)idx * 16, codes16(v[c], s, r));
     }
   } else {
     for (int idx = threadIdx.x; idx < nch; idx += 256) {
@@ -104,12 +139,12 @@ __global__ __launch_bounds__(256) void k_quant_per_token(const void* __restrict_
       for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
     }
     amax = block_max<256>(amax, red);
-    const float s = amax / 127.f;
+    const float s = amax / 127.f, r = sym_code_r(amax, s);
     if (threadIdx.x == 0) xs[row] = amax > 0.f ? s : 0.f;
     for (int idx = threadIdx.x; idx < nch; idx += 256) {
       float v[16];
       load_chunk16<DT>(xr, idx, v);
-      st16(qr + (int64_t)idx * 16, codes16(v, s, amax > 0.f));
+      st16(qr + (int64_t)idx * 16, codes16(v, s, r));
     }
   }
 }
@@ -170,7 +205,7 @@ __global__ __launch_bounds__(256) void k_quant_weight_i8(const float* __restrict
   const int cc = threadIdx.x >> 2, seg = threadIdx.x & 3;
   const int64_t ncol = n0 + cc;
   const float a = colmax[cc];
-  const float s = a / 127.f;
+  const float s = a / 127.f, rs = sym_code_r(a, s);
   for (int64_t k0 = 0; k0 < K; k0 += 64) {
     for (int kk = r; kk < 64; kk += 4)
       tile[kk][c] = (k0 + kk < K && n < N) ? w[(k0 + kk) * N + n] : 0.f;
@@ -179,7 +214,7 @@ __global__ __launch_bounds__(256) void k_quant_weight_i8(const float* __restrict
       float v[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) v[e] = tile[seg * 16 + e][cc];
-      st16(wq + ncol * K + k0 + seg * 16, codes16(v, s, a > 0.f));
+      st16(wq + ncol * K + k0 + seg * 16, codes16(v, s, rs));
     }
     __syncthreads();
   }
