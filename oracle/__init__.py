@@ -18,7 +18,8 @@ Sources (cited by page title and section):
   asymmetric scale), §1.3 (per-channel / per-group / per-token granularity),
   §2.2 (SmoothQuant fold), §3.2-3.3 (4-bit, group 128, zero point configs);
   「Quantization & Flash Attention」 §2.2-2.3 (AWQ per-channel fold);
-  「LLM推理降本五要素」 §2.2 (group-wise W4A8 with per-group scale and zero),
+  「LLM推理降本五要素」 §2.2 (group-wise W4A8 with per-group scale and zero;
+  the top 2% of each group kept in INT8 on a side path),
   §5.2 (round-then-clamp to int8; KV-cache position segments of 128 tokens
   with per-channel scales).
 
@@ -42,3 +43,5 @@ __all__ = [
     "smoothquant_scales", "awq_scales", "fold_weight", "fold_activation",
 ]
 from .kv import quantize_kv_segments, dequantize_kv_segments
+from .outlier import (quantize_weight_u4_g128_outliers, gemm_w4a8_g128_outliers,
+                      gemm_w4a8_g128_outlier_acc, decode_records, select_outliers)
