@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
   gemm_w4a16_g128(x, wq, w_scale, w_zero, out_dtype)
   smoothquant_fold(x_cal, w) / awq_fold(x_cal, w) -> (s f32 [K], w_folded f32 [K,N])
   apply_smoothing(x, s, out_dtype)
+  quantize_weight_u4_g128_outliers(w)           -> (wq, scale, zero, records int64 [N,G], s8 f32 [N])
+  gemm_w4a8_g128_outliers(xq, x_scale, wq, w_scale, w_zero, records, s8, out_dtype)
   quantize_kv_i8_segments(kv)                   -> (kv_q int8 [T,H,D], kv_scale f32 [H,ceil(T/128),D])
   dequantize_kv_i8_segments(kv_q, kv_scale, out_dtype) -> [T,H,D]
 """
@@ -32,6 +34,7 @@ __all__ = [
     "gemm_w8a8", "gemm_w4a8_g128", "gemm_w4a16_g128",
     "smoothquant_fold", "awq_fold", "apply_smoothing", "status_string",
     "quantize_kv_i8_segments", "dequantize_kv_i8_segments", "KV_SEGMENT",
+    "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemm.so")
@@ -52,6 +55,9 @@ _SIGNATURES = {
     "awq_fold": [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp],
     "apply_smoothing": [_vp, _i64, _i64, _vp, _vp, _int, _vp],
     "quantize_kv_i8_segments": [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp],
+    "quantize_weight_u4_g128_outliers": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp],
+    "gemm_w4a8_g128_outliers": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int,
+                                _vp],
     "dequantize_kv_i8_segments": [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
 }
 
@@ -194,6 +200,45 @@ def gemm_w4a16_g128(x, wq, w_scale, w_zero, out_dtype=None, out=None):
     out_dtype = out_dtype or x.dtype
     y = _out(out, (M, N), out_dtype, x.device)
     _call("gemm_w4a16_g128", px, _DTYPE_CODE[x.dtype], pwq, pws, pwz, M, N, K, y.data_ptr(),
+          _DTYPE_CODE[out_dtype], _stream())
+    return y
+
+
+def quantize_weight_u4_g128_outliers(w: torch.Tensor):
+    """w f32 [K, N] -> (wq int32 [N, K/8], scale f16 [N, G], zero f16 [N, G],
+    records int64 [N, G] (the uint64 bit patterns), s8 f32 [N]): uint4 groups
+    of 128 with each group's 3 largest weights in an INT8 side store."""
+    pw = _dev(w, "w", (torch.float32,))
+    K, N = w.shape
+    G = K // 128
+    wq = torch.empty((N, K // 8), dtype=torch.int32, device=w.device)
+    sc = torch.empty((N, G), dtype=torch.float16, device=w.device)
+    zz = torch.empty((N, G), dtype=torch.float16, device=w.device)
+    rec = torch.empty((N, G), dtype=torch.int64, device=w.device)
+    s8 = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _call("quantize_weight_u4_g128_outliers", pw, K, N, wq.data_ptr(), sc.data_ptr(),
+          zz.data_ptr(), rec.data_ptr(), s8.data_ptr(), _stream())
+    return wq, sc, zz, rec, s8
+
+
+def gemm_w4a8_g128_outliers(xq, x_scale, wq, w_scale, w_zero, records, s8,
+                            out_dtype=torch.bfloat16, out=None):
+    """W4A8 g=128 with the INT8 outlier side path; int32 out_dtype returns the
+    per-group accumulators and the side sum, [M, K/128 + 1, N]."""
+    pxq = _dev(xq, "xq", (torch.int8,))
+    pwq = _dev(wq, "wq", (torch.int32,))
+    pwz = _dev(w_zero, "w_zero", (torch.float16,))
+    prc = _dev(records, "records", (torch.int64,))
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] * 8 != K or tuple(records.shape) != (N, K // 128):
+        raise ValueError("xq, wq and records disagree on K or N")
+    pxs = _dev(x_scale, "x_scale", (torch.float32,)) if x_scale is not None else None
+    pws = _dev(w_scale, "w_scale", (torch.float16,)) if w_scale is not None else None
+    ps8 = _dev(s8, "s8", (torch.float32,)) if s8 is not None else None
+    shape = (M, K // 128 + 1, N) if out_dtype == torch.int32 else (M, N)
+    y = _out(out, shape, out_dtype, xq.device)
+    _call("gemm_w4a8_g128_outliers", pxq, pxs, pwq, pws, pwz, prc, ps8, M, N, K, y.data_ptr(),
           _DTYPE_CODE[out_dtype], _stream())
     return y
 

@@ -18,6 +18,8 @@
 #include "qg_device.hpp"
 #include "qg_launch.hpp"
 
+#include <algorithm>
+
 namespace qg {
 
 // bytes [b0..b7] of (lo, hi) -> [b0 b2 b4 b6 | b1 b3 b5 b7]
@@ -220,26 +222,49 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8(
 // the unit they belong to.  Wave w streams its contiguous run of units in
 // batches of UB, two batches in flight.
 // ---------------------------------------------------------------------------
-template <int UB>
+template <int UB, bool OUTL>
 struct W4A8DecBatch {
   v4i w[UB][2], xa[UB][2][2];   // unit v: weight loads; group s, MFMA h token fragment
+  v4i orc[OUTL ? UB : 1];       // unit v: the two groups' outlier records
 };
 
-template <int MR, int WAVES, int UB, typename OutT>
+// Outlier-retention side path (「LLM推理降本五要素」 §2.2).  A group's record
+// holds three (index << 8 | code byte) slots.  For one MFMA of the group, lane
+// (row r, k-block j) covers the 16 inputs k = 32 j + 16 h + [0, 16) of weight
+// row r; the slots falling there are placed at their byte positions, giving a
+// sparse int8 operand whose product with the raw (unpermuted) token fragment
+// accumulates sum_k x_q[m, k] * code exactly in int32.
+__device__ __forceinline__ v4i outlier_operand(u32 lo, u32 hi, int kb) {
+  uint64_t b0 = 0, b1 = 0;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const u32 slot = (i == 0 ? lo : i == 1 ? lo >> 16 : hi) & 0xFFFFu;
+    const int pos = (int)(slot >> 8) - kb;
+    const uint64_t v = (uint64_t)(slot & 0xFFu) << (8 * (pos & 7));
+    b0 |= (u32)pos < 8u ? v : 0;
+    b1 |= (u32)(pos - 8) < 8u ? v : 0;
+  }
+  return v4i{(int)(u32)b0, (int)(u32)(b0 >> 32), (int)(u32)b1, (int)(u32)(b1 >> 32)};
+}
+
+template <int MR, int WAVES, int UB, bool OUTL, typename OutT>
 __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, const int32_t* __restrict__ wq,
-    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero,
+    const uint64_t* __restrict__ orec, const float* __restrict__ os8, int M, int N, int K,
     OutT* __restrict__ y) {
   constexpr bool kI32 = __is_same(OutT, int32_t);
   constexpr int kThreads = 64 * WAVES;
   extern __shared__ __attribute__((aligned(16))) u32 szl[];   // 16 x sz_pitch(G) words
   __shared__ __attribute__((aligned(16))) int8_t tiles[WAVES][kTileBytes];
   __shared__ v4f red[kI32 ? 1 : WAVES][64];
+  __shared__ v4i redo[OUTL ? WAVES : 1][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int n_base = blockIdx.x * 16;
   const int G = K >> 7, Kw = K >> 3, RB = Kw * 4;
+  const int GY = OUTL ? G + 1 : G;   // int32 output slices per token: groups (+ side sum)
   const int units = (RB + kUnitBytes - 1) / kUnitBytes;
   const int ub = (int)((int64_t)units * wave / WAVES), ue = (int)((int64_t)units * (wave + 1) / WAVES);
 
@@ -249,8 +274,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec(
   // token row r (rows >= M past the resource's end read zeros), k = 32j + 16h
   const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
   const u32 xoff = (u32)((r < MR ? r : MR) * K + 32 * j);
+  // outlier records of row r: unit q's two groups are 16 bytes at 16 q
+  const rsrc_t orr = OUTL ? make_rsrc(orec + (int64_t)n_base * G, (u32)(rows_n * G * 8)) : wr;
+  const u32 ooff = (u32)(r * G * 8);
 
-  using Batch = W4A8DecBatch<UB>;
+  using Batch = W4A8DecBatch<UB, OUTL>;
   auto load = [&](Batch& bt, int q0) {
 #pragma unroll
     for (int v = 0; v < UB; ++v) {
@@ -263,6 +291,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec(
 #pragma unroll
         for (int h = 0; h < 2; ++h) bt.xa[v][s][h] = bld16(xr, gin ? xoff + 128 * g + 16 * h : kOOB);
       }
+      if constexpr (OUTL) bt.orc[v] = bld16(orr, q < ue ? ooff + 16 * q : kOOB);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -289,6 +318,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec(
   const u32* szrow = szl + r * sz_pitch(G);
   int8_t* tile = tiles[wave];
   v4f yacc = {0.f, 0.f, 0.f, 0.f};
+  v4i oacc = {0, 0, 0, 0};
   auto mma = [&](const Batch& bt, int q0) {
 #pragma unroll
     for (int v = 0; v < UB; ++v) {
@@ -313,13 +343,22 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec(
                                                     acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_u4_pair((u32)f[s][2], (u32)f[s][3]),
                                                     acc, 0, 0, 0);
+        if constexpr (OUTL) {
+          // a group past G (odd G) or past the run has a zero token fragment
+          const u32 lo = (u32)bt.orc[v][2 * s], hi = (u32)bt.orc[v][2 * s + 1];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            oacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(bt.xa[v][s][h],
+                                                         outlier_operand(lo, hi, 32 * j + 16 * h),
+                                                         oacc, 0, 0, 0);
+        }
         if constexpr (kI32) {
           const int n = n_base + r;
           if (gin && n < N) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int m = 4 * j + i;
-              if (m < M) y[((int64_t)m * G + g) * N + n] = acc[i];
+              if (m < M) y[((int64_t)m * GY + g) * N + n] = acc[i];
             }
           }
         } else {
@@ -337,19 +376,36 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec(
     mma(b1, q0 + UB);
   }
 
-  if constexpr (!kI32) {
-    red[wave][lane] = yacc;
+  if constexpr (!kI32) red[wave][lane] = yacc;
+  if constexpr (OUTL) redo[wave][lane] = oacc;
+  if constexpr (!kI32 || OUTL) {
     __syncthreads();
     if (tid < 64) {
-      v4f sum = red[0][lane];
-#pragma unroll
-      for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
       const int n = n_base + r;
-      if (n < N) {
+      v4i osum = {0, 0, 0, 0};
+      if constexpr (OUTL) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 4 * j + i;
-          if (m < M) store_out<OutT>(y, (int64_t)m * N + n, sum[i] * sx[i]);
+        for (int w = 0; w < WAVES; ++w) osum += redo[w][lane];
+      }
+      if (n < N) {
+        if constexpr (kI32) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 4 * j + i;
+            if (m < M) y[((int64_t)m * GY + G) * N + n] = osum[i];
+          }
+        } else {
+          v4f sum = red[0][lane];
+#pragma unroll
+          for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+          const float s8 = OUTL ? os8[n] : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 4 * j + i;
+            // y = s_x (sum_g s_g acc_g + s8 acc_o)
+            const float t = OUTL ? __builtin_fmaf(s8, (float)osum[i], sum[i]) : sum[i];
+            if (m < M) store_out<OutT>(y, (int64_t)m * N + n, t * sx[i]);
+          }
         }
       }
     }
@@ -366,11 +422,11 @@ static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* 
     const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
     const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
     switch (mr) {
-      case 1: k_w4a8_dec<1, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
-      case 2: k_w4a8_dec<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
-      case 4: k_w4a8_dec<4, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
-      case 8: k_w4a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
-      default: k_w4a8_dec<16, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
+      case 1: k_w4a8_dec<1, WAVES, UB, false, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, nullptr, nullptr, M, N, K, y); break;
+      case 2: k_w4a8_dec<2, WAVES, UB, false, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, nullptr, nullptr, M, N, K, y); break;
+      case 4: k_w4a8_dec<4, WAVES, UB, false, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, nullptr, nullptr, M, N, K, y); break;
+      case 8: k_w4a8_dec<8, WAVES, UB, false, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, nullptr, nullptr, M, N, K, y); break;
+      default: k_w4a8_dec<16, WAVES, UB, false, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, nullptr, nullptr, M, N, K, y); break;
     }
     return hipGetLastError();
   }
@@ -378,6 +434,50 @@ static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* 
   dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
   k_w4a8<MT, NT, WAVES, U, OutT><<<grid, dim3(64 * WAVES), 0, st>>>(xq, xs, wq, ws, wz, M, N, K, y);
   return hipGetLastError();
+}
+
+// W4A8 with the INT8 outlier side path: the decode kernel over chunks of up
+// to 16 token rows (the weight stream is re-read per chunk).
+template <typename OutT>
+static hipError_t gemm_w4a8_outl_t(const int8_t* xq, const float* xs, const int32_t* wq,
+                                   const uint16_t* ws, const uint16_t* wz, const uint64_t* orec,
+                                   const float* os8, int M, int N, int K, OutT* y,
+                                   hipStream_t st) {
+  constexpr int WAVES = 8, UB = 1;
+  const int G = K / 128;
+  const size_t lds = (size_t)16 * sz_pitch(G) * 4;
+  if (lds > kDecLdsMaxBytes) return hipErrorInvalidValue;   // excluded by the API checks
+  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
+  const int64_t ystride = __is_same(OutT, int32_t) ? (int64_t)(G + 1) * N : N;
+  for (int m0 = 0; m0 < M; m0 += 16) {
+    const int mc = std::min(16, M - m0);
+    const int mr = mc <= 1 ? 1 : mc <= 2 ? 2 : mc <= 4 ? 4 : mc <= 8 ? 8 : 16;
+    const int8_t* x = xq + (int64_t)m0 * K;
+    const float* s = xs ? xs + m0 : nullptr;
+    OutT* yy = y + m0 * ystride;
+    switch (mr) {
+      case 1: k_w4a8_dec<1, WAVES, UB, true, OutT><<<grid, block, lds, st>>>(x, s, wq, ws, wz, orec, os8, mc, N, K, yy); break;
+      case 2: k_w4a8_dec<2, WAVES, UB, true, OutT><<<grid, block, lds, st>>>(x, s, wq, ws, wz, orec, os8, mc, N, K, yy); break;
+      case 4: k_w4a8_dec<4, WAVES, UB, true, OutT><<<grid, block, lds, st>>>(x, s, wq, ws, wz, orec, os8, mc, N, K, yy); break;
+      case 8: k_w4a8_dec<8, WAVES, UB, true, OutT><<<grid, block, lds, st>>>(x, s, wq, ws, wz, orec, os8, mc, N, K, yy); break;
+      default: k_w4a8_dec<16, WAVES, UB, true, OutT><<<grid, block, lds, st>>>(x, s, wq, ws, wz, orec, os8, mc, N, K, yy); break;
+    }
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_gemm_w4a8_outl(const int8_t* xq, const float* xs, const int32_t* wq,
+                                 const uint16_t* ws, const uint16_t* wz, const uint64_t* orec,
+                                 const float* os8, int64_t M, int64_t N, int64_t K, void* y,
+                                 int y_dtype, hipStream_t st) {
+  const int m = (int)M, n = (int)N, k = (int)K;
+  switch (y_dtype) {
+    case F32: return gemm_w4a8_outl_t<float>(xq, xs, wq, ws, wz, orec, os8, m, n, k, (float*)y, st);
+    case F16: return gemm_w4a8_outl_t<_Float16>(xq, xs, wq, ws, wz, orec, os8, m, n, k, (_Float16*)y, st);
+    case BF16: return gemm_w4a8_outl_t<uint16_t>(xq, xs, wq, ws, wz, orec, os8, m, n, k, (uint16_t*)y, st);
+    default: return gemm_w4a8_outl_t<int32_t>(xq, xs, wq, ws, wz, orec, os8, m, n, k, (int32_t*)y, st);
+  }
 }
 
 hipError_t launch_gemm_w4a8(const int8_t* xq, const float* xs, const int32_t* wq,

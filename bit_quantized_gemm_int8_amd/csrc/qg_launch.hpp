@@ -21,6 +21,13 @@ hipError_t launch_gemm_w8a8(const int8_t* xq, const float* xs, const int8_t* wq,
 hipError_t launch_gemm_w4a8(const int8_t* xq, const float* xs, const int32_t* wq,
                             const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
                             int64_t K, void* y, int y_dtype, hipStream_t st);
+hipError_t launch_quant_weight_u4_outl(const float* w, int64_t K, int64_t N, int32_t* wq,
+                                       uint16_t* ws, uint16_t* wz, uint64_t* rec, float* s8,
+                                       hipStream_t st);
+hipError_t launch_gemm_w4a8_outl(const int8_t* xq, const float* xs, const int32_t* wq,
+                                 const uint16_t* ws, const uint16_t* wz, const uint64_t* orec,
+                                 const float* os8, int64_t M, int64_t N, int64_t K, void* y,
+                                 int y_dtype, hipStream_t st);
 hipError_t launch_gemm_w4a16(const void* x, int x_dtype, const int32_t* wq, const uint16_t* ws,
                              const uint16_t* wz, int64_t M, int64_t N, int64_t K, void* y,
                              int y_dtype, hipStream_t st);

@@ -298,4 +298,195 @@ hipError_t launch_quant_weight_u4(const float* w, int64_t K, int64_t N, int32_t*
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// g=128 uint4 weights with the top 3 of each group (by |w|, ties to the lower
+// index) kept in an INT8 side store (「LLM推理降本五要素」 §2.2).  Same
+// workgroup shape as k_quant_weight_u4.  Each thread picks the top 3 of its 32
+// weights; the four quarters' candidates meet in LDS and every thread merges
+// them in ascending index order, a candidate entering only if strictly
+// larger, so equal magnitudes keep the lower index.  The group's scale and
+// zero point come from the other 125 weights; outlier positions get code z.
+// The record gets the outliers' indices (ascending) with code bytes 0 and
+// slot 3 = 0xFFFF; k_outlier_codes fills in the codes once every group of
+// the column is known.
+// ---------------------------------------------------------------------------
+
+struct Top3 {
+  float m[3];   // magnitudes, descending
+  int k[3];     // indices
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      m[i] = -1.f;
+      k[i] = 1 << 20;
+    }
+  }
+  // offer in ascending index order: a candidate enters only if strictly larger
+  __device__ __forceinline__ void offer(float a, int idx) {
+    if (a > m[2]) {
+      if (a > m[1]) {
+        m[2] = m[1];
+        k[2] = k[1];
+        if (a > m[0]) {
+          m[1] = m[0];
+          k[1] = k[0];
+          m[0] = a;
+          k[0] = idx;
+        } else {
+          m[1] = a;
+          k[1] = idx;
+        }
+      } else {
+        m[2] = a;
+        k[2] = idx;
+      }
+    }
+  }
+};
+
+__global__ __launch_bounds__(256) void k_quant_weight_u4_outl(const float* __restrict__ w,
+                                                              int64_t K, int64_t N,
+                                                              int32_t* __restrict__ wq,
+                                                              uint16_t* __restrict__ wscale,
+                                                              uint16_t* __restrict__ wzero,
+                                                              uint64_t* __restrict__ rec) {
+  __shared__ float rlo[4][64], rhi[4][64];
+  __shared__ int cand[4][64][3];
+  const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 64 + c;
+  const int64_t g = blockIdx.y;
+  const int64_t G = K >> 7;
+  float v[32];
+  Top3 t3;
+  t3.init();
+  if (n < N) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      v[i] = w[(g * 128 + r * 32 + i) * N + n];
+      t3.offer(fabsf(v[i]), r * 32 + i);
+    }
+  }
+  // the quarter's candidates by ascending index
+  int ks[3] = {t3.k[0], t3.k[1], t3.k[2]};
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2 - a; ++b)
+      if (ks[b] > ks[b + 1]) {
+        const int tmp = ks[b];
+        ks[b] = ks[b + 1];
+        ks[b + 1] = tmp;
+      }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) cand[r][c][i] = ks[i];
+  __syncthreads();
+  const bool valid = n < N;   // no early return: a second barrier follows
+  // merge (every thread of the column, redundantly): magnitudes re-read from
+  // global memory, in ascending index order
+  Top3 all;
+  all.init();
+  if (valid)
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int kk = cand[q][c][i];
+        all.offer(fabsf(w[(g * 128 + kk) * N + n]), kk);
+      }
+  int o[3] = {all.k[0], all.k[1], all.k[2]};
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2 - a; ++b)
+      if (o[b] > o[b + 1]) {
+        const int tmp = o[b];
+        o[b] = o[b + 1];
+        o[b + 1] = tmp;
+      }
+  bool out[32];
+  float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int kk = r * 32 + i;
+    out[i] = kk == o[0] || kk == o[1] || kk == o[2];
+    if (valid && !out[i]) {
+      lo = fminf(lo, v[i]);
+      hi = fmaxf(hi, v[i]);
+    }
+  }
+  rlo[r][c] = lo;
+  rhi[r][c] = hi;
+  __syncthreads();
+  if (!valid) return;
+  lo = fminf(fminf(rlo[0][c], rlo[1][c]), fminf(rlo[2][c], rlo[3][c]));
+  hi = fmaxf(fmaxf(rhi[0][c], rhi[1][c]), fmaxf(rhi[2][c], rhi[3][c]));
+  const float t = (hi - lo) / 15.f;
+  const _Float16 h = f16_round_up(t);
+  const float s = (float)h;
+  float z = 0.f;
+  if (s > 0.f) z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.f), 15.f);
+  v4i words;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32 word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float q = 0.f;
+      if (s > 0.f) q = fminf(fmaxf(__builtin_rintf(v[8 * i + e] / s) + z, 0.f), 15.f);
+      if (out[8 * i + e]) q = z;
+      word |= ((u32)q) << (4 * e);
+    }
+    words[i] = (int)word;
+  }
+  st16(wq + n * (K >> 3) + g * 16 + r * 4, words);
+  if (r == 0) {
+    wscale[n * G + g] = __builtin_bit_cast(uint16_t, h);
+    wzero[n * G + g] = __builtin_bit_cast(uint16_t, (_Float16)z);
+    uint64_t rc = (uint64_t)0xFFFF << 48;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) rc |= (uint64_t)(o[i] << 8) << (16 * i);
+    rec[n * G + g] = rc;
+  }
+}
+
+// Per output channel: s8 = max |outlier| / 127 over the channel's records,
+// then the outliers' INT8 codes into the records' code bytes.
+__global__ __launch_bounds__(256) void k_outlier_codes(const float* __restrict__ w, int64_t K,
+                                                       int64_t N, uint64_t* __restrict__ rec,
+                                                       float* __restrict__ s8) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const int64_t G = K >> 7;
+  float amax = 0.f;
+  for (int64_t g = 0; g < G; ++g) {
+    const uint64_t rc = rec[n * G + g];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int kk = (int)((rc >> (16 * i + 8)) & 0xFF);
+      amax = fmaxf(amax, fabsf(w[(g * 128 + kk) * N + n]));
+    }
+  }
+  const float sc = amax / 127.f, rs = sym_code_r(amax, sc);
+  s8[n] = amax > 0.f ? sc : 0.f;
+  for (int64_t g = 0; g < G; ++g) {
+    uint64_t rc = rec[n * G + g];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int kk = (int)((rc >> (16 * i + 8)) & 0xFF);
+      const u32 byte = __float_as_uint(sym_code_t(w[(g * 128 + kk) * N + n], sc, rs)) & 0xFFu;
+      rc = (rc & ~((uint64_t)0xFF << (16 * i))) | ((uint64_t)byte << (16 * i));
+    }
+    rec[n * G + g] = rc;
+  }
+}
+
+hipError_t launch_quant_weight_u4_outl(const float* w, int64_t K, int64_t N, int32_t* wq,
+                                       uint16_t* ws, uint16_t* wz, uint64_t* rec, float* s8,
+                                       hipStream_t st) {
+  dim3 grid((unsigned)((N + 63) / 64), (unsigned)(K / 128)), block(256);
+  k_quant_weight_u4_outl<<<grid, block, 0, st>>>(w, K, N, wq, ws, wz, rec);
+  if (hipError_t e = hipGetLastError()) return e;
+  k_outlier_codes<<<(unsigned)((N + 255) / 256), 256, 0, st>>>(w, K, N, rec, s8);
+  return hipGetLastError();
+}
+
 }  // namespace qg

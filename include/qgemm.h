@@ -18,7 +18,8 @@
  *   「Quantization & Flash Attention」 §2.2-2.3: the AWQ per-channel fold.
  *   「LLM推理降本五要素」 §2.1 (W8A8 decode is weight-bandwidth bound), §2.2
  *     (W4A8 with per-group scale and zero; the quantized_matmul(x, weight,
- *     scale, zero) argument order), §5.2 (round, then clamp to int8).
+ *     scale, zero) argument order; the INT8 outlier side path), §5.2 (round,
+ *     then clamp to int8; KV-cache segments).
  *
  * Conventions for every function below.
  *   Pointers: DEVICE pointers, allocated and freed by the caller, contiguous
@@ -156,6 +157,55 @@ qg_status_t gemm_w4a8_g128(const int8_t* xq, const float* x_scale, const int32_t
                            const uint16_t* w_scale_f16, const uint16_t* w_zero_f16,
                            int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
                            void* stream);
+
+/*
+ * Group-wise (g = 128) uint4 weights with the largest weights of every group
+ * kept in an INT8 side store (offline).
+ * 「LLM推理降本五要素」 §2.2 (the top 2% of each group by magnitude stored at
+ * INT8 precision and computed on a side path); 「第4章：量化」 §1.1-1.3.
+ *   For each output channel n and group g: the 3 weights of largest |w|
+ *   (2% of 128 rounded up; equal magnitudes go to the lower index) are the
+ *   outliers.  Scale, zero point and codes of the other 125 weights follow
+ *   quantize_weight_u4_g128; an outlier position gets the code z (it adds
+ *   nothing to the 4-bit product).
+ *   Per output channel: s8 = max |outlier| / 127 (binary32; 0 if every
+ *   outlier is 0) and code = rne(w / s8) in [-127, 127].
+ * w:           [K][N] float, read only.
+ * wq, w_scale_f16, w_zero_f16: as quantize_weight_u4_g128, written.
+ * w_out_rec:   [N][K/128] uint64 records, written: bits 16i..16i+15 hold slot
+ *              i = (index in the group << 8) | code byte (two's complement)
+ *              for the outliers by ascending index (i = 0, 1, 2); slot 3 is
+ *              0xFFFF.
+ * w_out_scale: [N] float s8, written.
+ * K must be a positive multiple of 128 with K / 128 <= 1279.
+ */
+qg_status_t quantize_weight_u4_g128_outliers(const float* w, int64_t K, int64_t N, int32_t* wq,
+                                             uint16_t* w_scale_f16, uint16_t* w_zero_f16,
+                                             uint64_t* w_out_rec, float* w_out_scale,
+                                             void* stream);
+
+/*
+ * W4A8 GEMM with the INT8 outlier side path fused into the same kernel.
+ * 「LLM推理降本五要素」 §2.2; 「第4章：量化」 §1.1, §3.5.
+ *   acc[m,g,n] as gemm_w4a8_g128 (outlier positions hold q = z: no term);
+ *   acc_o[m,n] = sum over the channel's records of xq[m, 128 g + index] * code
+ *                (exact int32);
+ *   y[m,n]     = x_scale[m] * (sum_g s[n,g] acc[m,g,n] + s8[n] acc_o[m,n])
+ *                (binary32).
+ * Arguments as gemm_w4a8_g128 plus w_out_rec [N][K/128] and w_out_scale [N]
+ * from quantize_weight_u4_g128_outliers (only slots 0-2 of a record are read).
+ * y: [M][N] of QG_F32, QG_BF16 or QG_F16; or QG_I32, in which case y is
+ *    [M][K/128 + 1][N] int32: slices 0 .. K/128 - 1 hold acc[m,g,n], the last
+ *    holds acc_o[m,n] (x_scale, w_scale_f16 and w_out_scale unused, may be
+ *    NULL).
+ * K must be a positive multiple of 128 with K / 128 <= 1279.  The kernel
+ * streams the weights once per 16 token rows.
+ */
+qg_status_t gemm_w4a8_g128_outliers(const int8_t* xq, const float* x_scale, const int32_t* wq,
+                                    const uint16_t* w_scale_f16, const uint16_t* w_zero_f16,
+                                    const uint64_t* w_out_rec, const float* w_out_scale,
+                                    int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                                    void* stream);
 
 /*
  * W4A16 weight-only GEMM: 16-bit float activations, g=128 uint4 weights

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for n in ["quantize_per_token_i8", "quantize_weight_i8_per_channel",
               "quantize_weight_u4_g128", "gemm_w8a8", "gemm_w4a8_g128", "gemm_w4a16_g128",
               "smoothquant_fold", "awq_fold", "apply_smoothing", "qg_status_string",
-              "qg_abi_version", "quantize_kv_i8_segments", "dequantize_kv_i8_segments"]:
+              "qg_abi_version", "quantize_kv_i8_segments", "dequantize_kv_i8_segments",
+              "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers"]:
         assert n in names, n
 
 
@@ -99,6 +100,19 @@ def test_validation_codes():
     assert kd(A, A, 256, 8, 8, A, 2, None) == SHAPE
     assert kd(A, A, 256, 8, 128, A, 3, None) == DTYPE
     assert kd(MIS, A, 256, 8, 128, A, 2, None) == ALIGN
+    uo = lib.quantize_weight_u4_g128_outliers
+    assert uo(A, 130, 8, A, A, A, A, A, None) == SHAPE
+    assert uo(A, 128 * 1280, 8, A, A, A, A, A, None) == SHAPE   # too many groups to stage
+    assert uo(A, 128, 8, A, A, A, None, A, None) == NULL
+    assert uo(A, 128, 8, A, A, A, MIS, A, None) == ALIGN
+    assert uo(None, 128, 0, None, None, None, None, None, None) == OK
+    go = lib.gemm_w4a8_g128_outliers
+    assert go(A, A, A, A, A, A, A, 4, 4, 192, A, 2, None) == SHAPE
+    assert go(A, A, A, A, A, A, None, 4, 4, 128, A, 2, None) == NULL   # s8 needed unless I32
+    assert go(A, A, A, A, A, None, A, 4, 4, 128, A, 2, None) == NULL
+    assert go(A, A, A, A, A, A, A, 4, 4, 128, A, 9, None) == DTYPE
+    assert go(A, A, A, A, A, MIS, A, 4, 4, 128, A, 2, None) == ALIGN
+    assert go(None, None, None, None, None, None, None, 0, 4, 128, None, 2, None) == OK
     assert "SHAPE" in lib.qg_status_string(2).decode()
 
 

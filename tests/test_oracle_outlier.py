@@ -198,3 +198,21 @@ def test_three_nonzeros_per_group_is_w8a8():
 def test_rejects_bad_k():
     with pytest.raises(ValueError):
         quantize_weight_u4_g128_outliers(np.zeros((100, 2), np.float32))
+
+
+def test_error_vs_plain_u4():
+    """Keeping the 3 largest weights of each group in INT8 lowers the weight
+    round-trip error of the layer (the reason the page gives)."""
+    w = _random_w(11, 1024, 256)
+    p, s, z, r, s8 = oracle.quantize_weight_u4_g128_outliers(w)
+    index, code, valid = oracle.decode_records(r)
+    what = oracle.dequant_u4_g128(p, s, z).T                       # [N, K]
+    for g in range(1024 // 128):
+        for i in range(3):
+            what[np.arange(256), 128 * g + index[:, g, i]] = code[:, g, i] * s8.astype(np.float64)
+    pp, ps, pz = oracle.quantize_weight_u4_g128(w)
+    plain = oracle.dequant_u4_g128(pp, ps, pz).T
+    e_out = np.abs(what - w.T).mean()
+    e_plain = np.abs(plain - w.T).mean()
+    assert e_out < e_plain
+    print(f"mean |w - w_hat|: plain u4 {e_plain:.3e}, with INT8 outliers {e_out:.3e}")
