@@ -44,6 +44,7 @@ ROTATE_BYTES = 600 * 2 ** 20    # weight copies per rotation: > 2x the 256 MB MA
 KERNEL_SOURCES = {
     "w8a8": ["gemm_w8a8.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a8": ["gemm_w4a8.hip", "qg_decode.hpp", "qg_device.hpp"],
+    "w4a8_outl": ["gemm_w4a8.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a16": ["gemm_w4a16.hip", "qg_decode.hpp", "qg_device.hpp"],
     "quant": ["quant.hip", "qg_device.hpp"],
     "kv": ["kv.hip", "qg_device.hpp"],
@@ -97,6 +98,8 @@ def algorithmic(wl):
         gemm = N * K + 4 * N + M * K + 4 * M + out_b * M * N
     elif wl.path == "w4a8":
         gemm = N * K // 2 + 4 * N * G + M * K + 4 * M + out_b * M * N
+    elif wl.path == "w4a8_outl":   # plus one 8-byte outlier record per group, s8 per channel
+        gemm = N * K // 2 + 4 * N * G + 8 * N * G + 4 * N + M * K + 4 * M + out_b * M * N
     else:
         gemm = N * K // 2 + 4 * N * G + x_b * M * K + out_b * M * N
     quant = x_b * M * K + M * K + 4 * M if wl.path != "w4a16" else 0
@@ -228,6 +231,8 @@ def run_workload(wl, steps, warmup, traffic_db):
     if wl.path == "w8a8":
         wq, ws = qg.quantize_weight_i8_per_channel(w_d)
         weights = (wq, ws)
+    elif wl.path == "w4a8_outl":
+        weights = qg.quantize_weight_u4_g128_outliers(w_d)
     else:
         weights = qg.quantize_weight_u4_g128(w_d)
     del w_d
@@ -247,6 +252,8 @@ def run_workload(wl, steps, warmup, traffic_db):
             qg.gemm_w8a8(xq, xs, w[0], w[1], out_dtype=y.dtype, out=y)
         elif wl.path == "w4a8":
             qg.gemm_w4a8_g128(xq, xs, w[0], w[1], w[2], out_dtype=y.dtype, out=y)
+        elif wl.path == "w4a8_outl":
+            qg.gemm_w4a8_g128_outliers(xq, xs, *w, out_dtype=y.dtype, out=y)
         else:
             qg.gemm_w4a16_g128(x_in, w[0], w[1], w[2], out_dtype=y.dtype, out=y)
 
@@ -470,7 +477,8 @@ def batch_sweep(steps):
 KERNEL_OF = {
     "w8a8_decode_ffn_up": [("k_w8a8_dec<8,", "unsigned short>")],
     "w8a8_tiny": [("k_w8a8_wide<1,", "float>")],
-    "w4a8_ffn_down": [("k_w4a8_dec<16,", "unsigned short>")],
+    "w4a8_ffn_down": [("k_w4a8_dec<16, 8, 1, false, unsigned short>",)],
+    "w4a8_outl_ffn_down": [("k_w4a8_dec<16, 8, 1, true, unsigned short>",)],
     "w4a16_qkv": [("k_w4a16_dec<1,", "_Float16>"), ("k_w4a16_decILi1E", "DF16_E")],
     "w8a8_prefill": [("k_w8a8_tiled<", "unsigned short>")],
     "kv_llama2_7b_4k": [("k_kv_quant_seg<2, 4>",)],
@@ -479,7 +487,7 @@ KERNEL_OF = {
 KERNEL_LABEL = {
     "w8a8_decode_ffn_up": "gemm_w8a8_dec", "w8a8_tiny": "gemm_w8a8_wide",
     "w4a8_ffn_down": "gemm_w4a8_dec", "w4a16_qkv": "gemm_w4a16_dec", "w8a8_prefill": "gemm_w8a8_tiled",
-    "kv_llama2_7b_4k": "kv_quant_seg",
+    "kv_llama2_7b_4k": "kv_quant_seg", "w4a8_outl_ffn_down": "gemm_w4a8_outl_dec",
 }
 COPY_BYTES = 512 * 2 ** 20
 PROFILE_COMMANDS = """\
@@ -633,15 +641,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
-    from workloads import KV_WORKLOADS, WORKLOADS, by_name
+    from workloads import KV_WORKLOADS, VARIANT_WORKLOADS, WORKLOADS, by_name
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import bit_quantized_gemm_int8_amd as qg
     qg.load()
     kv_wls = {w.name: w for w in KV_WORKLOADS if w.name in BENCH_KV}
-    names = [w.name for w in WORKLOADS] + list(kv_wls) if args.workloads == "all" \
-        else args.workloads.split(",")
+    names = [w.name for w in WORKLOADS + VARIANT_WORKLOADS] + list(kv_wls) \
+        if args.workloads == "all" else args.workloads.split(",")
     names = sorted(names, key=lambda n: n != HEADLINE)
     traffic_db = load_traffic()
     results = [run_kv(kv_wls[n], args.steps, args.warmup, traffic_db) if n in kv_wls

@@ -30,7 +30,7 @@ import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "by_name", "draw", "f32_to_bf16_bits",
            "f32_to_f16", "bf16_bits_to_f32", "ragged", "KVWorkload", "KV_WORKLOADS",
-           "draw_kv"]
+           "draw_kv", "VARIANT_WORKLOADS"]
 
 
 @dataclass(frozen=True)
@@ -65,8 +65,16 @@ WORKLOADS = (
 )
 
 
+# Variants of a workload on another path, with the same draws (same index and
+# seeds): the FFN-down layer with the top 3 weights of each group kept in INT8
+# (「LLM推理降本五要素」 §2.2).
+VARIANT_WORKLOADS = (
+    replace(WORKLOADS[2], name="w4a8_outl_ffn_down", path="w4a8_outl"),
+)
+
+
 def by_name(name: str) -> Workload:
-    for wl in WORKLOADS:
+    for wl in WORKLOADS + VARIANT_WORKLOADS:
         if wl.name == name or str(wl.index) == str(name):
             return wl
     raise KeyError(name)
