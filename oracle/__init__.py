@@ -19,7 +19,8 @@ Sources (cited by page title and section):
   §2.2 (SmoothQuant fold), §3.2-3.3 (4-bit, group 128, zero point configs);
   「Quantization & Flash Attention」 §2.2-2.3 (AWQ per-channel fold);
   「LLM推理降本五要素」 §2.2 (group-wise W4A8 with per-group scale and zero;
-  the top 2% of each group kept in INT8 on a side path),
+  the top 2% of each group kept in INT8 on a side path; §3.2 2:4 structured
+  sparsity followed by 4-bit group quantization),
   §5.2 (round-then-clamp to int8; KV-cache position segments of 128 tokens
   with per-channel scales).
 
@@ -45,3 +46,5 @@ __all__ = [
 from .kv import quantize_kv_segments, dequantize_kv_segments
 from .outlier import (quantize_weight_u4_g128_outliers, gemm_w4a8_g128_outliers,
                       gemm_w4a8_g128_outlier_acc, decode_records, select_outliers)
+from .sparse24 import (quantize_weight_u4_g128_sparse24, gemm_w4a8_g128_sparse24,
+                       gemm_w4a8_g128_sparse24_acc, expand_sparse24, prune_2_4)
