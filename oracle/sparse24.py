@@ -24,6 +24,9 @@ Readings (also listed with the other readings of the pages):
     code word j // 8, at bits 8 i .. 8 i + 3 for i = j % 8 < 4 and at bits
     8 (i - 4) + 4 .. 8 (i - 4) + 7 for i >= 4; its position within its 4
     inputs (0..3) sits at bits 2 j .. 2 j + 1 of the position word.
+    Channels are stored in tiles of 16: [ceil(N/16)][G][16][12] words, the
+    channels past N of the last tile zero, so that the 16 channels' words of
+    one group are 768 contiguous bytes.
 """
 from __future__ import annotations
 
@@ -48,9 +51,27 @@ def prune_2_4(w_f32: np.ndarray) -> np.ndarray:
     return keep.reshape(K, N)
 
 
+def tile16(rows: np.ndarray) -> np.ndarray:
+    """[N, G*12] words per channel -> the stored tiles [ceil(N/16), G, 16, 12]."""
+    r = np.asarray(rows)
+    N, W = r.shape
+    G = W // WORDS_PER_GROUP
+    T = (N + 15) // 16
+    out = np.zeros((T * 16, G, WORDS_PER_GROUP), r.dtype)
+    out[:N] = r.reshape(N, G, WORDS_PER_GROUP)
+    return np.ascontiguousarray(out.reshape(T, 16, G, WORDS_PER_GROUP).transpose(0, 2, 1, 3))
+
+
+def untile16(tiles: np.ndarray, N: int) -> np.ndarray:
+    """Inverse of tile16: [T, G, 16, 12] -> [N, G*12]."""
+    t = np.asarray(tiles)
+    T, G = t.shape[0], t.shape[1]
+    return np.ascontiguousarray(t.transpose(0, 2, 1, 3).reshape(T * 16, G * WORDS_PER_GROUP)[:N])
+
+
 def quantize_weight_u4_g128_sparse24(w_f32: np.ndarray):
-    """w float32 [K, N] -> (packed int32 [N, (K/128) * 12], scale float16 [N, G],
-    zero float16 [N, G]); K % 128 == 0."""
+    """w float32 [K, N] -> (packed int32 [ceil(N/16), K/128, 16, 12] (the stored
+    tiles), scale float16 [N, G], zero float16 [N, G]); K % 128 == 0."""
     w = np.asarray(w_f32, np.float32)
     K, N = w.shape
     if K % G128:
@@ -72,33 +93,42 @@ def quantize_weight_u4_g128_sparse24(w_f32: np.ndarray):
     z = np.where(ok, z, 0.0)
     q = np.rint((wg / safe[:, None, :]).astype(np.float32)) + z[:, None, :]
     q = np.where(ok[:, None, :], np.clip(q, 0, 15), 0).astype(np.int64)    # [G, 128, N]
-    pos = np.tile(np.arange(4), G128 // 4)                                  # position within 4
+    # the two kept places of every 4 inputs, in ascending order: [G, 32, N]
+    k4 = kg.reshape(G, G128 // 4, 4, N)
+    pa = np.argmax(k4, axis=2)                                              # first kept
+    pb = 3 - np.argmax(k4[:, :, ::-1, :], axis=2)                           # last kept
+    t4 = np.arange(G128 // 4)[None, :, None]
+    qa = np.take_along_axis(q, (4 * t4 + pa)[:, :, None, :].reshape(G, -1, N), axis=1)
+    qb = np.take_along_axis(q, (4 * t4 + pb)[:, :, None, :].reshape(G, -1, N), axis=1)
+    # kept values in ascending k: value 2t is pa's, 2t + 1 is pb's  -> [G, 64, N]
+    vals = np.stack([qa, qb], axis=2).reshape(G, 64, N).astype(np.uint64)
+    wher = np.stack([pa, pb], axis=2).reshape(G, 64, N).astype(np.uint64)
 
     packed = np.zeros((N, G, WORDS_PER_GROUP), np.uint32)
-    for g in range(G):
-        for b in range(4):
-            ks = np.arange(32 * b, 32 * b + 32)
-            for n in range(N):
-                kk = ks[kg[g, ks, n]]                                       # 16 kept, ascending
-                codes, where = q[g, kk, n], pos[kk]
-                w0 = w1 = pw = 0
-                for j in range(16):
-                    i = j % 8
-                    sh = 8 * i if i < 4 else 8 * (i - 4) + 4
-                    if j < 8:
-                        w0 |= int(codes[j]) << sh
-                    else:
-                        w1 |= int(codes[j]) << sh
-                    pw |= int(where[j]) << (2 * j)
-                packed[n, g, 3 * b:3 * b + 3] = (w0, w1, pw)
-    return (packed.reshape(N, G * WORDS_PER_GROUP).view(np.int32),
+    for b in range(4):
+        w0 = np.zeros((G, N), np.uint64)
+        w1 = np.zeros((G, N), np.uint64)
+        pw = np.zeros((G, N), np.uint64)
+        for j in range(16):
+            i = j % 8
+            sh = np.uint64(8 * i if i < 4 else 8 * (i - 4) + 4)
+            v = vals[:, 16 * b + j, :]
+            if j < 8:
+                w0 |= v << sh
+            else:
+                w1 |= v << sh
+            pw |= wher[:, 16 * b + j, :] << np.uint64(2 * j)
+        packed[:, :, 3 * b] = w0.T
+        packed[:, :, 3 * b + 1] = w1.T
+        packed[:, :, 3 * b + 2] = pw.T
+    return (tile16(packed.reshape(N, G * WORDS_PER_GROUP).view(np.int32)),
             np.ascontiguousarray(s16.T), np.ascontiguousarray(z.astype(np.float16).T))
 
 
-def expand_sparse24(packed) -> np.ndarray:
-    """Inverse of the storage format: int32 [N, G*12] -> dense codes int64
+def expand_sparse24(packed, N: int) -> np.ndarray:
+    """Inverse of the storage format: the stored tiles -> dense codes int64
     [N, K] with -1 at pruned positions."""
-    p = np.asarray(packed, np.int32).view(np.uint32)
+    p = untile16(np.asarray(packed, np.int32), N).view(np.uint32)
     N, W = p.shape
     G = W // WORDS_PER_GROUP
     out = np.full((N, G * G128), -1, np.int64)
@@ -118,7 +148,7 @@ def expand_sparse24(packed) -> np.ndarray:
 def gemm_w4a8_g128_sparse24_acc(xq, packed, zero16) -> np.ndarray:
     """acc[m, g, n] = sum over the kept k of group g of xq[m,k] (q[n,k] - z[n,g]),
     exact int64 [M, G, N]."""
-    codes = expand_sparse24(packed)                                        # [N, K]
+    codes = expand_sparse24(packed, np.asarray(zero16).shape[0])          # [N, K]
     N, K = codes.shape
     G = K // G128
     z = np.repeat(np.asarray(zero16, np.float16).astype(np.int64), G128, axis=1)

@@ -34,7 +34,8 @@ def test_golden_groups():
         sbits, z, words = rows[name]
         assert int(s16[n, 0].view(np.uint16)) == sbits
         assert float(z16[n, 0]) == z
-        assert [int(v) for v in packed[n].view(np.uint32)] == words
+        assert [int(v) for v in packed[0, 0, n].view(np.uint32)] == words
+    assert not packed[0, 0, 2:].any()                                   # tile rows past N are zero
 
 
 def test_pruning_invariants_and_ties():
@@ -53,7 +54,7 @@ def test_pruning_invariants_and_ties():
 def test_format_inverse_and_round_trip():
     w = _w(2, 1024, 40)
     packed, s16, z16 = quantize_weight_u4_g128_sparse24(w)
-    codes = expand_sparse24(packed)                                     # [N, K], -1 = pruned
+    codes = expand_sparse24(packed, 40)                                 # [N, K], -1 = pruned
     keep = prune_2_4(w).T
     assert ((codes >= 0) == keep).all()
     assert codes.max() <= 15
@@ -69,7 +70,7 @@ def test_volume_is_one_eighth_of_fp16_for_codes():
     K, N = 4096, 64
     packed, _, _ = quantize_weight_u4_g128_sparse24(_w(3, K, N))
     code_bytes = packed.nbytes * 8 // 12          # two of every three words are codes
-    assert code_bytes * 8 == K * N * 2            # fp16 bytes / 8
+    assert code_bytes * 8 == K * N * 2            # fp16 bytes / 8 (N a multiple of 16: no padding)
     assert packed.nbytes == K * N * 3 // 8        # codes + positions: 3 bits per dense weight
 
 
@@ -82,7 +83,7 @@ def test_reduces_to_dense_w4a8():
     xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
     xs = (rng.random(M) * 0.1 + 1e-3).astype(np.float32)
     packed, s16, z16 = quantize_weight_u4_g128_sparse24(w)
-    codes = expand_sparse24(packed)
+    codes = expand_sparse24(packed, N)
     z = np.repeat(z16.astype(np.int64), 128, axis=1)
     dense = oracle.pack_u4(np.where(codes >= 0, codes, z).astype(np.uint8))
     np.testing.assert_array_equal(gemm_w4a8_g128_sparse24_acc(xq, packed, z16),
@@ -115,6 +116,15 @@ def test_product_brute_force():
                 mag += abs(t)
             exact = Fraction(float(xs[m])) * tot
             assert abs(Fraction(float(y[m, n])) - exact) <= Fraction(float(xs[m])) * mag * Fraction(1, 2 ** 48)
+
+
+def test_tiles_round_trip():
+    rows = np.arange(37 * 24, dtype=np.int32).reshape(37, 24)          # 37 channels, 2 groups
+    from oracle.sparse24 import tile16, untile16
+    t = tile16(rows)
+    assert t.shape == (3, 2, 16, 12) and not t[2, :, 5:].any()
+    np.testing.assert_array_equal(untile16(t, 37), rows)
+    assert t[1, 1, 3, 7] == rows[16 + 3, 12 + 7]
 
 
 def test_rejects_bad_k():
