@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "w8a8": ["gemm_w8a8.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a8": ["gemm_w4a8.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a8_outl": ["gemm_w4a8.hip", "qg_decode.hpp", "qg_device.hpp"],
+    "w4a8_sp24": ["gemm_w4a8_sp24.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a16": ["gemm_w4a16.hip", "qg_decode.hpp", "qg_device.hpp"],
     "quant": ["quant.hip", "qg_device.hpp"],
     "kv": ["kv.hip", "qg_device.hpp"],
@@ -100,6 +101,8 @@ def algorithmic(wl):
         gemm = N * K // 2 + 4 * N * G + M * K + 4 * M + out_b * M * N
     elif wl.path == "w4a8_outl":   # plus one 8-byte outlier record per group, s8 per channel
         gemm = N * K // 2 + 4 * N * G + 8 * N * G + 4 * N + M * K + 4 * M + out_b * M * N
+    elif wl.path == "w4a8_sp24":   # 48 bytes of kept codes and positions per 128 inputs
+        gemm = 48 * N * G + 4 * N * G + M * K + 4 * M + out_b * M * N
     else:
         gemm = N * K // 2 + 4 * N * G + x_b * M * K + out_b * M * N
     quant = x_b * M * K + M * K + 4 * M if wl.path != "w4a16" else 0
@@ -233,6 +236,8 @@ def run_workload(wl, steps, warmup, traffic_db):
         weights = (wq, ws)
     elif wl.path == "w4a8_outl":
         weights = qg.quantize_weight_u4_g128_outliers(w_d)
+    elif wl.path == "w4a8_sp24":
+        weights = qg.quantize_weight_u4_g128_sparse24(w_d)
     else:
         weights = qg.quantize_weight_u4_g128(w_d)
     del w_d
@@ -254,6 +259,8 @@ def run_workload(wl, steps, warmup, traffic_db):
             qg.gemm_w4a8_g128(xq, xs, w[0], w[1], w[2], out_dtype=y.dtype, out=y)
         elif wl.path == "w4a8_outl":
             qg.gemm_w4a8_g128_outliers(xq, xs, *w, out_dtype=y.dtype, out=y)
+        elif wl.path == "w4a8_sp24":
+            qg.gemm_w4a8_g128_sparse24(xq, xs, *w, out_dtype=y.dtype, out=y)
         else:
             qg.gemm_w4a16_g128(x_in, w[0], w[1], w[2], out_dtype=y.dtype, out=y)
 
@@ -479,6 +486,7 @@ KERNEL_OF = {
     "w8a8_tiny": [("k_w8a8_wide<1,", "float>")],
     "w4a8_ffn_down": [("k_w4a8_dec<16, 8, 1, false, unsigned short>",)],
     "w4a8_outl_ffn_down": [("k_w4a8_dec<16, 8, 1, true, unsigned short>",)],
+    "w4a8_sp24_ffn_down": [("k_w4a8_sp24<unsigned short>",)],
     "w4a16_qkv": [("k_w4a16_dec<1,", "_Float16>"), ("k_w4a16_decILi1E", "DF16_E")],
     "w8a8_prefill": [("k_w8a8_tiled<", "unsigned short>")],
     "kv_llama2_7b_4k": [("k_kv_quant_seg<2, 4>",)],
@@ -488,6 +496,7 @@ KERNEL_LABEL = {
     "w8a8_decode_ffn_up": "gemm_w8a8_dec", "w8a8_tiny": "gemm_w8a8_wide",
     "w4a8_ffn_down": "gemm_w4a8_dec", "w4a16_qkv": "gemm_w4a16_dec", "w8a8_prefill": "gemm_w8a8_tiled",
     "kv_llama2_7b_4k": "kv_quant_seg", "w4a8_outl_ffn_down": "gemm_w4a8_outl_dec",
+    "w4a8_sp24_ffn_down": "gemm_w4a8_sp24",
 }
 COPY_BYTES = 512 * 2 ** 20
 PROFILE_COMMANDS = """\

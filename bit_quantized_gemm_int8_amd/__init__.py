@@ -17,6 +17,8 @@ Entry points (same names as the C ABI):
   apply_smoothing(x, s, out_dtype)
   quantize_weight_u4_g128_outliers(w)           -> (wq, scale, zero, records int64 [N,G], s8 f32 [N])
   gemm_w4a8_g128_outliers(xq, x_scale, wq, w_scale, w_zero, records, s8, out_dtype)
+  quantize_weight_u4_g128_sparse24(w)           -> (wsp int32 [N/16,G,16,12], scale f16 [N,G], zero f16 [N,G])
+  gemm_w4a8_g128_sparse24(xq, x_scale, wsp, w_scale, w_zero, out_dtype)
   quantize_kv_i8_segments(kv)                   -> (kv_q int8 [T,H,D], kv_scale f32 [H,ceil(T/128),D])
   dequantize_kv_i8_segments(kv_q, kv_scale, out_dtype) -> [T,H,D]
 """
@@ -35,6 +37,7 @@ __all__ = [
     "smoothquant_fold", "awq_fold", "apply_smoothing", "status_string",
     "quantize_kv_i8_segments", "dequantize_kv_i8_segments", "KV_SEGMENT",
     "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
+    "quantize_weight_u4_g128_sparse24", "gemm_w4a8_g128_sparse24",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemm.so")
@@ -58,6 +61,8 @@ _SIGNATURES = {
     "quantize_weight_u4_g128_outliers": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp],
     "gemm_w4a8_g128_outliers": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int,
                                 _vp],
+    "quantize_weight_u4_g128_sparse24": [_vp, _i64, _i64, _vp, _vp, _vp, _vp],
+    "gemm_w4a8_g128_sparse24": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
     "dequantize_kv_i8_segments": [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
 }
 
@@ -239,6 +244,39 @@ def gemm_w4a8_g128_outliers(xq, x_scale, wq, w_scale, w_zero, records, s8,
     shape = (M, K // 128 + 1, N) if out_dtype == torch.int32 else (M, N)
     y = _out(out, shape, out_dtype, xq.device)
     _call("gemm_w4a8_g128_outliers", pxq, pxs, pwq, pws, pwz, prc, ps8, M, N, K, y.data_ptr(),
+          _DTYPE_CODE[out_dtype], _stream())
+    return y
+
+
+def quantize_weight_u4_g128_sparse24(w: torch.Tensor):
+    """w f32 [K, N] -> (wsp int32 [ceil(N/16), K/128, 16, 12], scale f16 [N, G],
+    zero f16 [N, G]): 2:4 structured-sparse uint4 groups of 128."""
+    pw = _dev(w, "w", (torch.float32,))
+    K, N = w.shape
+    G = K // 128
+    wsp = torch.empty(((N + 15) // 16, G, 16, 12), dtype=torch.int32, device=w.device)
+    sc = torch.empty((N, G), dtype=torch.float16, device=w.device)
+    zz = torch.empty((N, G), dtype=torch.float16, device=w.device)
+    _call("quantize_weight_u4_g128_sparse24", pw, K, N, wsp.data_ptr(), sc.data_ptr(),
+          zz.data_ptr(), _stream())
+    return wsp, sc, zz
+
+
+def gemm_w4a8_g128_sparse24(xq, x_scale, wsp, w_scale, w_zero, out_dtype=torch.bfloat16,
+                            out=None):
+    """W4A8 on 2:4 sparse uint4 weights; int32 out_dtype returns per-group acc [M, K/128, N]."""
+    pxq = _dev(xq, "xq", (torch.int8,))
+    pws_ = _dev(wsp, "wsp", (torch.int32,))
+    pwz = _dev(w_zero, "w_zero", (torch.float16,))
+    M, K = xq.shape
+    N = w_zero.shape[0]
+    if tuple(wsp.shape) != ((N + 15) // 16, K // 128, 16, 12):
+        raise ValueError("xq, wsp and w_zero disagree on K or N")
+    pxs = _dev(x_scale, "x_scale", (torch.float32,)) if x_scale is not None else None
+    pws = _dev(w_scale, "w_scale", (torch.float16,)) if w_scale is not None else None
+    shape = (M, K // 128, N) if out_dtype == torch.int32 else (M, N)
+    y = _out(out, shape, out_dtype, xq.device)
+    _call("gemm_w4a8_g128_sparse24", pxq, pxs, pws_, pws, pwz, M, N, K, y.data_ptr(),
           _DTYPE_CODE[out_dtype], _stream())
     return y
 

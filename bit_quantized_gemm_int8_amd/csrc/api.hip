@@ -18,8 +18,9 @@ inline bool is_float_dtype(int d) { return d == QG_F32 || d == QG_F16 || d == QG
 // Largest K for which K * 127 * 127 still fits int32.
 constexpr int64_t kMaxK8 = 2147483647LL / (127 * 127);
 constexpr int64_t kMaxDim = 2147483647LL;
-// Groups per row of the outlier-retention path: its kernel stages a 16-row
-// block's scales and zero points in 80 KB of LDS (16 x (G + 1) words).
+// Groups per row of the outlier-retention and 2:4 sparse paths: their kernels
+// stage a 16-row block's scales and zero points in 80 KB of LDS
+// (16 x (G + 1) words).
 constexpr int64_t kMaxOutlierGroups = 1279;
 
 qg_status_t check_dims(int64_t M, int64_t N, int64_t K) {
@@ -150,6 +151,36 @@ qg_status_t gemm_w4a8_g128_outliers(const int8_t* xq, const float* x_scale, cons
   return hip_status(qg::launch_gemm_w4a8_outl(xq, x_scale, wq, ws, w_zero_f16, w_out_rec,
                                               w_out_scale, M, N, K, y, y_dtype,
                                               static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t quantize_weight_u4_g128_sparse24(const float* w, int64_t K, int64_t N, int32_t* wsp,
+                                             uint16_t* w_scale_f16, uint16_t* w_zero_f16,
+                                             void* stream) {
+  if (qg_status_t s = check_dims(1, N, K)) return s;
+  if (K % 128 || K / 128 > 65535) return QG_ERR_SHAPE;
+  if (N == 0) return QG_OK;
+  if (!w || !wsp || !w_scale_f16 || !w_zero_f16) return QG_ERR_NULL;
+  if (!aligned16(w) || !aligned16(wsp)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_quant_weight_u4_sp24(w, K, N, wsp, w_scale_f16, w_zero_f16,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t gemm_w4a8_g128_sparse24(const int8_t* xq, const float* x_scale, const int32_t* wsp,
+                                    const uint16_t* w_scale_f16, const uint16_t* w_zero_f16,
+                                    int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                                    void* stream) {
+  if (qg_status_t s = check_dims(M, N, K)) return s;
+  if (K % 128 || K / 128 > kMaxOutlierGroups) return QG_ERR_SHAPE;
+  if (M > 16 * 65535) return QG_ERR_SHAPE;
+  if (y_dtype == QG_I32 && M * (K / 128) * N > kMaxDim) return QG_ERR_SHAPE;
+  if (!is_float_dtype(y_dtype) && y_dtype != QG_I32) return QG_ERR_DTYPE;
+  if (M == 0 || N == 0) return QG_OK;
+  if (!xq || !wsp || !w_zero_f16 || !y) return QG_ERR_NULL;
+  if (y_dtype != QG_I32 && (!x_scale || !w_scale_f16)) return QG_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(wsp)) return QG_ERR_ALIGN;
+  const uint16_t* ws = w_scale_f16 ? w_scale_f16 : w_zero_f16;   // read, unused in I32 mode
+  return hip_status(qg::launch_gemm_w4a8_sp24(xq, x_scale, wsp, ws, w_zero_f16, M, N, K, y,
+                                              y_dtype, static_cast<hipStream_t>(stream)));
 }
 
 qg_status_t gemm_w4a16_g128(const void* x, int x_dtype, const int32_t* wq,

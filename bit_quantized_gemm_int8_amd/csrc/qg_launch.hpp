@@ -28,6 +28,11 @@ hipError_t launch_gemm_w4a8_outl(const int8_t* xq, const float* xs, const int32_
                                  const uint16_t* ws, const uint16_t* wz, const uint64_t* orec,
                                  const float* os8, int64_t M, int64_t N, int64_t K, void* y,
                                  int y_dtype, hipStream_t st);
+hipError_t launch_quant_weight_u4_sp24(const float* w, int64_t K, int64_t N, int32_t* wsp,
+                                       uint16_t* ws, uint16_t* wz, hipStream_t st);
+hipError_t launch_gemm_w4a8_sp24(const int8_t* xq, const float* xs, const int32_t* wsp,
+                                 const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
+                                 int64_t K, void* y, int y_dtype, hipStream_t st);
 hipError_t launch_gemm_w4a16(const void* x, int x_dtype, const int32_t* wq, const uint16_t* ws,
                              const uint16_t* wz, int64_t M, int64_t N, int64_t K, void* y,
                              int y_dtype, hipStream_t st);

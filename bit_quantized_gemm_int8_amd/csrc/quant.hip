@@ -448,6 +448,106 @@ __global__ __launch_bounds__(256) void k_quant_weight_u4_outl(const float* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// 2:4 structured-sparse g=128 uint4 weights (「LLM推理降本五要素」 §3.2).
+// Same workgroup shape as k_quant_weight_u4: thread (column, quarter r) owns
+// block r of the group (32 inputs).  In each 4 it keeps the 2 largest |w|
+// (strictly larger wins, so ties keep the lower index); the kept weights'
+// min / max meet in LDS; each thread then writes its block: two code words
+// (value j at bits 8 i + 4 [i >= 4], i = j % 8) and the position word (2 bits
+// per kept value), in the 16-channel tile layout.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quant_weight_u4_sp24(const float* __restrict__ w,
+                                                              int64_t K, int64_t N,
+                                                              int32_t* __restrict__ wsp,
+                                                              uint16_t* __restrict__ wscale,
+                                                              uint16_t* __restrict__ wzero) {
+  __shared__ float rlo[4][64], rhi[4][64];
+  const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 64 + c;
+  const int64_t g = blockIdx.y;
+  const int64_t G = K >> 7;
+  const bool valid = n < N;
+  float kv[16];
+  u32 posw = 0;
+  float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+  if (valid) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = w[(g * 128 + r * 32 + 4 * t + i) * N + n];
+      // top 2 of 4 by |w|, in index order with strict comparisons
+      int i0 = 0, i1 = -1;
+      float m0 = fabsf(v[0]), m1 = -1.f;
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        const float a = fabsf(v[i]);
+        if (a > m0) {
+          m1 = m0;
+          i1 = i0;
+          m0 = a;
+          i0 = i;
+        } else if (a > m1) {
+          m1 = a;
+          i1 = i;
+        }
+      }
+      const int pa = i0 < i1 ? i0 : i1, pb = i0 < i1 ? i1 : i0;
+      kv[2 * t] = v[pa];
+      kv[2 * t + 1] = v[pb];
+      posw |= ((u32)pa << (4 * t)) | ((u32)pb << (4 * t + 2));
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        lo = fminf(lo, kv[2 * t + e]);
+        hi = fmaxf(hi, kv[2 * t + e]);
+      }
+    }
+  }
+  rlo[r][c] = lo;
+  rhi[r][c] = hi;
+  __syncthreads();
+  // channels are stored in tiles of 16: [N/16][G][16][12] words
+  int32_t* dst = wsp + (((n >> 4) * G + g) * 16 + (n & 15)) * 12 + 3 * r;
+  if (!valid) {
+    if (n < ((N + 15) & ~(int64_t)15)) {   // the last tile's rows past N are zero
+      dst[0] = 0;
+      dst[1] = 0;
+      dst[2] = 0;
+    }
+    return;
+  }
+  lo = fminf(fminf(rlo[0][c], rlo[1][c]), fminf(rlo[2][c], rlo[3][c]));
+  hi = fmaxf(fmaxf(rhi[0][c], rhi[1][c]), fmaxf(rhi[2][c], rhi[3][c]));
+  const float t = (hi - lo) / 15.f;
+  const _Float16 h = f16_round_up(t);
+  const float s = (float)h;
+  float z = 0.f;
+  if (s > 0.f) z = fminf(fmaxf(__builtin_rintf(-lo / s), 0.f), 15.f);
+  u32 cw[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float q = 0.f;
+    if (s > 0.f) q = fminf(fmaxf(__builtin_rintf(kv[j] / s) + z, 0.f), 15.f);
+    const int i = j & 7;
+    cw[j >> 3] |= (u32)q << (i < 4 ? 8 * i : 8 * (i - 4) + 4);
+  }
+  dst[0] = (int32_t)cw[0];
+  dst[1] = (int32_t)cw[1];
+  dst[2] = (int32_t)posw;
+  if (r == 0) {
+    wscale[n * G + g] = __builtin_bit_cast(uint16_t, h);
+    wzero[n * G + g] = __builtin_bit_cast(uint16_t, (_Float16)z);
+  }
+}
+
+hipError_t launch_quant_weight_u4_sp24(const float* w, int64_t K, int64_t N, int32_t* wsp,
+                                       uint16_t* ws, uint16_t* wz, hipStream_t st) {
+  dim3 grid((unsigned)((N + 63) / 64), (unsigned)(K / 128)), block(256);
+  k_quant_weight_u4_sp24<<<grid, block, 0, st>>>(w, K, N, wsp, ws, wz);
+  return hipGetLastError();
+}
+
 // Per output channel: s8 = max |outlier| / 127 over the channel's records,
 // then the outliers' INT8 codes into the records' code bytes.
 __global__ __launch_bounds__(256) void k_outlier_codes(const float* __restrict__ w, int64_t K,

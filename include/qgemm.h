@@ -208,6 +208,45 @@ qg_status_t gemm_w4a8_g128_outliers(const int8_t* xq, const float* x_scale, cons
                                     void* stream);
 
 /*
+ * 2:4 structured-sparse uint4 weights (offline): of every 4 consecutive input
+ * channels of an output channel the 2 of largest |w| are kept (equal
+ * magnitudes to the lower index), and the 64 kept weights of each group of 128
+ * inputs are quantized as quantize_weight_u4_g128 does (pruned weights have
+ * no code).  「LLM推理降本五要素」 §3.2; 「现代AI加速技术全景解析」 §3.1.
+ * w:           [K][N] float, read only.
+ * wsp:         [ceil(N/16)][K/128][16][12] int32, written: channels in tiles
+ *              of 16 (the last tile's channels past N zero); per (channel,
+ *              group) four blocks of 32 inputs, each three words: code words 0
+ *              and 1, then a position word.  The block's 16 kept weights in
+ *              ascending k are values j = 0..15; value j's code sits in word
+ *              j / 8 at bits 8 i .. 8 i + 3 (i = j % 8 < 4) or
+ *              8 (i - 4) + 4 .. 8 (i - 4) + 7 (i >= 4); its place within its 4
+ *              inputs (0..3) at bits 2 j, 2 j + 1 of the position word.
+ * w_scale_f16, w_zero_f16: [N][K/128] fp16 bits, written.
+ * K must be a positive multiple of 128.
+ */
+qg_status_t quantize_weight_u4_g128_sparse24(const float* w, int64_t K, int64_t N, int32_t* wsp,
+                                             uint16_t* w_scale_f16, uint16_t* w_zero_f16,
+                                             void* stream);
+
+/*
+ * W4A8 GEMM on 2:4 sparse uint4 weights, on the sparse int8 matrix cores.
+ * 「LLM推理降本五要素」 §3.2; 「第4章：量化」 §1.1.
+ *   acc[m,g,n] = sum over the kept k of group g of xq[m,k] (q[n,k] - z[n,g])
+ *                (exact int32);
+ *   y[m,n]     = x_scale[m] * sum_g s[n,g] acc[m,g,n]   (binary32).
+ * xq [M][K] int8, x_scale [M], wsp / w_scale_f16 / w_zero_f16 from
+ * quantize_weight_u4_g128_sparse24: read.
+ * y: [M][N] of QG_F32, QG_BF16 or QG_F16; or QG_I32: [M][K/128][N] int32
+ *    holding acc[m,g,n] (x_scale and w_scale_f16 unused, may be NULL).
+ * K must be a positive multiple of 128 with K / 128 <= 1279; M <= 1048560.
+ */
+qg_status_t gemm_w4a8_g128_sparse24(const int8_t* xq, const float* x_scale, const int32_t* wsp,
+                                    const uint16_t* w_scale_f16, const uint16_t* w_zero_f16,
+                                    int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                                    void* stream);
+
+/*
  * W4A16 weight-only GEMM: 16-bit float activations, g=128 uint4 weights
  * unpacked to exact (q - z) values in registers and fed to the fp16 (or bf16)
  * matrix cores; each group's binary32 partial sum is then scaled by s.

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
               "quantize_weight_u4_g128", "gemm_w8a8", "gemm_w4a8_g128", "gemm_w4a16_g128",
               "smoothquant_fold", "awq_fold", "apply_smoothing", "qg_status_string",
               "qg_abi_version", "quantize_kv_i8_segments", "dequantize_kv_i8_segments",
-              "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers"]:
+              "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
+              "quantize_weight_u4_g128_sparse24", "gemm_w4a8_g128_sparse24"]:
         assert n in names, n
 
 
@@ -113,6 +114,17 @@ def test_validation_codes():
     assert go(A, A, A, A, A, A, A, 4, 4, 128, A, 9, None) == DTYPE
     assert go(A, A, A, A, A, MIS, A, 4, 4, 128, A, 2, None) == ALIGN
     assert go(None, None, None, None, None, None, None, 0, 4, 128, None, 2, None) == OK
+    us = lib.quantize_weight_u4_g128_sparse24
+    assert us(A, 130, 8, A, A, A, None) == SHAPE
+    assert us(A, 128, 8, A, None, A, None) == NULL
+    assert us(A, 128, 8, MIS, A, A, None) == ALIGN
+    gs = lib.gemm_w4a8_g128_sparse24
+    assert gs(A, A, A, A, A, 4, 4, 192, A, 2, None) == SHAPE
+    assert gs(A, A, A, A, A, 16 * 65535 + 1, 4, 128, A, 2, None) == SHAPE
+    assert gs(A, None, A, A, A, 4, 4, 128, A, 2, None) == NULL
+    assert gs(A, A, A, A, A, 4, 4, 128, A, 7, None) == DTYPE
+    assert gs(A, A, MIS, A, A, 4, 4, 128, A, 2, None) == ALIGN
+    assert gs(None, None, None, None, None, 4, 0, 128, None, 2, None) == OK
     assert "SHAPE" in lib.qg_status_string(2).decode()
 
 

@@ -67,9 +67,10 @@ WORKLOADS = (
 
 # Variants of a workload on another path, with the same draws (same index and
 # seeds): the FFN-down layer with the top 3 weights of each group kept in INT8
-# (「LLM推理降本五要素」 §2.2).
+# (「LLM推理降本五要素」 §2.2), and pruned 2:4 before 4-bit quantization (§3.2).
 VARIANT_WORKLOADS = (
     replace(WORKLOADS[2], name="w4a8_outl_ffn_down", path="w4a8_outl"),
+    replace(WORKLOADS[2], name="w4a8_sp24_ffn_down", path="w4a8_sp24"),
 )
 
 
