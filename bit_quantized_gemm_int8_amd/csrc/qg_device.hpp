@@ -91,6 +91,33 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Max of non-negative values over a wave through DPP: rotations within each
+// row of 16 lanes (every lane then holds its row's max), then the four rows'
+// values read into scalars.  No LDS round trips.  The result is uniform.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  int x = __float_as_int(v);   // non-negative floats order as their bit patterns
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x121, 0xF, 0xF, false));   // row_ror:1
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x122, 0xF, 0xF, false));   // row_ror:2
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, false));   // row_ror:4
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));   // row_ror:8
+  const int a = max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16));
+  const int b = max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48));
+  return __int_as_float(max(a, b));
+}
+
+// Max of non-negative values over a workgroup of NT threads, for a kernel
+// that reduces once: one barrier (red is not reused afterwards).
+template <int NT>
+__device__ __forceinline__ float block_max_nonneg_once(float v, float* red /* LDS, NT/64 */) {
+  v = wave_max_nonneg(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
 // Max over a whole workgroup of NT threads; every thread gets the result.
 template <int NT>
 __device__ __forceinline__ float block_max(float v, float* red /* LDS, NT/64 floats */) {

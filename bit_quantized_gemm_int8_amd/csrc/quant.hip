@@ -95,25 +95,27 @@ __device__ __forceinline__ v4i codes16(const float (&v)[16], float s, float r) {
 template <int DT>
 constexpr int esize() { return DT == F32 ? 4 : 2; }
 
-// CH > 0: row cached in registers.  CH == 0: rows too long for that; the
-// second pass re-reads the row (it is then L2 resident).
-template <int DT, int CH>
-__global__ __launch_bounds__(256) void k_quant_per_token(const void* __restrict__ x, int64_t K,
-                                                         int8_t* __restrict__ xq,
-                                                         float* __restrict__ xs) {
-  __shared__ float red[4];
+// NT threads per row (256 to 1024: more for long rows, so that few rows
+// still keep many lanes busy).  CH > 0: row cached in registers.  CH == 0:
+// rows too long for that; the second pass re-reads the row (it is then L2
+// resident).
+template <int DT, int CH, int NT>
+__global__ __launch_bounds__(NT) void k_quant_per_token(const void* __restrict__ x, int64_t K,
+                                                        int8_t* __restrict__ xq,
+                                                        float* __restrict__ xs) {
+  __shared__ float red[NT / kWave];
   const int64_t row = blockIdx.x;
   const char* xr = reinterpret_cast<const char*>(x) + row * K * esize<DT>();
   int8_t* qr = xq + row * K;
   const int nch = (int)(K >> 4);
   float amax = 0.f;
   if constexpr (CH > 0) {
-    // K <= 1024 * 16 here, so the row's bytes fit a buffer resource
+    // K <= 4 * 1024 * 16 here, so the row's bytes fit a buffer resource
     const rsrc_t rr = make_rsrc(xr, (uint32_t)(K * esize<DT>()));
     v4i raw[CH][4];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int idx = threadIdx.x + c * 256;
+      const int idx = threadIdx.x + c * NT;
       load_chunk16_rs<DT>(rr, idx < nch, idx, raw[c]);
     }
     float v[CH][16];
@@ -123,25 +125,25 @@ __global__ __launch_bounds__(256) void k_quant_per_token(const void* __restrict_
 #pragma unroll
       for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[c][e]));   // zeros past the end
     }
-    amax = block_max<256>(amax, red);
+    amax = block_max_nonneg_once<NT>(amax, red);
     const float s = amax / 127.f, r = sym_code_r(amax, s);
     if (threadIdx.x == 0) xs[row] = amax > 0.f ? s : 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int idx = threadIdx.x + c * 256;
+      const int idx = threadIdx.x + c * NT;
       if (idx < nch) st16(qr + (int64_t)idx * 16, codes16(v[c], s, r));
     }
   } else {
-    for (int idx = threadIdx.x; idx < nch; idx += 256) {
+    for (int idx = threadIdx.x; idx < nch; idx += NT) {
       float v[16];
       load_chunk16<DT>(xr, idx, v);
 #pragma unroll
       for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
     }
-    amax = block_max<256>(amax, red);
+    amax = block_max_nonneg_once<NT>(amax, red);
     const float s = amax / 127.f, r = sym_code_r(amax, s);
     if (threadIdx.x == 0) xs[row] = amax > 0.f ? s : 0.f;
-    for (int idx = threadIdx.x; idx < nch; idx += 256) {
+    for (int idx = threadIdx.x; idx < nch; idx += NT) {
       float v[16];
       load_chunk16<DT>(xr, idx, v);
       st16(qr + (int64_t)idx * 16, codes16(v, s, r));
@@ -153,17 +155,19 @@ template <int DT>
 static hipError_t quant_per_token_dt(const void* x, int64_t M, int64_t K, int8_t* xq, float* xs,
                                      hipStream_t st) {
   const int64_t nch = K / 16;
-  dim3 grid((unsigned)M), block(256);
+  const dim3 grid((unsigned)M);
   if (nch <= 256)
-    k_quant_per_token<DT, 1><<<grid, block, 0, st>>>(x, K, xq, xs);
+    k_quant_per_token<DT, 1, 256><<<grid, 256, 0, st>>>(x, K, xq, xs);
   else if (nch <= 512)
-    k_quant_per_token<DT, 2><<<grid, block, 0, st>>>(x, K, xq, xs);
-  else if (nch <= 768)
-    k_quant_per_token<DT, 3><<<grid, block, 0, st>>>(x, K, xq, xs);
+    k_quant_per_token<DT, 1, 512><<<grid, 512, 0, st>>>(x, K, xq, xs);
   else if (nch <= 1024)
-    k_quant_per_token<DT, 4><<<grid, block, 0, st>>>(x, K, xq, xs);
+    k_quant_per_token<DT, 1, 1024><<<grid, 1024, 0, st>>>(x, K, xq, xs);
+  else if (nch <= 2048)
+    k_quant_per_token<DT, 2, 1024><<<grid, 1024, 0, st>>>(x, K, xq, xs);
+  else if (nch <= 4096)
+    k_quant_per_token<DT, 4, 1024><<<grid, 1024, 0, st>>>(x, K, xq, xs);
   else
-    k_quant_per_token<DT, 0><<<grid, block, 0, st>>>(x, K, xq, xs);
+    k_quant_per_token<DT, 0, 1024><<<grid, 1024, 0, st>>>(x, K, xq, xs);
   return hipGetLastError();
 }
 
