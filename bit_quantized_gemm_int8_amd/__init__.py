@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   quantize_weight_i8_per_channel(w)             -> (wq int8 [N,K], w_scale f32 [N])
   quantize_weight_u4_g128(w)                    -> (wq int32 [N,K/8], scale f16 [N,G], zero f16 [N,G])
   gemm_w8a8(xq, x_scale, wq, w_scale, out_dtype)
+  quantize_gemm_w8a8(x, wq, w_scale, out_dtype)  -> (y, xq, x_scale): both steps in one call
   gemm_w4a8_g128(xq, x_scale, wq, w_scale, w_zero, out_dtype)
   gemm_w4a16_g128(x, wq, w_scale, w_zero, out_dtype)
   smoothquant_fold(x_cal, w) / awq_fold(x_cal, w) -> (s f32 [K], w_folded f32 [K,N])
@@ -33,7 +34,7 @@ import torch
 __all__ = [
     "LIB_PATH", "load", "QG_F32", "QG_F16", "QG_BF16", "QG_I32",
     "quantize_per_token_i8", "quantize_weight_i8_per_channel", "quantize_weight_u4_g128",
-    "gemm_w8a8", "gemm_w4a8_g128", "gemm_w4a16_g128",
+    "gemm_w8a8", "gemm_w4a8_g128", "gemm_w4a16_g128", "quantize_gemm_w8a8",
     "smoothquant_fold", "awq_fold", "apply_smoothing", "status_string",
     "quantize_kv_i8_segments", "dequantize_kv_i8_segments", "KV_SEGMENT",
     "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
@@ -52,6 +53,7 @@ _SIGNATURES = {
     "quantize_weight_i8_per_channel": [_vp, _i64, _i64, _vp, _vp, _vp],
     "quantize_weight_u4_g128": [_vp, _i64, _i64, _vp, _vp, _vp, _vp],
     "gemm_w8a8": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
+    "quantize_gemm_w8a8": [_vp, _int, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _int, _vp],
     "gemm_w4a8_g128": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
     "gemm_w4a16_g128": [_vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
     "smoothquant_fold": [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp],
@@ -172,6 +174,30 @@ def gemm_w8a8(xq, x_scale, wq, w_scale, out_dtype=torch.bfloat16, out=None):
     _call("gemm_w8a8", pxq, pxs, pwq, pws, M, N, K, y.data_ptr(), _DTYPE_CODE[out_dtype],
           _stream())
     return y
+
+
+_FUSE = {None: 0, False: 1, True: 2}
+
+
+def quantize_gemm_w8a8(x, wq, w_scale, out_dtype=torch.bfloat16, out=None, xq_out=None, fuse=None):
+    """x [M, K] (f32/f16/bf16) -> (y [M, N], xq int8 [M, K], x_scale f32 [M]):
+    per-token quantization and the W8A8 product in one call.  fuse: None lets
+    the library choose, True runs the one-kernel form wherever it covers the
+    shape, False the two kernels; the results are the same."""
+    px = _dev(x, "x", _FLOATS)
+    pwq = _dev(wq, "wq", (torch.int8,))
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("x and wq disagree on K")
+    pws = _dev(w_scale, "w_scale", (torch.float32,)) if w_scale is not None else None
+    y = _out(out, (M, N), out_dtype, x.device)
+    xq, xs = xq_out if xq_out is not None else (None, None)
+    xq = _out(xq, (M, K), torch.int8, x.device)
+    xs = _out(xs, (M,), torch.float32, x.device)
+    _call("quantize_gemm_w8a8", px, _DTYPE_CODE[x.dtype], pwq, pws, M, N, K, y.data_ptr(),
+          _DTYPE_CODE[out_dtype], xq.data_ptr(), xs.data_ptr(), _FUSE[fuse], _stream())
+    return y, xq, xs
 
 
 def gemm_w4a8_g128(xq, x_scale, wq, w_scale, w_zero, out_dtype=torch.bfloat16, out=None):

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libqgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "quant.hip", "fold.hip", "gemm_w8a8.hip", "gemm_w4a8.hip", "gemm_w4a16.hip",
-           "kv.hip", "gemm_w4a8_sp24.hip"]
+           "kv.hip", "gemm_w4a8_sp24.hip", "gemm_w8a8_fq.hip"]
 
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

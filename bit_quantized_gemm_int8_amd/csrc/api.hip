@@ -49,6 +49,7 @@ const char* qg_status_string(int status) {
     case QG_ERR_ALIGN: return "QG_ERR_ALIGN: a pointer is not 16-byte aligned";
     case QG_ERR_DTYPE: return "QG_ERR_DTYPE: unsupported dtype for this function";
     case QG_ERR_HIP: return "QG_ERR_HIP: the HIP runtime refused the launch";
+    case QG_ERR_ARG: return "QG_ERR_ARG: unsupported mode argument for this function";
     default: return "unknown qg status";
   }
 }
@@ -100,6 +101,26 @@ qg_status_t gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
   if (!aligned16(xq) || !aligned16(wq)) return QG_ERR_ALIGN;
   return hip_status(qg::launch_gemm_w8a8(xq, x_scale, wq, w_scale, M, N, K, y, y_dtype,
                                          static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t quantize_gemm_w8a8(const void* x, int x_dtype, const int8_t* wq, const float* w_scale,
+                               int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int8_t* xq,
+                               float* x_scale, int fuse, void* stream) {
+  if (qg_status_t s = check_dims(M, N, K)) return s;
+  if (K % 16 || K > kMaxK8) return QG_ERR_SHAPE;
+  if (fuse != QG_FUSE_AUTO && fuse != QG_FUSE_NEVER && fuse != QG_FUSE_FIT) return QG_ERR_ARG;
+  if (!is_float_dtype(x_dtype)) return QG_ERR_DTYPE;
+  if (!is_float_dtype(y_dtype) && y_dtype != QG_I32) return QG_ERR_DTYPE;
+  if (M == 0) return QG_OK;
+  if (!x || !xq || !x_scale) return QG_ERR_NULL;
+  if (N > 0 && (!wq || !y || (y_dtype != QG_I32 && !w_scale))) return QG_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xq) || (N > 0 && !aligned16(wq))) return QG_ERR_ALIGN;
+  if (N == 0)   // nothing to multiply: the codes and scales alone
+    return hip_status(qg::launch_quant_per_token(x, x_dtype, M, K, xq, x_scale,
+                                                 static_cast<hipStream_t>(stream)));
+  return hip_status(qg::launch_quantize_gemm_w8a8(x, x_dtype, wq, w_scale, M, N, K, y, y_dtype,
+                                                  xq, x_scale, fuse,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 qg_status_t gemm_w4a8_g128(const int8_t* xq, const float* x_scale, const int32_t* wq,

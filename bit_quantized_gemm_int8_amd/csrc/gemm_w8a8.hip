@@ -253,6 +253,8 @@ __global__ __launch_bounds__(64 * NB) void k_w8a8_wide(
 // swizzle is applied by choosing which chunk each lane fetches.
 // ---------------------------------------------------------------------------
 constexpr int TBM = 256, TBN = 256, TBK = 128;
+// tile-rows per column-major group of the tile walk (see k_w8a8_tiled)
+constexpr int kPrefillGroupRows = 4;
 constexpr int kStageBytes = (TBM + TBN) * TBK;   // 64 KB
 
 __shared__ __attribute__((aligned(16))) int8_t g_stage0[kStageBytes];
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict
                                                         const int8_t* __restrict__ wq,
                                                         const float* __restrict__ ws, int M,
                                                         int N, int K, OutT* __restrict__ y,
-                                                        int vec_store) {
+                                                        int vec_store, int group_rows) {
   constexpr int WJ = NW == 4 ? 4 : 2;           // column tiles per wave
   constexpr int WAVES_N = NW / 2;               // waves across the 256 columns
   const int tid = threadIdx.x, lane = tid & 63;
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict
     const int xcd = bid % 8, idx = bid / 8;
     bid = xcd * per + (xcd < rem ? xcd : rem) + idx;
   }
-  constexpr int GROUP = 4;
+  const int GROUP = group_rows;
   const int group = bid / (GROUP * tiles_n);
   const int first_m = group * GROUP;
   const int gsize = (tiles_m - first_m) < GROUP ? (tiles_m - first_m) : GROUP;
@@ -535,23 +537,43 @@ static void launch_w8a8_wide(const int8_t* xq, const float* xs, const int8_t* wq
   }
 }
 
+// Token rows longer than kDecLdsMaxBytes (a long K: the down projection of
+// an FFN) still stage whole in LDS up to kDecLdsBigBytes, at one workgroup
+// per compute unit.
+constexpr size_t kDecLdsBigBytes = 112 * 1024;
+
+// Waves per 16-row workgroup of the decode kernel (they split K): more when
+// few 16-row blocks would leave the chip short of loads in flight (measured
+// on MI355X: K = 11008, N = 4096 and K = 4096, N = 11008; 16 waves is slower).
+static int dec_waves(int N, size_t lds) {
+  if (lds > kDecLdsMaxBytes) return 8;
+  return (N + 15) / 16 <= 384 ? 8 : 4;
+}
+
+template <int WAVES, typename OutT>
+static void dec_mr(int mr, const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
+                   int M, int N, int K, OutT* y, size_t lds, hipStream_t st) {
+  constexpr int UB = 2;
+  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
+  switch (mr) {
+    case 1: k_w8a8_dec<1, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+    case 2: k_w8a8_dec<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+    case 4: k_w8a8_dec<4, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+    default: k_w8a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+  }
+}
+
 template <typename OutT>
 static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* wq,
                               const float* ws, int M, int N, int K, OutT* y, hipStream_t st) {
   if (M <= 64) {
-    // shapes picked by measurement on MI355X (decode, K = 4096, N = 11008)
-    constexpr int WAVES = 4;
     const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
     const size_t lds = (size_t)mr * stage_pitch(K);
-    if (M <= 8 && lds <= kDecLdsMaxBytes) {
-      constexpr int UB = 2;
-      const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
-      switch (mr) {
-        case 1: k_w8a8_dec<1, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-        case 2: k_w8a8_dec<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-        case 4: k_w8a8_dec<4, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-        default: k_w8a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-      }
+    if (M <= 8 && lds <= kDecLdsBigBytes) {
+      const int waves = dec_waves(N, lds);
+      if (waves >= 16) dec_mr<16, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, st);
+      else if (waves >= 8) dec_mr<8, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, st);
+      else dec_mr<4, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, st);
     } else if (M <= 16) {
       launch_w8a8_wide<1, OutT>(xq, xs, wq, ws, M, N, K, y, st);
     } else if (M <= 32) {
@@ -566,7 +588,7 @@ static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* w
     // whole-line stores need every row of y to start on a 16-byte boundary
     const int vec = ((uintptr_t)y % 16 == 0) && ((size_t)N * sizeof(OutT)) % 16 == 0;
     k_w8a8_tiled<kPrefillWaves, OutT><<<dim3((unsigned)tiles), dim3(64 * kPrefillWaves), 0, st>>>(
-        xq, xs, wq, ws, M, N, K, y, vec);
+        xq, xs, wq, ws, M, N, K, y, vec, kPrefillGroupRows);
   }
   return hipGetLastError();
 }

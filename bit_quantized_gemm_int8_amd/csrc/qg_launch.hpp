@@ -9,6 +9,8 @@
 namespace qg {
 
 enum DType { F32 = 0, F16 = 1, BF16 = 2, I32 = 3 };
+// fused quantize + W8A8 policy (values of the C interface's qg_fuse)
+enum Fuse { kFuseAuto = 0, kFuseNever = 1, kFuseFit = 2 };
 
 hipError_t launch_quant_per_token(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* xq,
                                   float* x_scale, hipStream_t st);
@@ -18,6 +20,10 @@ hipError_t launch_quant_weight_u4(const float* w, int64_t K, int64_t N, int32_t*
                                   uint16_t* ws, uint16_t* wz, hipStream_t st);
 hipError_t launch_gemm_w8a8(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
                             int64_t M, int64_t N, int64_t K, void* y, int y_dtype, hipStream_t st);
+hipError_t launch_quantize_gemm_w8a8(const void* x, int x_dtype, const int8_t* wq,
+                                     const float* ws, int64_t M, int64_t N, int64_t K, void* y,
+                                     int y_dtype, int8_t* xq, float* xs, int fuse,
+                                     hipStream_t st);
 hipError_t launch_gemm_w4a8(const int8_t* xq, const float* xs, const int32_t* wq,
                             const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
                             int64_t K, void* y, int y_dtype, hipStream_t st);

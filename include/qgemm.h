@@ -32,7 +32,7 @@
  *     problem: nothing is launched and QG_OK is returned.
  *   Errors: arguments are checked on the host before anything is enqueued; a
  *     bad argument returns QG_ERR_NULL / QG_ERR_SHAPE / QG_ERR_ALIGN /
- *     QG_ERR_DTYPE and enqueues nothing.  A failed launch returns QG_ERR_HIP.
+ *     QG_ERR_DTYPE / QG_ERR_ARG and enqueues nothing.  A failed launch returns QG_ERR_HIP.
  *     A device fault surfaces at the caller's next synchronisation.  Inputs
  *     holding NaN or Inf give undefined codes and outputs.
  *   Rounding: quantization decisions use IEEE binary32 with correctly rounded
@@ -58,7 +58,8 @@ typedef enum qg_status {
                         divisibility rule stated below                         */
   QG_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned                        */
   QG_ERR_DTYPE = 4,  /* a dtype argument is not one the function accepts       */
-  QG_ERR_HIP = 5     /* the HIP runtime refused the launch                      */
+  QG_ERR_HIP = 5,    /* the HIP runtime refused the launch                      */
+  QG_ERR_ARG = 6     /* a mode argument is not one the function accepts        */
 } qg_status_t;
 
 typedef enum qg_dtype {
@@ -139,6 +140,36 @@ qg_status_t quantize_weight_u4_g128(const float* w, int64_t K, int64_t N, int32_
 qg_status_t gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
                       const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
                       int y_dtype, void* stream);
+
+/*
+ * Per-token int8 quantization of the activations and the W8A8 GEMM in one
+ * call: the results of quantize_per_token_i8 followed by gemm_w8a8, bit for
+ * bit (same codes, scales, accumulators and epilogue roundings).
+ * 「第4章：量化」 §1.3, §1.2, §1.1, §2.3; 「LLM推理降本五要素」 §2.1, §5.2.
+ * x:        [M][K] of x_dtype (QG_F32, QG_F16 or QG_BF16), read only.
+ * wq [N][K] int8, w_scale [N] float: read (w_scale unused for QG_I32).
+ * y:        [M][N] of y_dtype (QG_F32, QG_BF16, QG_F16 or QG_I32), written.
+ * xq [M][K] int8 and x_scale [M] float: written (the activation codes and
+ *           scales, as quantize_per_token_i8 writes them).
+ * fuse:     QG_FUSE_AUTO, QG_FUSE_NEVER or QG_FUSE_FIT (below).
+ * K must be a positive multiple of 16 (K <= 133144).  The fused kernel
+ * quantizes the token rows into on-chip memory and runs the product in one
+ * launch (no separate quantization pass); it covers 16-bit activations with
+ * M <= 8 and M K <= 32768.  QG_FUSE_FIT runs it on every shape it covers,
+ * QG_FUSE_NEVER never, QG_FUSE_AUTO only where it is the faster choice
+ * (M <= 4 and N K >= 2^25: a long weight stream, few token rows); every
+ * other case runs the two steps in sequence.  The results do not depend on
+ * the choice.  N == 0 computes xq and x_scale only.
+ */
+typedef enum qg_fuse {
+  QG_FUSE_AUTO = 0,
+  QG_FUSE_NEVER = 1,
+  QG_FUSE_FIT = 2
+} qg_fuse_t;
+
+qg_status_t quantize_gemm_w8a8(const void* x, int x_dtype, const int8_t* wq, const float* w_scale,
+                               int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int8_t* xq,
+                               float* x_scale, int fuse, void* stream);
 
 /*
  * W4A8 GEMM with g=128 uint4 weights unpacked and zero-point corrected inside

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
               "smoothquant_fold", "awq_fold", "apply_smoothing", "qg_status_string",
               "qg_abi_version", "quantize_kv_i8_segments", "dequantize_kv_i8_segments",
               "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
-              "quantize_weight_u4_g128_sparse24", "gemm_w4a8_g128_sparse24"]:
+              "quantize_weight_u4_g128_sparse24", "gemm_w4a8_g128_sparse24",
+              "quantize_gemm_w8a8"]:
         assert n in names, n
 
 
@@ -125,6 +126,16 @@ def test_validation_codes():
     assert gs(A, A, A, A, A, 4, 4, 128, A, 7, None) == DTYPE
     assert gs(A, A, MIS, A, A, 4, 4, 128, A, 2, None) == ALIGN
     assert gs(None, None, None, None, None, 4, 0, 128, None, 2, None) == OK
+    fq = lib.quantize_gemm_w8a8
+    assert fq(A, 2, A, A, 8, 16, 4096, A, 2, None, A, 0, None) == NULL     # xq needed
+    assert fq(A, 2, A, None, 8, 16, 4096, A, 2, A, A, 0, None) == NULL     # w_scale needed unless I32
+    assert fq(A, 2, A, A, 8, 16, 4100, A, 2, A, A, 0, None) == SHAPE
+    assert fq(A, 3, A, A, 8, 16, 4096, A, 2, A, A, 0, None) == DTYPE
+    assert fq(MIS, 2, A, A, 8, 16, 4096, A, 2, A, A, 0, None) == ALIGN
+    assert fq(A, 2, A, A, 8, 16, 4096, A, 2, A, A, 3, None) == 6          # QG_ERR_ARG
+    assert fq(A, 2, A, A, 8, 16, 4096, A, 2, A, A, -1, None) == 6
+    assert fq(None, 2, None, None, 0, 16, 4096, None, 2, None, None, 2, None) == OK
+    assert "ARG" in lib.qg_status_string(6).decode()
     assert "SHAPE" in lib.qg_status_string(2).decode()
 
 

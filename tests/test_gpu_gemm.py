@@ -27,7 +27,13 @@ W8A8_SHAPES = [(16, 512, 512), (1, 16, 16), (3, 17, 48), (8, 11008, 4096), (17, 
                (5, 33, 4112), (12, 100, 9008), (16, 40, 8192),
                # wide decode kernel: three weight blocks per workgroup with the last
                # workgroup partly past N, and the full 64-token FFN-up shape
-               (40, 10256, 512), (64, 11008, 4096)]
+               (40, 10256, 512), (64, 11008, 4096),
+               # decode kernel with long token rows (above 80 KB of LDS, one
+               # workgroup per compute unit), the last size that fits and the first
+               # that does not; 8 and 4 waves per workgroup on either side of 384
+               # weight blocks
+               (8, 40, 11008), (6, 1040, 13824), (8, 24, 14336), (3, 5000, 20000),
+               (4, 6144, 1024), (2, 6160, 4096)]
 
 
 def _codes(rng, shape):
