@@ -160,8 +160,8 @@ static hipError_t quant_per_token_dt(const void* x, int64_t M, int64_t K, int8_t
     k_quant_per_token<DT, 1, 256><<<grid, 256, 0, st>>>(x, K, xq, xs);
   else if (nch <= 512)
     k_quant_per_token<DT, 1, 512><<<grid, 512, 0, st>>>(x, K, xq, xs);
-  else if (nch <= 1024)
-    k_quant_per_token<DT, 1, 1024><<<grid, 1024, 0, st>>>(x, K, xq, xs);
+  else if (nch <= 1024)   // 512 threads x 2 chunks: measured faster than 1024 x 1 on MI355X
+    k_quant_per_token<DT, 2, 512><<<grid, 512, 0, st>>>(x, K, xq, xs);
   else if (nch <= 2048)
     k_quant_per_token<DT, 2, 1024><<<grid, 1024, 0, st>>>(x, K, xq, xs);
   else if (nch <= 4096)

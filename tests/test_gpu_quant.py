@@ -37,7 +37,8 @@ def _check_per_token(x32, fmt):
 
 @pytest.mark.parametrize("fmt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("M,K", [(16, 512), (8, 4096), (16, 11008), (3, 16), (5, 48),
-                                 (2, 4112), (7, 12304), (2, 16400), (3, 20000)])
+                                 (2, 4112), (7, 12304), (2, 16400), (3, 20000), (4, 16384),
+                                 (2, 8208)])
 def test_per_token_parity(fmt, M, K):
     rng = np.random.default_rng(M * 100003 + K)
     x = rng.standard_normal((M, K)).astype(np.float32)
