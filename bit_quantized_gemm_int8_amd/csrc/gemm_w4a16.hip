@@ -492,6 +492,20 @@ static void launch_w4a16_wide(const uint16_t* x, const int32_t* wq, const uint16
   }
 }
 
+template <int WAVES, int XDT, typename OutT>
+static void dec_w4a16_mr(int mr, const uint16_t* x, const int32_t* wq, const uint16_t* ws,
+                         const uint16_t* wz, int M, int N, int K, OutT* y, size_t lds,
+                         hipStream_t st) {
+  constexpr int UB = 1;  // measured on MI355X
+  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
+  switch (mr) {
+    case 1: k_w4a16_dec<1, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    case 2: k_w4a16_dec<2, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    case 4: k_w4a16_dec<4, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    default: k_w4a16_dec<8, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+  }
+}
+
 template <int XDT, typename OutT>
 static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
                                const uint16_t* wz, int M, int N, int K, OutT* y, hipStream_t st) {
@@ -499,14 +513,11 @@ static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint1
   const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
   const size_t lds = (size_t)mr * stage_pitch(2 * K) + (size_t)16 * sz_pitch(G) * 4;
   if (M <= 8 && lds <= kDecLdsMaxBytes) {
-    constexpr int WAVES = 4, UB = 1;  // measured on MI355X
-    const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
-    switch (mr) {
-      case 1: k_w4a16_dec<1, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-      case 2: k_w4a16_dec<2, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-      case 4: k_w4a16_dec<4, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-      default: k_w4a16_dec<8, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-    }
+    // 8 waves split K when few 16-row blocks would leave the chip short of
+    // loads in flight (measured on MI355X: K = 11008, N = 4096 takes 8.6 us
+    // with 8 waves, 10.4 us with 4; N >= 11008 is best with 4)
+    if ((N + 15) / 16 <= 384) dec_w4a16_mr<8, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds, st);
+    else dec_w4a16_mr<4, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds, st);
     return hipGetLastError();
   }
   const size_t lds_wide = (size_t)16 * wide_waves(N) * sz_pitch(G) * 4;

@@ -374,7 +374,7 @@ __global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict
                                                         const int8_t* __restrict__ wq,
                                                         const float* __restrict__ ws, int M,
                                                         int N, int K, OutT* __restrict__ y,
-                                                        int vec_store, int group_rows) {
+                                                        int vec_store) {
   constexpr int WJ = NW == 4 ? 4 : 2;           // column tiles per wave
   constexpr int WAVES_N = NW / 2;               // waves across the 256 columns
   const int tid = threadIdx.x, lane = tid & 63;
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict
     const int xcd = bid % 8, idx = bid / 8;
     bid = xcd * per + (xcd < rem ? xcd : rem) + idx;
   }
-  const int GROUP = group_rows;
+  constexpr int GROUP = kPrefillGroupRows;
   const int group = bid / (GROUP * tiles_n);
   const int first_m = group * GROUP;
   const int gsize = (tiles_m - first_m) < GROUP ? (tiles_m - first_m) : GROUP;
@@ -588,7 +588,7 @@ static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* w
     // whole-line stores need every row of y to start on a 16-byte boundary
     const int vec = ((uintptr_t)y % 16 == 0) && ((size_t)N * sizeof(OutT)) % 16 == 0;
     k_w8a8_tiled<kPrefillWaves, OutT><<<dim3((unsigned)tiles), dim3(64 * kPrefillWaves), 0, st>>>(
-        xq, xs, wq, ws, M, N, K, y, vec, kPrefillGroupRows);
+        xq, xs, wq, ws, M, N, K, y, vec);
   }
   return hipGetLastError();
 }
