@@ -559,7 +559,8 @@ static void dec_mr(int mr, const int8_t* xq, const float* xs, const int8_t* wq, 
     case 1: k_w8a8_dec<1, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
     case 2: k_w8a8_dec<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
     case 4: k_w8a8_dec<4, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-    default: k_w8a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+    case 8: k_w8a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+    default: k_w8a8_dec<16, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
   }
 }
 
@@ -567,9 +568,13 @@ template <typename OutT>
 static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* wq,
                               const float* ws, int M, int N, int K, OutT* y, hipStream_t st) {
   if (M <= 64) {
-    const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+    const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
     const size_t lds = (size_t)mr * stage_pitch(K);
-    if (M <= 8 && lds <= kDecLdsBigBytes) {
+    // 9..16 token rows: the decode kernel when N gives at most 256 blocks of
+    // 16 weight rows (one workgroup per CU; measured on MI355X: N = 4096
+    // 6.4 us against the wide kernel's 8.4, K = 6912 7.9 against 12.5);
+    // wider layers keep the wide kernel (N = 11008: 10.9 against 11.3 us)
+    if (M <= 16 && lds <= kDecLdsBigBytes && (M <= 8 || (N + 15) / 16 <= 256)) {
       const int waves = dec_waves(N, lds);
       if (waves >= 16) dec_mr<16, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, st);
       else if (waves >= 8) dec_mr<8, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, st);

@@ -134,7 +134,7 @@ qg_status_t quantize_weight_u4_g128(const float* w, int64_t K, int64_t N, int32_
  * y: [M][N] of y_dtype, written: QG_F32, QG_BF16 or QG_F16 (the scaled
  *    result), or QG_I32 (acc itself, scales ignored and may be NULL).
  * K must be a positive multiple of 16 (|acc| <= K 127^2 must fit int32, so
- * K <= 133144).  M <= 64 runs the weight-streaming decode kernel, larger M the
+ * K <= 133144).  M <= 64 runs a weight-streaming decode kernel, larger M the
  * LDS-tiled matrix-core kernel.
  */
 qg_status_t gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,

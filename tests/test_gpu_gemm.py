@@ -33,7 +33,10 @@ W8A8_SHAPES = [(16, 512, 512), (1, 16, 16), (3, 17, 48), (8, 11008, 4096), (17, 
                # that does not; 8 and 4 waves per workgroup on either side of 384
                # weight blocks
                (8, 40, 11008), (6, 1040, 13824), (8, 24, 14336), (3, 5000, 20000),
-               (4, 6144, 1024), (2, 6160, 4096)]
+               (4, 6144, 1024), (2, 6160, 4096),
+               # 9..16 token rows on the decode kernel (N/16 <= 256), at its LDS
+               # limit, and just past 256 weight blocks (wide kernel)
+               (16, 4096, 4096), (9, 300, 6912), (13, 4112, 1024)]
 
 
 def _codes(rng, shape):
