@@ -4,10 +4,11 @@
 // 「LLM推理降本五要素」 §2.1 (at decode the layer waits on weight bandwidth).
 //
 // Three kernels:
-//  * decode (M <= 8, token rows fit LDS): the weight stream is the whole
-//    cost.  Whole-line weight units transposed through LDS into MFMA
-//    operands, token rows staged once per workgroup (qg_decode.hpp); the K
-//    loop is split across the waves and the int32 partials meet in LDS.
+//  * decode (M <= 8, and M <= 16 on layers of at most 256 16-row blocks):
+//    the weight stream is the whole cost.  Whole-line weight units transposed
+//    through LDS into MFMA operands, token rows staged in LDS once per
+//    workgroup (or per phase of K when they are too long); the K loop is
+//    split across the waves and the int32 partials meet in LDS.
 //  * wide decode (M <= 64): one 16-row weight block per wave over the whole
 //    K, several blocks per workgroup sharing each phase's token-row panel.
 //  * large M (prefill): 256x256 output tiles, K in 128-byte stages brought
@@ -35,17 +36,19 @@ __device__ __forceinline__ int32_t w8a8_epilogue<int32_t>(int acc, float, float)
 
 // ---------------------------------------------------------------------------
 // Decode kernel (M <= 16) on whole-line weight units (see qg_decode.hpp): a
-// unit is two 64-deep int8 MFMA steps of 16 weight rows.  The token rows are
-// staged whole in LDS first (MR rows, MR >= M, rows past M as zeros); wave w
-// then streams its contiguous run of units in batches of UB, two batches in
-// flight, each unit transposed through the wave's tile and multiplied against
-// the matching token fragments.  The int32 partials of the waves meet in LDS.
+// unit is two 64-deep int8 MFMA steps of 16 weight rows.  The K range is
+// walked in `phases` contiguous runs of units (one unless the token rows are
+// too long for LDS).  Per phase the token rows' slice is staged in LDS (MR
+// rows, MR >= M, rows past M as zeros); wave w then streams its contiguous
+// share of the phase's units in batches of UB, two batches in flight, each
+// unit transposed through the wave's tile and multiplied against the matching
+// token fragments.  The int32 partials of the waves meet in LDS.
 // ---------------------------------------------------------------------------
 template <int MR, int WAVES, int UB, typename OutT>
 __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, const int8_t* __restrict__ wq,
-    const float* __restrict__ ws, int M, int N, int K, OutT* __restrict__ y) {
-  extern __shared__ __attribute__((aligned(16))) int8_t xl[];   // MR rows, pitch stage_pitch(K)
+    const float* __restrict__ ws, int M, int N, int K, OutT* __restrict__ y, int phases) {
+  extern __shared__ __attribute__((aligned(16))) int8_t xl[];   // MR rows of one phase's slice
   __shared__ __attribute__((aligned(16))) int8_t tiles[WAVES][kTileBytes];
   __shared__ v4i red[WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -53,23 +56,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
   const int r = lane & 15, j = lane >> 4;
   const int n_base = blockIdx.x * 16;
   const int units = (K + kUnitBytes - 1) / kUnitBytes;
-  const int ub = (int)((int64_t)units * wave / WAVES), ue = (int)((int64_t)units * (wave + 1) / WAVES);
-  const int pitch = stage_pitch(K);
+  const int pitch = stage_pitch(kUnitBytes * ((units + phases - 1) / phases));
 
   const int rows_n = min(16, N - n_base);
   const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * K, (u32)(rows_n * K));
+  const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
   const UnitLanes ul = unit_lanes(lane, K);
 
-  v4i b0[UB][2], b1[UB][2];
-  auto load = [&](v4i (&b)[UB][2], int q0) {
-#pragma unroll
-    for (int v = 0; v < UB; ++v) unit_load(b[v], wr, ul, q0 + v, q0 + v < ue, K);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // token rows into LDS; the first weight batch is issued behind the first
-  // round of their loads
-  stage_rows<MR, 64 * WAVES>(xl, make_rsrc(xq, (u32)(M * K)), K, [](v4i v) { return v; },
-                             [&]() { load(b0, ub); });
   // epilogue scales, fetched early so the tail of the kernel waits on nothing
   // (int32 output takes no scales, and its scale pointers may be null)
   const int n_out = n_base + r;
@@ -82,33 +75,50 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
       sx[i] = xs[m < M ? m : M - 1];
     }
   }
-  lds_barrier();
 
   // Rows r >= MR, units past this wave's run and fragments past K read valid
-  // LDS (row 0, k 0): their weight operand is zero, and rows >= M are never
-  // stored.
+  // LDS (row 0 of the slice): their weight operand is zero, and rows >= M are
+  // never stored.
   const int8_t* xrow = xl + (r < MR ? r : 0) * pitch;
   int8_t* tile = tiles[wave];
   v4i acc = {0, 0, 0, 0};
-  auto mma = [&](const v4i (&b)[UB][2], int q0) {
+  v4i b0[UB][2], b1[UB][2];
+  for (int p = 0; p < phases; ++p) {
+    const int pu0 = (int)((int64_t)units * p / phases), pu1 = (int)((int64_t)units * (p + 1) / phases);
+    const int ub = pu0 + (int)((int64_t)(pu1 - pu0) * wave / WAVES);
+    const int ue = pu0 + (int)((int64_t)(pu1 - pu0) * (wave + 1) / WAVES);
+    const int col0 = kUnitBytes * pu0, cols = min(kUnitBytes * pu1, K) - col0;
+    auto load = [&](v4i (&b)[UB][2], int q0) {
 #pragma unroll
-    for (int v = 0; v < UB; ++v) {
-      v4i f[2];
-      unit_transpose(tile, b[v], ul, f);
-      const bool qin = q0 + v < ue;
+      for (int v = 0; v < UB; ++v) unit_load(b[v], wr, ul, q0 + v, q0 + v < ue, K);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (p > 0) __syncthreads();   // every wave is done with the previous slice
+    // the slice's token rows into LDS; the phase's first weight batch is
+    // issued behind the first round of their loads
+    stage_slice<MR, 64 * WAVES>(xl, pitch, xr, K, col0, cols, [&]() { load(b0, ub); });
+    lds_barrier();
+
+    auto mma = [&](const v4i (&b)[UB][2], int q0) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int ka = kUnitBytes * (q0 + v) + 64 * s + 16 * j;
-        const v4i a = ld16(xrow + (qin && ka < K ? ka : 0));
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, f[s], acc, 0, 0, 0);
+      for (int v = 0; v < UB; ++v) {
+        v4i f[2];
+        unit_transpose(tile, b[v], ul, f);
+        const bool qin = q0 + v < ue;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int ka = kUnitBytes * (q0 + v) + 64 * s + 16 * j;
+          const v4i a = ld16(xrow + (qin && ka < K ? ka - col0 : 0));
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, f[s], acc, 0, 0, 0);
+        }
       }
+    };
+    for (int q0 = ub; q0 < ue; q0 += 2 * UB) {
+      load(b1, q0 + UB);
+      mma(b0, q0);
+      load(b0, q0 + 2 * UB);
+      mma(b1, q0 + UB);
     }
-  };
-  for (int q0 = ub; q0 < ue; q0 += 2 * UB) {
-    load(b1, q0 + UB);
-    mma(b0, q0);
-    load(b0, q0 + 2 * UB);
-    mma(b1, q0 + UB);
   }
 
   red[wave][lane] = acc;
@@ -539,8 +549,16 @@ static void launch_w8a8_wide(const int8_t* xq, const float* xs, const int8_t* wq
 
 // Token rows longer than kDecLdsMaxBytes (a long K: the down projection of
 // an FFN) still stage whole in LDS up to kDecLdsBigBytes, at one workgroup
-// per compute unit.
+// per compute unit; beyond that the decode kernel walks K in phases, each
+// staging its own slice of the rows.
 constexpr size_t kDecLdsBigBytes = 112 * 1024;
+
+// LDS bytes of the decode kernel's token slice with `phases` phases (the
+// kernel's own pitch: whole units per phase).
+static size_t dec_lds(int mr, int K, int phases) {
+  const int units = (K + kUnitBytes - 1) / kUnitBytes;
+  return (size_t)mr * stage_pitch(kUnitBytes * ((units + phases - 1) / phases));
+}
 
 // Waves per 16-row workgroup of the decode kernel (they split K): more when
 // few 16-row blocks would leave the chip short of loads in flight (measured
@@ -552,15 +570,15 @@ static int dec_waves(int N, size_t lds) {
 
 template <int WAVES, typename OutT>
 static void dec_mr(int mr, const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
-                   int M, int N, int K, OutT* y, size_t lds, hipStream_t st) {
+                   int M, int N, int K, OutT* y, size_t lds, int phases, hipStream_t st) {
   constexpr int UB = 2;
   const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
   switch (mr) {
-    case 1: k_w8a8_dec<1, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-    case 2: k_w8a8_dec<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-    case 4: k_w8a8_dec<4, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-    case 8: k_w8a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-    default: k_w8a8_dec<16, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+    case 1: k_w8a8_dec<1, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
+    case 2: k_w8a8_dec<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
+    case 4: k_w8a8_dec<4, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
+    case 8: k_w8a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
+    default: k_w8a8_dec<16, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
   }
 }
 
@@ -569,16 +587,18 @@ static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* w
                               const float* ws, int M, int N, int K, OutT* y, hipStream_t st) {
   if (M <= 64) {
     const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
-    const size_t lds = (size_t)mr * stage_pitch(K);
     // 9..16 token rows: the decode kernel when N gives at most 256 blocks of
     // 16 weight rows (one workgroup per CU; measured on MI355X: N = 4096
     // 6.4 us against the wide kernel's 8.4, K = 6912 7.9 against 12.5);
     // wider layers keep the wide kernel (N = 11008: 10.9 against 11.3 us)
-    if (M <= 16 && lds <= kDecLdsBigBytes && (M <= 8 || (N + 15) / 16 <= 256)) {
+    if (M <= 8 || (M <= 16 && (N + 15) / 16 <= 256)) {
+      const int units = (K + kUnitBytes - 1) / kUnitBytes;
+      int phases = 1;
+      while (phases < units && dec_lds(mr, K, phases) > kDecLdsBigBytes) ++phases;
+      const size_t lds = dec_lds(mr, K, phases);
       const int waves = dec_waves(N, lds);
-      if (waves >= 16) dec_mr<16, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, st);
-      else if (waves >= 8) dec_mr<8, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, st);
-      else dec_mr<4, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, st);
+      if (waves >= 8) dec_mr<8, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, st);
+      else dec_mr<4, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, st);
     } else if (M <= 16) {
       launch_w8a8_wide<1, OutT>(xq, xs, wq, ws, M, N, K, y, st);
     } else if (M <= 32) {

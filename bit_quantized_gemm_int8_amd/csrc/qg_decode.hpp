@@ -130,6 +130,43 @@ __device__ __forceinline__ void stage_rows(int8_t* dst, rsrc_t src, int row_byte
   }
 }
 
+// Like stage_rows, for a slice of longer rows: bytes col0 .. col0 + row_bytes
+// of each of ROWS rows src_stride bytes apart, into LDS rows of pitch bytes
+// (at least stage_pitch(row_bytes)).  Chunks past the slice are written as
+// zeros into the row's padding; rows past the resource's end are zeros.
+template <int ROWS, int THREADS, typename A>
+__device__ __forceinline__ void stage_slice(int8_t* dst, int pitch, rsrc_t src, int src_stride,
+                                            int col0, int row_bytes, A after) {
+  constexpr int CPR = ROWS <= 4 ? 2 : 1;
+  const int kc = row_bytes >> 4;
+  v4i v[ROWS][CPR];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < CPR; ++i) {
+      const int c = c0 + (int)threadIdx.x + i * THREADS;
+#pragma unroll
+      for (int m = 0; m < ROWS; ++m)
+        v[m][i] = bld16(src, c < kc ? (u32)(m * src_stride + col0 + 16 * c) : kOOB);
+    }
+  };
+  auto store = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < CPR; ++i) {
+      const int c = c0 + (int)threadIdx.x + i * THREADS, cc = c < kc ? c : kc;
+#pragma unroll
+      for (int m = 0; m < ROWS; ++m) st16(dst + m * pitch + 16 * cc, v[m][i]);
+    }
+  };
+  load(0);
+  __builtin_amdgcn_sched_barrier(0);
+  after();
+  store(0);
+  for (int c0 = CPR * THREADS; c0 < kc; c0 += CPR * THREADS) {
+    load(c0);
+    store(c0);
+  }
+}
+
 // Scale and zero point of the weight rows of a workgroup (`rows` rows of G
 // groups, fp16 bits, contiguous in global memory) staged in LDS as words
 // s | z << 16 at pitch G + 1, an odd number of words, so that the 16 rows of

@@ -36,7 +36,10 @@ W8A8_SHAPES = [(16, 512, 512), (1, 16, 16), (3, 17, 48), (8, 11008, 4096), (17, 
                (4, 6144, 1024), (2, 6160, 4096),
                # 9..16 token rows on the decode kernel (N/16 <= 256), at its LDS
                # limit, and just past 256 weight blocks (wide kernel)
-               (16, 4096, 4096), (9, 300, 6912), (13, 4112, 1024)]
+               (16, 4096, 4096), (9, 300, 6912), (13, 4112, 1024),
+               # decode kernel walking K in phases: 2, 3 (K not a multiple of
+               # 128) and 10 token-row slices, and the longest K the API takes
+               (16, 200, 11008), (9, 48, 20016), (16, 64, 65536), (1, 32, 133136)]
 
 
 def _codes(rng, shape):
