@@ -54,7 +54,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
-  const int n_base = blockIdx.x * 16;
+  // this workgroup's 16-row weight blocks [bb0, bb0 + nb) (one unless the
+  // grid is smaller than the block count); block blk gets waves blk,
+  // blk + nb, ..., which split its K
+  const int nblocks = (N + 15) / 16;
+  const int bb0 = (int)((int64_t)nblocks * blockIdx.x / gridDim.x);
+  const int nb = (int)((int64_t)nblocks * (blockIdx.x + 1) / gridDim.x) - bb0;
+  const int blk = wave % nb, sub = wave / nb, subs = (WAVES - blk + nb - 1) / nb;
+  const int n_base = (bb0 + blk) * 16;
   const int units = (K + kUnitBytes - 1) / kUnitBytes;
   const int pitch = stage_pitch(kUnitBytes * ((units + phases - 1) / phases));
 
@@ -85,8 +92,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
   v4i b0[UB][2], b1[UB][2];
   for (int p = 0; p < phases; ++p) {
     const int pu0 = (int)((int64_t)units * p / phases), pu1 = (int)((int64_t)units * (p + 1) / phases);
-    const int ub = pu0 + (int)((int64_t)(pu1 - pu0) * wave / WAVES);
-    const int ue = pu0 + (int)((int64_t)(pu1 - pu0) * (wave + 1) / WAVES);
+    const int ub = pu0 + (int)((int64_t)(pu1 - pu0) * sub / subs);
+    const int ue = pu0 + (int)((int64_t)(pu1 - pu0) * (sub + 1) / subs);
     const int col0 = kUnitBytes * pu0, cols = min(kUnitBytes * pu1, K) - col0;
     auto load = [&](v4i (&b)[UB][2], int q0) {
 #pragma unroll
@@ -123,10 +130,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
 
   red[wave][lane] = acc;
   __syncthreads();
-  if (tid < 64) {
-    v4i sum = red[0][lane];
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+  if (sub == 0) {   // wave blk: its block's partials, in wave order
+    v4i sum = red[blk][lane];
+    for (int sb = 1; sb < subs; ++sb) sum += red[blk + nb * sb][lane];
     if (n_out < N) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -553,6 +559,10 @@ static void launch_w8a8_wide(const int8_t* xq, const float* xs, const int8_t* wq
 // staging its own slice of the rows.
 constexpr size_t kDecLdsBigBytes = 112 * 1024;
 
+// Compute units of an MI355X, and the LDS of one.
+constexpr int kDecCUs = 256;
+constexpr size_t kCuLdsBytes = 160 * 1024;
+
 // LDS bytes of the decode kernel's token slice with `phases` phases (the
 // kernel's own pitch: whole units per phase).
 static size_t dec_lds(int mr, int K, int phases) {
@@ -570,9 +580,10 @@ static int dec_waves(int N, size_t lds) {
 
 template <int WAVES, typename OutT>
 static void dec_mr(int mr, const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
-                   int M, int N, int K, OutT* y, size_t lds, int phases, hipStream_t st) {
+                   int M, int N, int K, OutT* y, size_t lds, int phases, int groups,
+                   hipStream_t st) {
   constexpr int UB = 2;
-  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
+  const dim3 grid((unsigned)groups), block(64 * WAVES);
   switch (mr) {
     case 1: k_w8a8_dec<1, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
     case 2: k_w8a8_dec<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
@@ -596,9 +607,23 @@ static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* w
       int phases = 1;
       while (phases < units && dec_lds(mr, K, phases) > kDecLdsBigBytes) ++phases;
       const size_t lds = dec_lds(mr, K, phases);
-      const int waves = dec_waves(N, lds);
-      if (waves >= 8) dec_mr<8, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, st);
-      else dec_mr<4, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, st);
+      const int nblocks = (N + 15) / 16;
+      // One-block workgroups of 4 waves: how many fit a CU (LDS, and 28
+      // waves at this kernel's register count).
+      const size_t wg_lds = lds + 4 * (kTileBytes + 64 * sizeof(v4i));
+      const int per_cu = (int)std::min<size_t>(7, kCuLdsBytes / wg_lds);
+      if (nblocks > per_cu * kDecCUs && nblocks <= 4 * kDecCUs && lds <= kDecLdsMaxBytes) {
+        // more blocks than one-block workgroups can be resident at once: one
+        // workgroup of 12 waves per CU over 3-4 blocks instead of a second
+        // round of workgroups (measured on MI355X: N = 13824, K = 5120, M = 8
+        // 15.9 us against 18.8; with all one-block workgroups resident they
+        // are faster, e.g. N = 11008: 10.7 against 11.0 us)
+        dec_mr<12, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, kDecCUs, st);
+      } else {
+        const int waves = dec_waves(N, lds);
+        if (waves >= 8) dec_mr<8, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, nblocks, st);
+        else dec_mr<4, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, nblocks, st);
+      }
     } else if (M <= 16) {
       launch_w8a8_wide<1, OutT>(xq, xs, wq, ws, M, N, K, y, st);
     } else if (M <= 32) {

@@ -39,7 +39,10 @@ W8A8_SHAPES = [(16, 512, 512), (1, 16, 16), (3, 17, 48), (8, 11008, 4096), (17, 
                (16, 4096, 4096), (9, 300, 6912), (13, 4112, 1024),
                # decode kernel walking K in phases: 2, 3 (K not a multiple of
                # 128) and 10 token-row slices, and the longest K the API takes
-               (16, 200, 11008), (9, 48, 20016), (16, 64, 65536), (1, 32, 133136)]
+               (16, 200, 11008), (9, 48, 20016), (16, 64, 65536), (1, 32, 133136),
+               # more 16-row blocks than one-block workgroups can be resident:
+               # 12-wave workgroups over 3 or 4 blocks, the last one ragged
+               (5, 13830, 5120), (7, 16384, 4096)]
 
 
 def _codes(rng, shape):
