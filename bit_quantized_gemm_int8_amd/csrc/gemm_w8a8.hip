@@ -44,10 +44,13 @@ __device__ __forceinline__ int32_t w8a8_epilogue<int32_t>(int acc, float, float)
 // unit transposed through the wave's tile and multiplied against the matching
 // token fragments.  The int32 partials of the waves meet in LDS.
 // ---------------------------------------------------------------------------
-template <int MR, int WAVES, int UB, typename OutT>
+// GEN = false compiles the common case (one block per workgroup, one phase)
+// with those counts as constants: the general form measured ~1 us slower on
+// the 45 MB FFN-up stream.
+template <int MR, int WAVES, int UB, bool GEN, typename OutT>
 __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, const int8_t* __restrict__ wq,
-    const float* __restrict__ ws, int M, int N, int K, OutT* __restrict__ y, int phases) {
+    const float* __restrict__ ws, int M, int N, int K, OutT* __restrict__ y, int phases_arg) {
   extern __shared__ __attribute__((aligned(16))) int8_t xl[];   // MR rows of one phase's slice
   __shared__ __attribute__((aligned(16))) int8_t tiles[WAVES][kTileBytes];
   __shared__ v4i red[WAVES][64];
@@ -58,9 +61,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
   // grid is smaller than the block count); block blk gets waves blk,
   // blk + nb, ..., which split its K
   const int nblocks = (N + 15) / 16;
-  const int bb0 = (int)((int64_t)nblocks * blockIdx.x / gridDim.x);
-  const int nb = (int)((int64_t)nblocks * (blockIdx.x + 1) / gridDim.x) - bb0;
-  const int blk = wave % nb, sub = wave / nb, subs = (WAVES - blk + nb - 1) / nb;
+  const int bb0 = GEN ? (int)((int64_t)nblocks * blockIdx.x / gridDim.x) : (int)blockIdx.x;
+  const int nb = GEN ? (int)((int64_t)nblocks * (blockIdx.x + 1) / gridDim.x) - bb0 : 1;
+  const int blk = GEN ? wave % nb : 0, sub = GEN ? wave / nb : wave;
+  const int subs = GEN ? (WAVES - blk + nb - 1) / nb : WAVES;
+  const int phases = GEN ? phases_arg : 1;
   const int n_base = (bb0 + blk) * 16;
   const int units = (K + kUnitBytes - 1) / kUnitBytes;
   const int pitch = stage_pitch(kUnitBytes * ((units + phases - 1) / phases));
@@ -70,18 +75,22 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
   const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
   const UnitLanes ul = unit_lanes(lane, K);
 
-  // epilogue scales, fetched early so the tail of the kernel waits on nothing
-  // (int32 output takes no scales, and its scale pointers may be null)
+  // epilogue scales, fetched behind the first phase's staging and weight
+  // loads (vector loads complete in issue order: fetched first, they would
+  // delay the staging) and long before the tail needs them; int32 output
+  // takes no scales, and its scale pointers may be null
   const int n_out = n_base + r;
   float sw = 0.f, sx[4] = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (!std::is_same<OutT, int32_t>::value) {
-    sw = ws[n_out < N ? n_out : N - 1];
+  auto fetch_scales = [&]() {
+    if constexpr (!std::is_same<OutT, int32_t>::value) {
+      sw = ws[n_out < N ? n_out : N - 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * j + i;
-      sx[i] = xs[m < M ? m : M - 1];
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * j + i;
+        sx[i] = xs[m < M ? m : M - 1];
+      }
     }
-  }
+  };
 
   // Rows r >= MR, units past this wave's run and fragments past K read valid
   // LDS (row 0 of the slice): their weight operand is zero, and rows >= M are
@@ -104,6 +113,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
     // the slice's token rows into LDS; the phase's first weight batch is
     // issued behind the first round of their loads
     stage_slice<MR, 64 * WAVES>(xl, pitch, xr, K, col0, cols, [&]() { load(b0, ub); });
+    if (p == 0) fetch_scales();
     lds_barrier();
 
     auto mma = [&](const v4i (&b)[UB][2], int q0) {
@@ -573,23 +583,23 @@ static size_t dec_lds(int mr, int K, int phases) {
 // Waves per 16-row workgroup of the decode kernel (they split K): more when
 // few 16-row blocks would leave the chip short of loads in flight (measured
 // on MI355X: K = 11008, N = 4096 and K = 4096, N = 11008; 16 waves is slower).
-static int dec_waves(int N, size_t lds) {
+static int dec_waves(int N, int K, size_t lds) {
   if (lds > kDecLdsMaxBytes) return 8;
-  return (N + 15) / 16 <= 384 ? 8 : 4;
+  return (N + 15) / 16 <= 384 && K >= 4096 ? 8 : 4;
 }
 
-template <int WAVES, typename OutT>
+template <int WAVES, bool GEN, typename OutT>
 static void dec_mr(int mr, const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
                    int M, int N, int K, OutT* y, size_t lds, int phases, int groups,
                    hipStream_t st) {
   constexpr int UB = 2;
   const dim3 grid((unsigned)groups), block(64 * WAVES);
   switch (mr) {
-    case 1: k_w8a8_dec<1, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
-    case 2: k_w8a8_dec<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
-    case 4: k_w8a8_dec<4, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
-    case 8: k_w8a8_dec<8, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
-    default: k_w8a8_dec<16, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
+    case 1: k_w8a8_dec<1, WAVES, UB, GEN, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
+    case 2: k_w8a8_dec<2, WAVES, UB, GEN, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
+    case 4: k_w8a8_dec<4, WAVES, UB, GEN, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
+    case 8: k_w8a8_dec<8, WAVES, UB, GEN, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
+    default: k_w8a8_dec<16, WAVES, UB, GEN, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, M, N, K, y, phases); break;
   }
 }
 
@@ -599,10 +609,12 @@ static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* w
   if (M <= 64) {
     const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
     // 9..16 token rows: the decode kernel when N gives at most 256 blocks of
-    // 16 weight rows (one workgroup per CU; measured on MI355X: N = 4096
-    // 6.4 us against the wide kernel's 8.4, K = 6912 7.9 against 12.5);
-    // wider layers keep the wide kernel (N = 11008: 10.9 against 11.3 us)
-    if (M <= 8 || (M <= 16 && (N + 15) / 16 <= 256)) {
+    // 16 weight rows (one workgroup per CU) and K is long enough to share
+    // out (measured on MI355X: N = 4096 6.4 us against the wide kernel's
+    // 8.4, K = 6912 7.9 against 12.5); wider layers (N = 11008: 10.9 against
+    // 11.3 us) and short K (K = N = 512: 4.1 against 6.3 us) keep the wide
+    // kernel
+    if (M <= 8 || (M <= 16 && (N + 15) / 16 <= 256 && K >= 2048)) {
       const int units = (K + kUnitBytes - 1) / kUnitBytes;
       int phases = 1;
       while (phases < units && dec_lds(mr, K, phases) > kDecLdsBigBytes) ++phases;
@@ -618,11 +630,16 @@ static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* w
         // round of workgroups (measured on MI355X: N = 13824, K = 5120, M = 8
         // 15.9 us against 18.8; with all one-block workgroups resident they
         // are faster, e.g. N = 11008: 10.7 against 11.0 us)
-        dec_mr<12, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, kDecCUs, st);
+        dec_mr<12, true, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, kDecCUs, st);
       } else {
-        const int waves = dec_waves(N, lds);
-        if (waves >= 8) dec_mr<8, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, nblocks, st);
-        else dec_mr<4, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, nblocks, st);
+        const int waves = dec_waves(N, K, lds);
+        if (phases > 1) {
+          if (waves >= 8) dec_mr<8, true, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, nblocks, st);
+          else dec_mr<4, true, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, phases, nblocks, st);
+        } else {
+          if (waves >= 8) dec_mr<8, false, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, 1, nblocks, st);
+          else dec_mr<4, false, OutT>(mr, xq, xs, wq, ws, M, N, K, y, lds, 1, nblocks, st);
+        }
       }
     } else if (M <= 16) {
       launch_w8a8_wide<1, OutT>(xq, xs, wq, ws, M, N, K, y, st);
