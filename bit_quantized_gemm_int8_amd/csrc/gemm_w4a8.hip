@@ -412,6 +412,153 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode kernel for 16 < M <= 16 MT token rows: as k_w4a8_dec (whole-line
+// units, scales and zero points staged in LDS, waves splitting K), but each
+// group's codes are unpacked once and multiplied against MT tiles of 16
+// token rows, so the weights stream once for all of them.  The token
+// fragments of every tile come straight from L2 with the unit they belong to.
+// ---------------------------------------------------------------------------
+template <int MT, int UB>
+struct W4A8MtBatch {
+  v4i w[UB][2], xa[UB][2][MT][2];   // unit v: weight loads; group s, tile t, MFMA h fragment
+};
+
+template <int MT, int WAVES, int UB, typename OutT>
+__global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec_mt(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, const int32_t* __restrict__ wq,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
+    OutT* __restrict__ y) {
+  constexpr bool kI32 = __is_same(OutT, int32_t);
+  constexpr int kThreads = 64 * WAVES;
+  extern __shared__ __attribute__((aligned(16))) u32 szl[];   // 16 x sz_pitch(G) words
+  __shared__ __attribute__((aligned(16))) int8_t tiles[WAVES][kTileBytes];
+  __shared__ v4f red[kI32 ? 1 : WAVES][MT][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int n_base = blockIdx.x * 16;
+  const int G = K >> 7, Kw = K >> 3, RB = Kw * 4;
+  const int units = (RB + kUnitBytes - 1) / kUnitBytes;
+  const int ub = (int)((int64_t)units * wave / WAVES), ue = (int)((int64_t)units * (wave + 1) / WAVES);
+
+  const int rows_n = min(16, N - n_base);
+  const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * Kw, (u32)(rows_n * RB));
+  const UnitLanes ul = unit_lanes(lane, RB);
+  // token row 16 t + r of tile t (rows past M lie past the resource's end:
+  // zeros), k = 32j + 16h of the group
+  const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
+  u32 xoff[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) xoff[t] = (u32)((16 * t + r) * K + 32 * j);
+
+  using Batch = W4A8MtBatch<MT, UB>;
+  auto load = [&](Batch& bt, int q0) {
+#pragma unroll
+    for (int v = 0; v < UB; ++v) {
+      const int q = q0 + v;
+      unit_load(bt.w[v], wr, ul, q, q < ue, RB);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int g = 2 * q + s;
+        const bool gin = q < ue && g < G;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            bt.xa[v][s][t][h] = bld16(xr, gin ? xoff[t] + 128 * g + 16 * h : kOOB);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  Batch b0, b1;
+  ScaleZeroStage<kThreads, 4> sz;
+  const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  sz.load(sr, zr, 16 * G, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(b0, ub);
+  sz.finish(sr, zr, szl, G, 16 * G);
+  lds_barrier();
+
+  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  const u32* szrow = szl + r * sz_pitch(G);
+  int8_t* tile = tiles[wave];
+  v4f yacc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) yacc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const Batch& bt, int q0) {
+#pragma unroll
+    for (int v = 0; v < UB; ++v) {
+      v4i f[2];
+      unit_transpose(tile, bt.w[v], ul, f);
+      const int q = q0 + v;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        // groups past this wave's run or past G: zero codes, zero point and scale
+        const int g = 2 * q + s;
+        const bool gin = q < ue && g < G;
+        const u32 szw = gin ? szrow[g] : 0u;
+        const int z = (int)f16_bits_to_f32((uint16_t)(szw >> 16));
+        const float sc = f16_bits_to_f32((uint16_t)(szw & 0xFFFFu));
+        const v4i w0 = unpack_u4_pair((u32)f[s][0], (u32)f[s][1]);
+        const v4i w1 = unpack_u4_pair((u32)f[s][2], (u32)f[s][3]);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const v4i a0 = shuffle_act16(bt.xa[v][s][t][0]), a1 = shuffle_act16(bt.xa[v][s][t][1]);
+          v4i rs = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+          rs = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, ones, rs, 0, 0, 0);
+          // |z| <= 15 and |token sum| <= 128 * 127: the 24-bit multiply is exact
+          v4i acc;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = __mul24(-z, rs[i]);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, w0, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, w1, acc, 0, 0, 0);
+          if constexpr (kI32) {
+            const int n = n_base + r;
+            if (gin && n < N) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int m = 16 * t + 4 * j + i;
+                if (m < M) y[((int64_t)m * G + g) * N + n] = acc[i];
+              }
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yacc[t][i] = __builtin_fmaf(sc, (float)acc[i], yacc[t][i]);
+          }
+        }
+      }
+    }
+  };
+  for (int q0 = ub; q0 < ue; q0 += 2 * UB) {
+    load(b1, q0 + UB);
+    mma(b0, q0);
+    load(b0, q0 + 2 * UB);
+    mma(b1, q0 + UB);
+  }
+
+  if constexpr (!kI32) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[wave][t][lane] = yacc[t];
+    __syncthreads();
+    for (int it = tid; it < MT * 64; it += kThreads) {
+      const int l = it & 63, t = it >> 6;
+      v4f sum = red[0][t][l];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) sum += red[w][t][l];
+      const int n = n_base + (l & 15);
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * t + 4 * (l >> 4) + i;
+        if (m < M) store_out<OutT>(y, (int64_t)m * N + n, sum[i] * xs[m]);
+      }
+    }
+  }
+}
+
 template <typename OutT>
 static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* wq,
                               const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
@@ -428,6 +575,16 @@ static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* 
       case 8: k_w4a8_dec<8, WAVES, UB, false, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, nullptr, nullptr, M, N, K, y); break;
       default: k_w4a8_dec<16, WAVES, UB, false, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, nullptr, nullptr, M, N, K, y); break;
     }
+    return hipGetLastError();
+  }
+  if (M <= 64 && lds <= kDecLdsMaxBytes) {
+    // 17..64 token rows: one weight stream for 2 or 4 tiles of 16 rows
+    constexpr int WAVES = 8, UB = 1;
+    const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
+    if (M <= 32)
+      k_w4a8_dec_mt<2, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y);
+    else
+      k_w4a8_dec_mt<4, WAVES, UB, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y);
     return hipGetLastError();
   }
   constexpr int MT = 1, NT = 1, WAVES = 8, U = 2;  // measured on MI355X

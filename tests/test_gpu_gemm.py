@@ -125,7 +125,10 @@ def _w4_devs(packed, sc, zz):
 
 
 W4_SHAPES = [(16, 4096, 11008), (1, 16, 128), (5, 17, 256), (16, 300, 1024), (17, 64, 384),
-             (33, 40, 640), (1, 12288, 4096), (3, 100, 2048), (2, 48, 14336)]
+             (33, 40, 640), (1, 12288, 4096), (3, 100, 2048), (2, 48, 14336),
+             # 17..64 token rows on 2 or 4 tiles of one weight stream: partial
+             # last tiles, an odd group count, the full FFN-down shape
+             (32, 4096, 11008), (64, 40, 256), (48, 300, 640), (20, 16, 128), (57, 33, 1152)]
 
 
 @pytest.mark.parametrize("M,N,K", W4_SHAPES)
@@ -148,7 +151,8 @@ def _w4a8_floor(xq, sx, packed, sc, zz):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f32", "f16"])
-@pytest.mark.parametrize("M,N,K", [(16, 4096, 11008), (5, 17, 256), (33, 40, 640), (2, 48, 14336)])
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 11008), (5, 17, 256), (33, 40, 640), (2, 48, 14336),
+                                   (64, 300, 1024)])
 def test_w4a8_scaled(fmt, M, N, K):
     rng = np.random.default_rng(M + 3 * N + K)
     packed, sc, zz = _u4_weights(rng, K, N)
