@@ -18,6 +18,8 @@
 #include "qg_device.hpp"
 #include "qg_launch.hpp"
 
+#include <algorithm>
+
 namespace qg {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -225,23 +227,31 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16(
 // flight.  Rows r >= MR of the MFMA read token row 0 (never stored): with one
 // token row every lane reads the same bytes, an LDS broadcast.
 // ---------------------------------------------------------------------------
-template <int MR, int WAVES, int UB, int XDT, typename OutT>
+// GEN = true: the workgroup owns the 16-row blocks [bb0, bb0 + nb) given by
+// its share of the grid (block blk gets waves blk, blk + nb, ..., which split
+// its K); GEN = false compiles the one-block case with constant counts.
+template <int MR, int WAVES, int UB, int XDT, bool GEN, typename OutT>
 __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ wq,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
     OutT* __restrict__ y) {
   constexpr int kThreads = 64 * WAVES;
-  // LDS: MR token rows (pitch stage_pitch(2K)), then 16 x sz_pitch(G) words
+  // LDS: MR token rows (pitch stage_pitch(2K)), then 16 nb x sz_pitch(G) words
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
   __shared__ __attribute__((aligned(16))) int8_t tiles[WAVES][kTileBytes];
   __shared__ v4f red[WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
-  const int n_base = blockIdx.x * 16;
+  const int nblocks = (N + 15) / 16;
+  const int bb0 = GEN ? (int)((int64_t)nblocks * blockIdx.x / gridDim.x) : (int)blockIdx.x;
+  const int nb = GEN ? (int)((int64_t)nblocks * (blockIdx.x + 1) / gridDim.x) - bb0 : 1;
+  const int blk = GEN ? wave % nb : 0, sub = GEN ? wave / nb : wave;
+  const int subs = GEN ? (WAVES - blk + nb - 1) / nb : WAVES;
+  const int n_base = (bb0 + blk) * 16;
   const int G = K >> 7, Kw = K >> 3, RB = Kw * 4;   // RB: packed bytes per weight row
   const int units = (RB + kUnitBytes - 1) / kUnitBytes;
-  const int ub = (int)((int64_t)units * wave / WAVES), ue = (int)((int64_t)units * (wave + 1) / WAVES);
+  const int ub = (int)((int64_t)units * sub / subs), ue = (int)((int64_t)units * (sub + 1) / subs);
   const int xpitch = stage_pitch(2 * K);
   int8_t* xl = smem;
   u32* szl = reinterpret_cast<u32*>(smem + MR * xpitch);
@@ -258,17 +268,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
   };
   // scales and zero points, token rows, and behind them the first weight batch
   ScaleZeroStage<kThreads, 4> sz;
-  const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
-  const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
-  sz.load(sr, zr, 16 * G, 0);
+  const int srows = min(16 * nb, N - 16 * bb0);   // the workgroup's weight rows
+  const rsrc_t sr = make_rsrc(wscale + (int64_t)16 * bb0 * G, (u32)(srows * G * 2));
+  const rsrc_t zr = make_rsrc(wzero + (int64_t)16 * bb0 * G, (u32)(srows * G * 2));
+  sz.load(sr, zr, 16 * nb * G, 0);
   stage_rows<MR, kThreads>(xl, make_rsrc(x, (u32)(M * K * 2)), 2 * K,
                            [](v4i v) { return shuffle_halves(v); },
                            [&]() { load(b0, ub); });
-  sz.finish(sr, zr, szl, G, 16 * G);
+  sz.finish(sr, zr, szl, G, 16 * nb * G);
   lds_barrier();
 
   const int8_t* xrow = xl + (r < MR ? r : 0) * xpitch + 64 * j;
-  const u32* szrow = szl + r * sz_pitch(G);
+  const u32* szrow = szl + (16 * blk + r) * sz_pitch(G);
   int8_t* tile = tiles[wave];
   v4f yacc = {0.f, 0.f, 0.f, 0.f};
   auto mma = [&](const v4i (&b)[UB][2], int q0) {
@@ -322,10 +333,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
 
   red[wave][lane] = yacc;
   __syncthreads();
-  if (tid < 64) {
-    v4f sum = red[0][lane];
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+  if (sub == 0) {   // wave blk: its block's partials, in wave order
+    v4f sum = red[blk][lane];
+    for (int sb = 1; sb < subs; ++sb) sum += red[blk + nb * sb][lane];
     const int n = n_base + r;
     if (n < N) {
 #pragma unroll
@@ -492,19 +502,23 @@ static void launch_w4a16_wide(const uint16_t* x, const int32_t* wq, const uint16
   }
 }
 
-template <int WAVES, int XDT, typename OutT>
+template <int WAVES, bool GEN, int XDT, typename OutT>
 static void dec_w4a16_mr(int mr, const uint16_t* x, const int32_t* wq, const uint16_t* ws,
-                         const uint16_t* wz, int M, int N, int K, OutT* y, size_t lds,
+                         const uint16_t* wz, int M, int N, int K, OutT* y, size_t lds, int groups,
                          hipStream_t st) {
   constexpr int UB = 1;  // measured on MI355X
-  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
+  const dim3 grid((unsigned)groups), block(64 * WAVES);
   switch (mr) {
-    case 1: k_w4a16_dec<1, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-    case 2: k_w4a16_dec<2, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-    case 4: k_w4a16_dec<4, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-    default: k_w4a16_dec<8, WAVES, UB, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    case 1: k_w4a16_dec<1, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    case 2: k_w4a16_dec<2, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    case 4: k_w4a16_dec<4, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    default: k_w4a16_dec<8, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
   }
 }
+
+// Compute units of an MI355X, and the LDS of one.
+constexpr int kW16CUs = 256;
+constexpr size_t kW16CuLdsBytes = 160 * 1024;
 
 template <int XDT, typename OutT>
 static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
@@ -513,11 +527,24 @@ static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint1
   const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
   const size_t lds = (size_t)mr * stage_pitch(2 * K) + (size_t)16 * sz_pitch(G) * 4;
   if (M <= 8 && lds <= kDecLdsMaxBytes) {
-    // 8 waves split K when few 16-row blocks would leave the chip short of
-    // loads in flight (measured on MI355X: K = 11008, N = 4096 takes 8.6 us
-    // with 8 waves, 10.4 us with 4; N >= 11008 is best with 4)
-    if ((N + 15) / 16 <= 384) dec_w4a16_mr<8, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds, st);
-    else dec_w4a16_mr<4, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds, st);
+    const int nblocks = (N + 15) / 16;
+    // one-block workgroups of 4 waves that fit a CU (LDS; at most 7 by registers)
+    const size_t wg_lds = lds + 4 * (kTileBytes + 64 * sizeof(v4f));
+    const int per_cu = (int)std::min<size_t>(7, kW16CuLdsBytes / wg_lds);
+    const size_t lds_multi = (size_t)mr * stage_pitch(2 * K) + (size_t)64 * sz_pitch(G) * 4;
+    if (nblocks > per_cu * kW16CUs && nblocks <= 4 * kW16CUs && lds_multi <= kDecLdsMaxBytes) {
+      // more blocks than one-block workgroups can be resident at once: one
+      // workgroup of 12 waves per CU over 3-4 blocks, the token rows staged
+      // once (measured on MI355X: M = 8, K = 4096, N = 12288)
+      dec_w4a16_mr<12, true, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds_multi, kW16CUs, st);
+    } else if (nblocks <= 384) {
+      // 8 waves split K when few 16-row blocks would leave the chip short of
+      // loads in flight (measured on MI355X: K = 11008, N = 4096 takes 8.6 us
+      // with 8 waves, 10.4 us with 4; N >= 11008 is best with 4)
+      dec_w4a16_mr<8, false, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds, nblocks, st);
+    } else {
+      dec_w4a16_mr<4, false, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds, nblocks, st);
+    }
     return hipGetLastError();
   }
   const size_t lds_wide = (size_t)16 * wide_waves(N) * sz_pitch(G) * 4;

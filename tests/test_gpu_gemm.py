@@ -180,7 +180,10 @@ def _w4a16_floor(x64, packed, sc, zz):
 @pytest.mark.parametrize("xfmt", ["f16", "bf16"])
 @pytest.mark.parametrize("fmt", ["f16", "f32", "bf16"])
 @pytest.mark.parametrize("M,N,K", [(1, 12288, 4096), (5, 17, 256), (16, 300, 1024), (33, 40, 640),
-                                   (2, 48, 14336), (48, 10256, 512), (64, 512, 4096)])
+                                   (2, 48, 14336), (48, 10256, 512), (64, 512, 4096),
+                                   # 12-wave workgroups over 3 and 4 weight blocks
+                                   # (more blocks than 2 per CU), the last ragged
+                                   (8, 12288, 4096), (6, 11000, 4096), (7, 16384, 4096)])
 def test_w4a16(xfmt, fmt, M, N, K):
     rng = np.random.default_rng(M * 5 + N + K)
     packed, sc, zz = _u4_weights(rng, K, N)
