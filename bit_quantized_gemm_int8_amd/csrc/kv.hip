@@ -82,6 +82,10 @@ struct KvQuant {
   int8_t* q;
   float* scale;
   int T, H, D, S, n, cpw, nsplit, rp, cc, r0;
+  // exact division by nsplit and by H for quotients below 2^31:
+  // n / d = (n * mag) >> (31 + sh), mag = ceil(2^(31 + sh) / d), sh = ceil(log2 d)
+  u32 smag, hmag;
+  int ssh, hsh;
   int64_t row;      // elements per position (H * D)
   // per pass: byte offset of the thread's chunk from the slice's first
   // element, for the cache (xo) and the codes (qo); kOOB for threads that
@@ -102,8 +106,8 @@ struct KvQuant {
 
   __device__ __forceinline__ KvItem item(int it) const {
     KvItem w;
-    const int split = it % nsplit, sh = it / nsplit;
-    const int h = sh % H, seg = sh / H;
+    const int sh = (int)(((uint64_t)(u32)it * smag) >> (31 + ssh)), split = it - sh * nsplit;
+    const int seg = (int)(((uint64_t)(u32)sh * hmag) >> (31 + hsh)), h = sh - seg * H;
     const int c0 = 8 * cpw * split, t0 = seg * kKvSeg;
     const int tn = it < n ? min(kKvSeg, T - t0) : 0;
     const int64_t base = ((int64_t)t0 * H + h) * D + c0;
@@ -183,7 +187,8 @@ template <int DT, int KC>
 __global__ __launch_bounds__(kKvThreads) void k_kv_quant_seg(const void* __restrict__ kv, int T,
                                                              int H, int D, int cpw,
                                                              int8_t* __restrict__ q,
-                                                             float* __restrict__ scale) {
+                                                             float* __restrict__ scale,
+                                                             u32 smag, int ssh, u32 hmag, int hsh) {
   __shared__ float part[kKvThreads * 8];   // [RP][8 * CPW] partial maxima (<= 2048)
   __shared__ __align__(16) float chs[kKvMaxD];   // per-channel scale of the slice
   __shared__ __align__(16) float chr[kKvMaxD];   // and its reciprocal
@@ -197,6 +202,10 @@ __global__ __launch_bounds__(kKvThreads) void k_kv_quant_seg(const void* __restr
   k.S = (T + kKvSeg - 1) / kKvSeg;
   k.cpw = cpw;
   k.nsplit = (D >> 3) / cpw;
+  k.smag = smag;
+  k.ssh = ssh;
+  k.hmag = hmag;
+  k.hsh = hsh;
   k.n = k.S * H * k.nsplit;
   k.rp = kKvThreads / cpw;
   k.cc = (int)threadIdx.x % cpw;
@@ -286,11 +295,18 @@ static hipError_t kv_quant_dt(const void* kv, int T, int H, int D, int8_t* q, fl
   const unsigned grid = (unsigned)std::min<int64_t>((items + 1) / 2, kKvMaxWgs);
   // passes over the segment: ceil(128 / RP), taken up to a power of two
   const int rp = kKvThreads / cpw, need = (kKvSeg + rp - 1) / rp;
-  if (need <= 1) k_kv_quant_seg<DT, 1><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s);
-  else if (need <= 2) k_kv_quant_seg<DT, 2><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s);
-  else if (need <= 4) k_kv_quant_seg<DT, 4><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s);
-  else if (need <= 8) k_kv_quant_seg<DT, 8><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s);
-  else k_kv_quant_seg<DT, 16><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s);
+  auto magic = [](int d, int& sh) {
+    sh = 0;
+    while ((1LL << sh) < d) ++sh;
+    return (u32)((((uint64_t)1 << (31 + sh)) + (uint64_t)d - 1) / (uint64_t)d);
+  };
+  int ssh, hsh;
+  const u32 smag = magic(cpr / cpw, ssh), hmag = magic(H, hsh);
+  if (need <= 1) k_kv_quant_seg<DT, 1><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s, smag, ssh, hmag, hsh);
+  else if (need <= 2) k_kv_quant_seg<DT, 2><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s, smag, ssh, hmag, hsh);
+  else if (need <= 4) k_kv_quant_seg<DT, 4><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s, smag, ssh, hmag, hsh);
+  else if (need <= 8) k_kv_quant_seg<DT, 8><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s, smag, ssh, hmag, hsh);
+  else k_kv_quant_seg<DT, 16><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s, smag, ssh, hmag, hsh);
   return hipGetLastError();
 }
 

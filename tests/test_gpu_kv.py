@@ -53,6 +53,9 @@ CASES = [
     (257, 2, 64, "bf16"), (200, 2, 256, "bf16"), (131, 3, 16, "f32"), (140, 2, 32, "f16"),
     (200, 2, 96, "bf16"), (150, 3, 80, "f32"), (260, 1, 112, "f16"), (384, 5, 240, "bf16"),
     (127, 7, 48, "bf16"),
+    # three 64-channel slices per head (D = 192) and a head count that is not
+    # a power of two: the work-item index is divided by both
+    (300, 3, 192, "bf16"), (129, 5, 192, "f16"), (130, 40, 128, "bf16"),
 ]
 
 
