@@ -258,17 +258,32 @@ __device__ __forceinline__ void kv_store8(OutT* p, const float (&x)[8]) {
 
 // x_hat = code * s: the binary32 product (rounded once), then rounded to the
 // output type; one thread per 8 channels of one (position, head),
-// grid-stride.
-template <typename OutT>
+// grid-stride.  FAST (fewer than 2^31 chunks): the chunk index is split into
+// (position, head, channel chunk) by multiply-high divisions.
+template <typename OutT, bool FAST>
 __global__ __launch_bounds__(256) void k_kv_dequant_seg(const int8_t* __restrict__ q,
                                                         const float* __restrict__ scale, int T,
-                                                        int H, int D, OutT* __restrict__ out) {
+                                                        int H, int D, OutT* __restrict__ out,
+                                                        u32 cmag, int csh, u32 hmag, int hsh) {
   const int S = (T + kKvSeg - 1) / kKvSeg, cpr = D >> 3;
   const int64_t n8 = (int64_t)T * H * cpr;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
-    const int64_t th = i / cpr;
-    const int cc = (int)(i - th * cpr);
-    const int t = (int)(th / H), hh = (int)(th - (int64_t)t * H);
+    int64_t th;
+    int cc, t, hh;
+    if constexpr (FAST) {
+      // n8 < 2^31: exact multiply-high divisions by cpr and H
+      const u32 iu = (u32)i;
+      const u32 thu = (u32)(((uint64_t)iu * cmag) >> (31 + csh));
+      cc = (int)(iu - thu * (u32)cpr);
+      t = (int)(((uint64_t)thu * hmag) >> (31 + hsh));
+      hh = (int)thu - t * H;
+      th = thu;
+    } else {
+      th = i / cpr;
+      cc = (int)(i - th * cpr);
+      t = (int)(th / H);
+      hh = (int)(th - (int64_t)t * H);
+    }
     const uint2 c = *reinterpret_cast<const uint2*>(q + 8 * i);
     const float* sp = scale + ((int64_t)hh * S + t / kKvSeg) * D + 8 * cc;
     const v4i s0 = ld16(sp), s1 = ld16(sp + 4);
@@ -283,6 +298,15 @@ __global__ __launch_bounds__(256) void k_kv_dequant_seg(const int8_t* __restrict
   }
 }
 
+// Exact division of n < 2^31 by d >= 1 as a multiply-high: n / d =
+// (n * mag) >> (31 + sh) with sh = ceil(log2 d), mag = ceil(2^(31 + sh) / d)
+// (mag * d - 2^(31 + sh) < d, so the error term stays below 1 / d).
+static u32 kv_magic(int d, int& sh) {
+  sh = 0;
+  while ((1LL << sh) < d) ++sh;
+  return (u32)((((uint64_t)1 << (31 + sh)) + (uint64_t)d - 1) / (uint64_t)d);
+}
+
 // Workgroups of the quantizer: about two items per workgroup, at most
 // kKvMaxWgs (an even split over the 256 CUs).
 constexpr int kKvMaxWgs = 1024;
@@ -295,13 +319,8 @@ static hipError_t kv_quant_dt(const void* kv, int T, int H, int D, int8_t* q, fl
   const unsigned grid = (unsigned)std::min<int64_t>((items + 1) / 2, kKvMaxWgs);
   // passes over the segment: ceil(128 / RP), taken up to a power of two
   const int rp = kKvThreads / cpw, need = (kKvSeg + rp - 1) / rp;
-  auto magic = [](int d, int& sh) {
-    sh = 0;
-    while ((1LL << sh) < d) ++sh;
-    return (u32)((((uint64_t)1 << (31 + sh)) + (uint64_t)d - 1) / (uint64_t)d);
-  };
   int ssh, hsh;
-  const u32 smag = magic(cpr / cpw, ssh), hmag = magic(H, hsh);
+  const u32 smag = kv_magic(cpr / cpw, ssh), hmag = kv_magic(H, hsh);
   if (need <= 1) k_kv_quant_seg<DT, 1><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s, smag, ssh, hmag, hsh);
   else if (need <= 2) k_kv_quant_seg<DT, 2><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s, smag, ssh, hmag, hsh);
   else if (need <= 4) k_kv_quant_seg<DT, 4><<<grid, kKvThreads, 0, st>>>(kv, T, H, D, cpw, q, s, smag, ssh, hmag, hsh);
@@ -320,15 +339,26 @@ hipError_t launch_kv_quant_seg(const void* kv, int kv_dtype, int64_t T, int64_t 
   }
 }
 
+template <typename OutT>
+static void kv_dequant_t(const int8_t* kv_q, const float* kv_scale, int T, int H, int D, OutT* out,
+                         int64_t n8, hipStream_t st) {
+  const unsigned grid = (unsigned)std::min<int64_t>((n8 + 255) / 256, 65536);
+  int csh, hsh;
+  const u32 cmag = kv_magic(D / 8, csh), hmag = kv_magic(H, hsh);
+  if (n8 < ((int64_t)1 << 31))   // 32-bit chunk indices: multiply-high divisions
+    k_kv_dequant_seg<OutT, true><<<grid, 256, 0, st>>>(kv_q, kv_scale, T, H, D, out, cmag, csh, hmag, hsh);
+  else
+    k_kv_dequant_seg<OutT, false><<<grid, 256, 0, st>>>(kv_q, kv_scale, T, H, D, out, cmag, csh, hmag, hsh);
+}
+
 hipError_t launch_kv_dequant_seg(const int8_t* kv_q, const float* kv_scale, int64_t T, int64_t H,
                                  int64_t D, void* out, int out_dtype, hipStream_t st) {
   const int64_t n8 = T * H * (D / 8);
-  const unsigned grid = (unsigned)std::min<int64_t>((n8 + 255) / 256, 65536);
   const int t = (int)T, h = (int)H, d = (int)D;
   switch (out_dtype) {
-    case F32: k_kv_dequant_seg<float><<<grid, 256, 0, st>>>(kv_q, kv_scale, t, h, d, (float*)out); break;
-    case F16: k_kv_dequant_seg<_Float16><<<grid, 256, 0, st>>>(kv_q, kv_scale, t, h, d, (_Float16*)out); break;
-    default: k_kv_dequant_seg<uint16_t><<<grid, 256, 0, st>>>(kv_q, kv_scale, t, h, d, (uint16_t*)out); break;
+    case F32: kv_dequant_t<float>(kv_q, kv_scale, t, h, d, (float*)out, n8, st); break;
+    case F16: kv_dequant_t<_Float16>(kv_q, kv_scale, t, h, d, (_Float16*)out, n8, st); break;
+    default: kv_dequant_t<uint16_t>(kv_q, kv_scale, t, h, d, (uint16_t*)out, n8, st); break;
   }
   return hipGetLastError();
 }
