@@ -559,11 +559,146 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec_mt(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode kernel for wide layers (M <= 16, N / 32 >= 256): each wave streams
+// two 16-row weight blocks over its run of K, so one token fragment -- and
+// one token-sum MFMA -- serves both blocks' codes: half the token traffic
+// and a third fewer MFMAs per weight byte, at half as many workgroups.
+// Otherwise as k_w4a8_dec (scales and zero points of the 32 rows staged in
+// LDS, whole-line units transposed through the wave's tile).
+// ---------------------------------------------------------------------------
+template <int WAVES, typename OutT>
+__global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec2(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, const int32_t* __restrict__ wq,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
+    OutT* __restrict__ y) {
+  constexpr bool kI32 = __is_same(OutT, int32_t);
+  constexpr int kThreads = 64 * WAVES;
+  extern __shared__ __attribute__((aligned(16))) u32 szl[];   // 32 x sz_pitch(G) words
+  __shared__ __attribute__((aligned(16))) int8_t tiles[WAVES][kTileBytes];
+  __shared__ v4f red[kI32 ? 1 : WAVES][2][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int n0 = blockIdx.x * 32;
+  const int G = K >> 7, Kw = K >> 3, RB = Kw * 4;
+  const int units = (RB + kUnitBytes - 1) / kUnitBytes;
+  const int ub = (int)((int64_t)units * wave / WAVES), ue = (int)((int64_t)units * (wave + 1) / WAVES);
+  rsrc_t wr[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int nb = n0 + 16 * b;
+    const int rows = max(0, min(16, N - nb));
+    wr[b] = make_rsrc(wq + (int64_t)min(nb, N) * Kw, (u32)(rows * RB));
+  }
+  const UnitLanes ul = unit_lanes(lane, RB);
+  const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
+  const u32 xoff = (u32)(r * K + 32 * j);
+  struct Batch { v4i w[2][2], xa[2][2]; };
+  auto load = [&](Batch& bt, int q) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) unit_load(bt.w[b], wr[b], ul, q, q < ue, RB);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int g = 2 * q + s;
+      const bool gin = q < ue && g < G;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) bt.xa[s][h] = bld16(xr, gin ? xoff + 128 * g + 16 * h : kOOB);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  Batch b0, b1;
+  ScaleZeroStage<kThreads, 4> sz;
+  const int srows = max(0, min(32, N - n0));
+  const rsrc_t sr = make_rsrc(wscale + (int64_t)min(n0, N) * G, (u32)(srows * G * 2));
+  const rsrc_t zr = make_rsrc(wzero + (int64_t)min(n0, N) * G, (u32)(srows * G * 2));
+  sz.load(sr, zr, 32 * G, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(b0, ub);
+  sz.finish(sr, zr, szl, G, 32 * G);
+  lds_barrier();
+
+  const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  int8_t* tile = tiles[wave];
+  v4f yacc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+  auto mma = [&](const Batch& bt, int q) {
+    v4i f[2][2];
+    unit_transpose(tile, bt.w[0], ul, f[0]);
+    unit_transpose(tile, bt.w[1], ul, f[1]);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int g = 2 * q + s;
+      const bool gin = q < ue && g < G;
+      const v4i a0 = shuffle_act16(bt.xa[s][0]), a1 = shuffle_act16(bt.xa[s][1]);
+      v4i rs = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+      rs = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, ones, rs, 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const u32 szw = gin ? szl[(16 * b + r) * sz_pitch(G) + g] : 0u;
+        const int z = (int)f16_bits_to_f32((uint16_t)(szw >> 16));
+        v4i acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __mul24(-z, rs[i]);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_u4_pair((u32)f[b][s][0], (u32)f[b][s][1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_u4_pair((u32)f[b][s][2], (u32)f[b][s][3]), acc, 0, 0, 0);
+        if constexpr (kI32) {
+          const int n = n0 + 16 * b + r;
+          if (gin && n < N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = 4 * j + i;
+              if (m < M) y[((int64_t)m * G + g) * N + n] = acc[i];
+            }
+          }
+        } else {
+          const float sc = f16_bits_to_f32((uint16_t)(szw & 0xFFFFu));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) yacc[b][i] = __builtin_fmaf(sc, (float)acc[i], yacc[b][i]);
+        }
+      }
+    }
+  };
+  for (int q = ub; q < ue; q += 2) {
+    load(b1, q + 1);
+    mma(b0, q);
+    load(b0, q + 2);
+    mma(b1, q + 1);
+  }
+  if constexpr (!kI32) {
+    red[wave][0][lane] = yacc[0];
+    red[wave][1][lane] = yacc[1];
+    __syncthreads();
+    if (wave < 2) {
+      const int b = wave;
+      v4f sum = red[0][b][lane];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) sum += red[w][b][lane];
+      const int n = n0 + 16 * b + r;
+      if (n < N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * j + i;
+          if (m < M) store_out<OutT>(y, (int64_t)m * N + n, sum[i] * xs[m]);
+        }
+      }
+    }
+  }
+}
+
 template <typename OutT>
 static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* wq,
                               const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
                               hipStream_t st) {
   const size_t lds = (size_t)16 * sz_pitch(K / 128) * 4;
+  if (M <= 16 && 2 * lds <= kDecLdsMaxBytes && (N + 31) / 32 >= 256) {
+    // wide layers (measured on MI355X, K = 4096: N = 11008 M = 16 14.4 ->
+    // 11.0 us, M = 1 at N = 12288 10.1 -> 9.3 us); at N = 4096 its 128
+    // workgroups leave half the CUs idle (11.0 -> 13.6 us), so not there
+    constexpr int WAVES = 8;
+    const dim3 grid((unsigned)((N + 31) / 32)), block(64 * WAVES);
+    k_w4a8_dec2<WAVES, OutT><<<grid, block, 2 * lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y);
+    return hipGetLastError();
+  }
   if (M <= 16 && lds <= kDecLdsMaxBytes) {
     constexpr int WAVES = 8, UB = 1;  // measured on MI355X
     const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);

@@ -60,6 +60,8 @@ def test_w8a8_boundaries(M, N, K):
 
 W4A8_CASES = [
     (16, 64, 1024),      # decode kernel (M <= 16)
+    (4, 8160, 1024),     # decode kernel (N / 32 = 255)
+    (4, 8176, 1024),     # two weight blocks per wave (N / 32 = 256, last block ragged)
     (17, 64, 1024),      # one weight stream, 2 tiles of 16 rows
     (32, 64, 1024),      # 2 tiles, both full
     (33, 64, 1024),      # 4 tiles

@@ -128,7 +128,10 @@ W4_SHAPES = [(16, 4096, 11008), (1, 16, 128), (5, 17, 256), (16, 300, 1024), (17
              (33, 40, 640), (1, 12288, 4096), (3, 100, 2048), (2, 48, 14336),
              # 17..64 token rows on 2 or 4 tiles of one weight stream: partial
              # last tiles, an odd group count, the full FFN-down shape
-             (32, 4096, 11008), (64, 40, 256), (48, 300, 640), (20, 16, 128), (57, 33, 1152)]
+             (32, 4096, 11008), (64, 40, 256), (48, 300, 640), (20, 16, 128), (57, 33, 1152),
+             # two weight blocks per wave on wide layers (N / 32 >= 256): full,
+             # ragged last pair of blocks with an odd group count, 16 rows
+             (1, 8192, 1024), (3, 8200, 384), (16, 11008, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", W4_SHAPES)
@@ -152,7 +155,7 @@ def _w4a8_floor(xq, sx, packed, sc, zz):
 
 @pytest.mark.parametrize("fmt", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("M,N,K", [(16, 4096, 11008), (5, 17, 256), (33, 40, 640), (2, 48, 14336),
-                                   (64, 300, 1024)])
+                                   (64, 300, 1024), (4, 8200, 1024), (16, 11008, 4096)])
 def test_w4a8_scaled(fmt, M, N, K):
     rng = np.random.default_rng(M + 3 * N + K)
     packed, sc, zz = _u4_weights(rng, K, N)
