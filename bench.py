@@ -352,12 +352,41 @@ def run_workload(wl, steps, warmup, traffic_db):
         "gemm_tops": round(ops / (gemm_us * 1e-6) / 1e12, 2),
         "weight_copies": R, "roofline": roof,
     }
+    if wl.path == "w8a8" and wl.M > 64:
+        res["vendor_int8"] = vendor_int8(torch, qg, copies, xq, steps, capture, timed)
     print(f"[bench] {wl.name}: gemm {gemm_us:.2f} us ({roof['achieved']} {roof['unit']}, "
           f"{100 * roof['frac']:.1f}% of peak), quant {quant_us:.2f} us, "
           f"step {step_s * 1e6:.2f} us", file=sys.stderr, flush=True)
     del copies, g_warm, g_step, g_gemm, g_quant
     torch.cuda.empty_cache()
     return res
+
+
+def vendor_int8(torch, qg, copies, xq, steps, capture, timed):
+    """Context for the prefill GEMM: the same int8 x int8 -> int32 product by
+    the vendor BLAS (torch._int_mm), next to this library's kernel with int32
+    output, on the same operands and weight rotation.  Both results are
+    compared element by element."""
+    M, N = xq.shape[0], copies[0][0].shape[0]
+    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+
+    def ours(i):
+        qg.gemm_w8a8(xq, None, copies[i % len(copies)][0], None, out_dtype=torch.int32, out=acc)
+
+    def vendor(i):
+        torch._int_mm(xq, copies[i % len(copies)][0].t())
+
+    ours(0)
+    ref = torch._int_mm(xq, copies[0][0].t())   # eager first: the BLAS sets itself up
+    torch.cuda.synchronize()
+    equal = bool(torch.equal(acc, ref))
+    del ref
+    g_ours, g_vendor = capture(ours, steps), capture(vendor, steps)
+    ours_us = median_replay(lambda: timed(g_ours)[1]) / steps * 1e6
+    vendor_us = median_replay(lambda: timed(g_vendor)[1]) / steps * 1e6
+    del g_ours, g_vendor, acc
+    return {"kernel": "torch._int_mm (vendor BLAS), int32 output", "vendor_us": round(vendor_us, 2),
+            "ours_int32_us": round(ours_us, 2), "int32_equal": equal}
 
 
 def copy_calibration():
