@@ -5,7 +5,8 @@
 
 A step is one pass of the layer's hot path over one batch of synthetic input:
 per-token int8 activation quantization followed by the quantized GEMM
-(W4A16 has no activation quantization).  Weights are prepared offline
+(W4A16 has no activation quantization; W8A8 goes through quantize_gemm_w8a8,
+which runs the two as one kernel where the library finds that faster).  Weights are prepared offline
 (fold, quantization) before timing.  Each timed region is one captured HIP
 graph of exactly K steps; consecutive steps rotate over enough copies of the
 quantized weights (> 512 MB) that every GEMM streams its weights from HBM
@@ -45,6 +46,7 @@ ROTATE_BYTES = 600 * 2 ** 20    # weight copies per rotation: > 2x the 256 MB MA
 KERNEL_REPLAYS = 5              # replays of a per-kernel graph; the median is reported
 KERNEL_SOURCES = {
     "w8a8": ["gemm_w8a8.hip", "qg_decode.hpp", "qg_device.hpp"],
+    "w8a8_fq": ["gemm_w8a8_fq.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a8": ["gemm_w4a8.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a8_outl": ["gemm_w4a8.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a8_sp24": ["gemm_w4a8_sp24.hip", "qg_decode.hpp", "qg_device.hpp"],
@@ -117,6 +119,27 @@ def algorithmic(wl):
     quant = x_b * M * K + M * K + 4 * M if wl.path != "w4a16" else 0
     ops = 2 * M * N * K
     return gemm, quant, ops
+
+
+def fused_step(wl) -> bool:
+    """Whether the workload's step runs the fused quantize + W8A8 kernel: the
+    library's own choice for these sizes, asked of the library (host only)."""
+    if wl.path != "w8a8":
+        return False
+    import torch
+    import bit_quantized_gemm_int8_amd as qg
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+    return qg.quantize_gemm_w8a8_plan(tdt[wl.x_dtype], wl.M, wl.N, wl.K)
+
+
+def dominant(wl):
+    """(algorithmic bytes, ops, source key) of the workload's dominant kernel:
+    the GEMM, or for a fused step the one kernel, which reads the activations
+    and writes their codes and scales but never reads the codes back."""
+    gemm, quant, ops = algorithmic(wl)
+    if fused_step(wl):
+        return gemm + quant - (wl.M * wl.K + 4 * wl.M), ops, "w8a8_fq"
+    return gemm, ops, wl.path
 
 
 def kv_algorithmic(wl):
@@ -273,7 +296,16 @@ def run_workload(wl, steps, warmup, traffic_db):
         else:
             qg.gemm_w4a16_g128(x_in, w[0], w[1], w[2], out_dtype=y.dtype, out=y)
 
+    fused = fused_step(wl)
+
+    def layer(i):   # the W8A8 layer through its one entry point (the library's choice)
+        w = copies[i % R]
+        qg.quantize_gemm_w8a8(x_in, w[0], w[1], out_dtype=y.dtype, out=y, xq_out=(xq, xs))
+
     def step(i):
+        if wl.path == "w8a8":
+            layer(i)
+            return
         if wl.path != "w4a16":
             quant()
         gemm(i)
@@ -292,8 +324,9 @@ def run_workload(wl, steps, warmup, traffic_db):
 
     g_warm = capture(step, max(warmup, 1))
     g_step = capture(step, steps)
-    g_gemm = capture(gemm, steps)
-    g_quant = capture(lambda i: quant(), steps) if wl.path != "w4a16" else None
+    # the dominant kernel alone: the fused kernel is the whole step
+    g_gemm = capture(layer if fused else gemm, steps)
+    g_quant = capture(lambda i: quant(), steps) if wl.path != "w4a16" and not fused else None
 
     # warmup replays, each checked against the eager result (all copies equal)
     for _ in range(2):
@@ -323,10 +356,10 @@ def run_workload(wl, steps, warmup, traffic_db):
         raise RuntimeError(f"{wl.name}: timed replay differs from the eager result")
 
     gemm_b, quant_b, ops = algorithmic(wl)
+    kern_b, _, path_key = dominant(wl)
     gemm_us = gemm_s / steps * 1e6
     quant_us = quant_s / steps * 1e6
     step_s = wall / steps
-    path_key = wl.path
     tr = traffic_db.get(path_key + ":" + wl.name)
     traffic = None
     if tr and tr.get("source_sha") == source_sha(path_key):
@@ -337,13 +370,13 @@ def run_workload(wl, steps, warmup, traffic_db):
                 "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic}
         value, unit = (ops / step_s / 1e12), "TOP/s"
     else:
-        achieved = gemm_b / (gemm_us * 1e-6) / 1e9
+        achieved = kern_b / (gemm_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
         value, unit = ((gemm_b + quant_b) / step_s / 1e12), "TB/s"
     res = {
         "workload": wl.name, "path": wl.path, "M": wl.M, "K": wl.K, "N": wl.N,
-        "x_dtype": wl.x_dtype, "out_dtype": wl.out_dtype,
+        "x_dtype": wl.x_dtype, "out_dtype": wl.out_dtype, "fused": fused,
         "value": round(value, 4), "unit": unit,
         "ms_per_step": round(step_s * 1e3, 5),
         "gpu_us_per_step": round(gpu / steps * 1e6, 3),
@@ -501,11 +534,11 @@ def batch_sweep(steps):
                 if path == "w4a16":
                     qg.gemm_w4a16_g128(x, c[0], c[1], c[2], out_dtype=y.dtype, out=y)
                     return
-                qg.quantize_per_token_i8(x, out=(xq, xs))
                 if path == "w8a8":
-                    qg.gemm_w8a8(xq, xs, c[0], c[1], out_dtype=y.dtype, out=y)
-                else:
-                    qg.gemm_w4a8_g128(xq, xs, c[0], c[1], c[2], out_dtype=y.dtype, out=y)
+                    qg.quantize_gemm_w8a8(x, c[0], c[1], out_dtype=y.dtype, out=y, xq_out=(xq, xs))
+                    return
+                qg.quantize_per_token_i8(x, out=(xq, xs))
+                qg.gemm_w4a8_g128(xq, xs, c[0], c[1], c[2], out_dtype=y.dtype, out=y)
 
             def dense(i):
                 torch.matmul(x16, copies16[i % R16], out=y16)
@@ -526,7 +559,7 @@ def batch_sweep(steps):
 # (rocprofv3 leaves names with _Float16 mangled, hence the alternatives)
 KERNEL_OF = {
     "w8a8_decode_ffn_up": [("k_w8a8_dec<8,", "unsigned short>")],
-    "w8a8_tiny": [("k_w8a8_wide<1,", "float>")],
+    "w8a8_tiny": [("k_w8a8_fq<16,", "float>")],
     "w4a8_ffn_down": [("k_w4a8_dec<16, 8, 1, false, unsigned short>",)],
     "w4a8_outl_ffn_down": [("k_w4a8_dec<16, 8, 1, true, unsigned short>",)],
     "w4a8_sp24_ffn_down": [("k_w4a8_sp24<unsigned short>",)],
@@ -536,7 +569,7 @@ KERNEL_OF = {
 }
 # profile file label of each workload's dominant kernel
 KERNEL_LABEL = {
-    "w8a8_decode_ffn_up": "gemm_w8a8_dec", "w8a8_tiny": "gemm_w8a8_wide",
+    "w8a8_decode_ffn_up": "gemm_w8a8_dec", "w8a8_tiny": "gemm_w8a8_fq",
     "w4a8_ffn_down": "gemm_w4a8_dec", "w4a16_qkv": "gemm_w4a16_dec", "w8a8_prefill": "gemm_w8a8_tiled",
     "kv_llama2_7b_4k": "kv_quant_seg", "w4a8_outl_ffn_down": "gemm_w4a8_outl_dec",
     "w4a8_sp24_ffn_down": "gemm_w4a8_sp24",
@@ -568,8 +601,8 @@ def _profiled(name):
         wl = kv[name]
         return kv_algorithmic(wl)[0], 0, "kv", f"T={wl.T}, H={wl.H}, D={wl.D}, {wl.dtype}"
     wl = by_name(name)
-    gemm_b, _, ops = algorithmic(wl)
-    return gemm_b, ops, wl.path, f"M={wl.M}, K={wl.K}, N={wl.N}"
+    kern_b, ops, key = dominant(wl)
+    return kern_b, ops, key, f"M={wl.M}, K={wl.K}, N={wl.N}"
 
 
 def ingest_counters(d):
@@ -666,6 +699,16 @@ def ingest_counters(d):
     print(json.dumps(out, indent=1))
 
 
+STEP_TEXT = {
+    "w8a8": lambda h: "quantize_gemm_w8a8: " + ("one fused kernel" if h["fused"] else
+                                                  "quantize_per_token_i8 + gemm_w8a8 kernels"),
+    "w4a8": lambda h: "quantize_per_token_i8 + gemm_w4a8_g128",
+    "w4a8_outl": lambda h: "quantize_per_token_i8 + gemm_w4a8_g128_outliers",
+    "w4a8_sp24": lambda h: "quantize_per_token_i8 + gemm_w4a8_g128_sparse24",
+    "w4a16": lambda h: "gemm_w4a16_g128",
+}
+
+
 def _config(head):
     if "T" in head:   # a KV-cache workload run on its own
         return {"workload": head["workload"], "T": head["T"], "H": head["H"], "D": head["D"],
@@ -674,8 +717,7 @@ def _config(head):
                 "parallelism": "single GPU"}
     return {"workload": head["workload"], "M": head["M"], "K": head["K"], "N": head["N"],
             "x_dtype": head["x_dtype"], "out_dtype": head["out_dtype"],
-            "step": ("quantize_per_token_i8 + gemm_w8a8" if head["path"] != "w4a16"
-                     else "gemm_w4a16_g128") + " (captured HIP graph)",
+            "step": STEP_TEXT[head["path"]](head) + " (captured HIP graph)",
             "parallelism": "single GPU"}
 
 

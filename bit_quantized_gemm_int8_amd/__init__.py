@@ -35,6 +35,7 @@ __all__ = [
     "LIB_PATH", "load", "QG_F32", "QG_F16", "QG_BF16", "QG_I32",
     "quantize_per_token_i8", "quantize_weight_i8_per_channel", "quantize_weight_u4_g128",
     "gemm_w8a8", "gemm_w4a8_g128", "gemm_w4a16_g128", "quantize_gemm_w8a8",
+    "quantize_gemm_w8a8_plan",
     "smoothquant_fold", "awq_fold", "apply_smoothing", "status_string",
     "quantize_kv_i8_segments", "dequantize_kv_i8_segments", "KV_SEGMENT",
     "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
@@ -54,6 +55,7 @@ _SIGNATURES = {
     "quantize_weight_u4_g128": [_vp, _i64, _i64, _vp, _vp, _vp, _vp],
     "gemm_w8a8": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
     "quantize_gemm_w8a8": [_vp, _int, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _int, _vp],
+    "quantize_gemm_w8a8_plan": [_int, _i64, _i64, _i64, _int, _vp],
     "gemm_w4a8_g128": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
     "gemm_w4a16_g128": [_vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
     "smoothquant_fold": [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp],
@@ -198,6 +200,15 @@ def quantize_gemm_w8a8(x, wq, w_scale, out_dtype=torch.bfloat16, out=None, xq_ou
     _call("quantize_gemm_w8a8", px, _DTYPE_CODE[x.dtype], pwq, pws, M, N, K, y.data_ptr(),
           _DTYPE_CODE[out_dtype], xq.data_ptr(), xs.data_ptr(), _FUSE[fuse], _stream())
     return y, xq, xs
+
+
+def quantize_gemm_w8a8_plan(x_dtype, M, N, K, fuse=None) -> bool:
+    """True when quantize_gemm_w8a8 with activations of x_dtype and these
+    sizes runs the one-kernel form, False for the two kernels (host only)."""
+    fused = ctypes.c_int(0)
+    _call("quantize_gemm_w8a8_plan", _DTYPE_CODE[x_dtype], M, N, K, _FUSE[fuse],
+          ctypes.byref(fused))
+    return bool(fused.value)
 
 
 def gemm_w4a8_g128(xq, x_scale, wq, w_scale, w_zero, out_dtype=torch.bfloat16, out=None):

@@ -123,6 +123,17 @@ qg_status_t quantize_gemm_w8a8(const void* x, int x_dtype, const int8_t* wq, con
                                                   static_cast<hipStream_t>(stream)));
 }
 
+qg_status_t quantize_gemm_w8a8_plan(int x_dtype, int64_t M, int64_t N, int64_t K, int fuse,
+                                    int* fused) {
+  if (qg_status_t s = check_dims(M, N, K)) return s;
+  if (K % 16 || K > kMaxK8) return QG_ERR_SHAPE;
+  if (fuse != QG_FUSE_AUTO && fuse != QG_FUSE_NEVER && fuse != QG_FUSE_FIT) return QG_ERR_ARG;
+  if (!is_float_dtype(x_dtype)) return QG_ERR_DTYPE;
+  if (!fused) return QG_ERR_NULL;
+  *fused = qg::quantize_gemm_w8a8_fused(x_dtype, M, N, K, fuse) ? 1 : 0;
+  return QG_OK;
+}
+
 qg_status_t gemm_w4a8_g128(const int8_t* xq, const float* x_scale, const int32_t* wq,
                            const uint16_t* w_scale_f16, const uint16_t* w_zero_f16, int64_t M,
                            int64_t N, int64_t K, void* y, int y_dtype, void* stream) {

@@ -36,26 +36,37 @@ namespace qg {
 constexpr int kFqWaves = 16;    // waves per workgroup: BL blocks x (16 / BL) K splits
 constexpr int kFqDepth = 4;     // weight units in flight per wave (8 measured slower)
 
+// Bytes of one activation element, and 16-byte loads per 8-value chunk.
 template <int DT>
-__device__ __forceinline__ void fq_widen8(v4i raw, float (&v)[8]) {
+constexpr int fq_esize() { return DT == F32 ? 4 : 2; }
+template <int DT>
+constexpr int fq_loads() { return DT == F32 ? 2 : 1; }
+
+template <int DT>
+__device__ __forceinline__ void fq_widen8(const v4i (&raw)[fq_loads<DT>()], float (&v)[8]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const u32 u = (u32)raw[e];
-    if constexpr (DT == BF16) {
-      v[2 * e] = bf16_bits_to_f32(u & 0xFFFFu);
-      v[2 * e + 1] = bf16_bits_to_f32(u >> 16);
+    if constexpr (DT == F32) {
+      v[e] = __int_as_float(raw[0][e]);
+      v[4 + e] = __int_as_float(raw[fq_loads<DT>() - 1][e]);
     } else {
-      v[2 * e] = f16_bits_to_f32((uint16_t)(u & 0xFFFFu));
-      v[2 * e + 1] = f16_bits_to_f32((uint16_t)(u >> 16));
+      const u32 u = (u32)raw[0][e];
+      if constexpr (DT == BF16) {
+        v[2 * e] = bf16_bits_to_f32(u & 0xFFFFu);
+        v[2 * e + 1] = bf16_bits_to_f32(u >> 16);
+      } else {
+        v[2 * e] = f16_bits_to_f32((uint16_t)(u & 0xFFFFu));
+        v[2 * e + 1] = f16_bits_to_f32((uint16_t)(u >> 16));
+      }
     }
   }
 }
 
-// MR token rows of K 16-bit values (DT = BF16 or F16); CPT 8-value chunks
-// per thread (K / 8 <= 64 (kFqWaves / MR) CPT).
+// MR token rows of K values of type DT (F32, F16 or BF16); CPT 8-value
+// chunks per thread (K / 8 <= 64 (kFqWaves / MR) CPT).
 template <int MR, int CPT, int BL, int DT, typename OutT>
 __global__ __launch_bounds__(64 * kFqWaves) void k_w8a8_fq(
-    const uint16_t* __restrict__ x, const int8_t* __restrict__ wq, const float* __restrict__ ws,
+    const void* __restrict__ x, const int8_t* __restrict__ wq, const float* __restrict__ ws,
     int M, int N, int K, OutT* __restrict__ y, int8_t* __restrict__ xq_out,
     float* __restrict__ xs_out) {
   constexpr int kFqSplit = kFqWaves / BL;
@@ -81,12 +92,15 @@ __global__ __launch_bounds__(64 * kFqWaves) void k_w8a8_fq(
   //    p * 64 * CPT + l + 64 i (i < CPT) of the row's cpr chunks.
   constexpr int WPR = kFqWaves / MR;
   const int m_w = wave / WPR, part = wave % WPR;        // wave-uniform
-  const rsrc_t xr = make_rsrc(x, (u32)(M * K * 2));
-  v4i raw[CPT];
+  constexpr int kL = fq_loads<DT>();
+  const rsrc_t xr = make_rsrc(x, (u32)(M * K * fq_esize<DT>()));
+  v4i raw[CPT][kL];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int ch = part * 64 * CPT + lane + 64 * i;
-    raw[i] = bld16(xr, m_w < M && ch < cpr ? (u32)(16 * (m_w * cpr + ch)) : kOOB);
+    const u32 off = m_w < M && ch < cpr ? (u32)(16 * kL * (m_w * cpr + ch)) : kOOB;
+#pragma unroll
+    for (int l = 0; l < kL; ++l) raw[i][l] = bld16(xr, off + 16 * l);   // kOOB + 16: still out
   }
   // 2. this wave's first kFqDepth weight units, in flight during the
   //    quantization below
@@ -183,7 +197,7 @@ __global__ __launch_bounds__(64 * kFqWaves) void k_w8a8_fq(
 }
 
 template <int MR, int BL, int DT, typename OutT>
-static hipError_t fq_bl(const uint16_t* x, const int8_t* wq, const float* ws, int M, int N, int K,
+static hipError_t fq_bl(const void* x, const int8_t* wq, const float* ws, int M, int N, int K,
                         OutT* y, int8_t* xq, float* xs, hipStream_t st) {
   const size_t lds = (size_t)MR * stage_pitch(K);
   // a row's K / 8 chunks over kFqWaves / MR waves: cpt per lane
@@ -202,7 +216,7 @@ static hipError_t fq_bl(const uint16_t* x, const int8_t* wq, const float* ws, in
 constexpr int kFqMinGroups = 160;
 
 template <int MR, int DT, typename OutT>
-static hipError_t fq_mr(const uint16_t* x, const int8_t* wq, const float* ws, int M, int N, int K,
+static hipError_t fq_mr(const void* x, const int8_t* wq, const float* ws, int M, int N, int K,
                         OutT* y, int8_t* xq, float* xs, hipStream_t st) {
   const int blocks = (N + 15) / 16;
   if (blocks >= 4 * kFqMinGroups) return fq_bl<MR, 4, DT, OutT>(x, wq, ws, M, N, K, y, xq, xs, st);
@@ -211,53 +225,64 @@ static hipError_t fq_mr(const uint16_t* x, const int8_t* wq, const float* ws, in
 }
 
 template <int DT, typename OutT>
-static hipError_t fq_dt(const uint16_t* x, const int8_t* wq, const float* ws, int M, int N, int K,
+static hipError_t fq_dt(const void* x, const int8_t* wq, const float* ws, int M, int N, int K,
                         OutT* y, int8_t* xq, float* xs, hipStream_t st) {
   if (M <= 1) return fq_mr<1, DT, OutT>(x, wq, ws, M, N, K, y, xq, xs, st);
   if (M <= 2) return fq_mr<2, DT, OutT>(x, wq, ws, M, N, K, y, xq, xs, st);
   if (M <= 4) return fq_mr<4, DT, OutT>(x, wq, ws, M, N, K, y, xq, xs, st);
-  return fq_mr<8, DT, OutT>(x, wq, ws, M, N, K, y, xq, xs, st);
+  if (M <= 8) return fq_mr<8, DT, OutT>(x, wq, ws, M, N, K, y, xq, xs, st);
+  return fq_mr<16, DT, OutT>(x, wq, ws, M, N, K, y, xq, xs, st);
 }
 
-// The fused kernel covers 16-bit token rows with M <= 8 whose codes fit the
-// LDS budget and a thread's registers (M K / 8 <= 4 chunks x 1024 threads).
+// Token rows handled by one launch: M rounded up to 1, 2, 4, 8 or 16.
+static int64_t fq_rows(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+
+// The fused kernel covers M <= 16 token rows whose codes fit the LDS budget
+// and a thread's registers (rows x K / 8 <= 4 chunks x 1024 threads).
 bool fq_fused_fits(int x_dtype, int64_t M, int64_t K) {
-  const int64_t mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
-  return (x_dtype == BF16 || x_dtype == F16) && M >= 1 && M <= 8 &&
+  const int64_t mr = fq_rows(M);
+  return (x_dtype == F32 || x_dtype == BF16 || x_dtype == F16) && M >= 1 && M <= 16 &&
          (size_t)mr * stage_pitch((int)K) <= kDecLdsMaxBytes && mr * (K / 8) <= 4 * 64 * kFqWaves;
 }
 
 // Where it pays (measured on MI355X against the two kernels in sequence):
-// with few token rows the repeated quantization is cheap and one launch and
-// its dependency are saved; with 8 rows it costs more than the separate pass.
+// with few token rows and a long weight stream the repeated quantization is
+// hidden behind the first weight loads, and one launch and its dependency
+// are saved; with 9-16 short rows (K <= 768) the two-kernel path would take
+// the wide GEMM, and the single launch is the shorter chain.  Elsewhere the
+// repeated quantization costs more than the separate pass.
 static bool fq_fused_pays(int64_t M, int64_t N, int64_t K) {
-  return M <= 4 && N * K >= (int64_t(1) << 25);
+  return (M <= 4 && N * K >= (int64_t(1) << 25)) || (M > 8 && K <= 768);
+}
+
+bool quantize_gemm_w8a8_fused(int x_dtype, int64_t M, int64_t N, int64_t K, int fuse) {
+  return M > 0 && N > 0 && fuse != kFuseNever && fq_fused_fits(x_dtype, M, K) &&
+         (fuse == kFuseFit || fq_fused_pays(M, N, K));
+}
+
+template <int DT>
+static hipError_t fq_xt(const void* x, const int8_t* wq, const float* ws, int m, int n, int k,
+                        void* y, int y_dtype, int8_t* xq, float* xs, hipStream_t st) {
+  switch (y_dtype) {
+    case F32: return fq_dt<DT, float>(x, wq, ws, m, n, k, (float*)y, xq, xs, st);
+    case F16: return fq_dt<DT, _Float16>(x, wq, ws, m, n, k, (_Float16*)y, xq, xs, st);
+    case BF16: return fq_dt<DT, uint16_t>(x, wq, ws, m, n, k, (uint16_t*)y, xq, xs, st);
+    default: return fq_dt<DT, int32_t>(x, wq, ws, m, n, k, (int32_t*)y, xq, xs, st);
+  }
 }
 
 hipError_t launch_quantize_gemm_w8a8(const void* x, int x_dtype, const int8_t* wq,
                                      const float* ws, int64_t M, int64_t N, int64_t K, void* y,
                                      int y_dtype, int8_t* xq, float* xs, int fuse, hipStream_t st) {
-  const bool fused = fuse != kFuseNever && fq_fused_fits(x_dtype, M, K) &&
-                     (fuse == kFuseFit || fq_fused_pays(M, N, K));
-  if (!fused) {
+  if (!quantize_gemm_w8a8_fused(x_dtype, M, N, K, fuse)) {
     if (hipError_t e = launch_quant_per_token(x, x_dtype, M, K, xq, xs, st)) return e;
     return launch_gemm_w8a8(xq, xs, wq, ws, M, N, K, y, y_dtype, st);
   }
-  const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (x_dtype == F16) {
-    switch (y_dtype) {
-      case F32: return fq_dt<F16, float>(xh, wq, ws, m, n, k, (float*)y, xq, xs, st);
-      case F16: return fq_dt<F16, _Float16>(xh, wq, ws, m, n, k, (_Float16*)y, xq, xs, st);
-      case BF16: return fq_dt<F16, uint16_t>(xh, wq, ws, m, n, k, (uint16_t*)y, xq, xs, st);
-      default: return fq_dt<F16, int32_t>(xh, wq, ws, m, n, k, (int32_t*)y, xq, xs, st);
-    }
-  }
-  switch (y_dtype) {
-    case F32: return fq_dt<BF16, float>(xh, wq, ws, m, n, k, (float*)y, xq, xs, st);
-    case F16: return fq_dt<BF16, _Float16>(xh, wq, ws, m, n, k, (_Float16*)y, xq, xs, st);
-    case BF16: return fq_dt<BF16, uint16_t>(xh, wq, ws, m, n, k, (uint16_t*)y, xq, xs, st);
-    default: return fq_dt<BF16, int32_t>(xh, wq, ws, m, n, k, (int32_t*)y, xq, xs, st);
+  switch (x_dtype) {
+    case F32: return fq_xt<F32>(x, wq, ws, m, n, k, y, y_dtype, xq, xs, st);
+    case F16: return fq_xt<F16>(x, wq, ws, m, n, k, y, y_dtype, xq, xs, st);
+    default: return fq_xt<BF16>(x, wq, ws, m, n, k, y, y_dtype, xq, xs, st);
   }
 }
 

@@ -24,6 +24,9 @@ hipError_t launch_quantize_gemm_w8a8(const void* x, int x_dtype, const int8_t* w
                                      const float* ws, int64_t M, int64_t N, int64_t K, void* y,
                                      int y_dtype, int8_t* xq, float* xs, int fuse,
                                      hipStream_t st);
+// Whether launch_quantize_gemm_w8a8 with these arguments runs the one-kernel
+// form (host only).
+bool quantize_gemm_w8a8_fused(int x_dtype, int64_t M, int64_t N, int64_t K, int fuse);
 hipError_t launch_gemm_w4a8(const int8_t* xq, const float* xs, const int32_t* wq,
                             const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
                             int64_t K, void* y, int y_dtype, hipStream_t st);

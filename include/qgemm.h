@@ -154,12 +154,14 @@ qg_status_t gemm_w8a8(const int8_t* xq, const float* x_scale, const int8_t* wq,
  * fuse:     QG_FUSE_AUTO, QG_FUSE_NEVER or QG_FUSE_FIT (below).
  * K must be a positive multiple of 16 (K <= 133144).  The fused kernel
  * quantizes the token rows into on-chip memory and runs the product in one
- * launch (no separate quantization pass); it covers 16-bit activations with
- * M <= 8 and M K <= 32768.  QG_FUSE_FIT runs it on every shape it covers,
- * QG_FUSE_NEVER never, QG_FUSE_AUTO only where it is the faster choice
- * (M <= 4 and N K >= 2^25: a long weight stream, few token rows); every
- * other case runs the two steps in sequence.  The results do not depend on
- * the choice.  N == 0 computes xq and x_scale only.
+ * launch (no separate quantization pass); it covers M <= 16 and m K <= 32768,
+ * m being M rounded up to 1, 2, 4, 8 or 16.  QG_FUSE_FIT runs it on every
+ * shape it covers, QG_FUSE_NEVER never, QG_FUSE_AUTO only where it is the
+ * faster choice (M <= 4 and N K >= 2^25: a long weight stream, few token
+ * rows; or 9 <= M <= 16 with K <= 768); every other case runs the two steps
+ * in sequence.  The results do not depend on the choice.  N == 0 computes
+ * xq and x_scale only.  quantize_gemm_w8a8_plan tells which form a call
+ * takes.
  */
 typedef enum qg_fuse {
   QG_FUSE_AUTO = 0,
@@ -170,6 +172,16 @@ typedef enum qg_fuse {
 qg_status_t quantize_gemm_w8a8(const void* x, int x_dtype, const int8_t* wq, const float* w_scale,
                                int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int8_t* xq,
                                float* x_scale, int fuse, void* stream);
+
+/*
+ * Which form quantize_gemm_w8a8 takes for these arguments: *fused = 1 for
+ * the one-kernel form, 0 for the two kernels in sequence (and for M == 0 or
+ * N == 0).  Host only: launches nothing and needs no device.  Returns the
+ * status quantize_gemm_w8a8 would return for a bad size, dtype or fuse
+ * argument; QG_ERR_NULL when fused is NULL.
+ */
+qg_status_t quantize_gemm_w8a8_plan(int x_dtype, int64_t M, int64_t N, int64_t K, int fuse,
+                                    int* fused);
 
 /*
  * W4A8 GEMM with g=128 uint4 weights unpacked and zero-point corrected inside

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
               "qg_abi_version", "quantize_kv_i8_segments", "dequantize_kv_i8_segments",
               "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
               "quantize_weight_u4_g128_sparse24", "gemm_w4a8_g128_sparse24",
-              "quantize_gemm_w8a8"]:
+              "quantize_gemm_w8a8", "quantize_gemm_w8a8_plan"]:
         assert n in names, n
 
 
@@ -137,6 +137,38 @@ def test_validation_codes():
     assert fq(None, 2, None, None, 0, 16, 4096, None, 2, None, None, 2, None) == OK
     assert "ARG" in lib.qg_status_string(6).decode()
     assert "SHAPE" in lib.qg_status_string(2).decode()
+
+
+def test_fused_plan_on_the_host():
+    """quantize_gemm_w8a8_plan: the automatic choice on both sides of each of
+    its thresholds, the forced modes and the fused kernel's coverage (a host
+    query: nothing is launched)."""
+    import torch
+    import bit_quantized_gemm_int8_amd as q
+    _lib()
+    plan = q.quantize_gemm_w8a8_plan
+    bf, f32 = torch.bfloat16, torch.float32
+    assert plan(bf, 4, 8192, 4096)                  # few rows, N K = 2^25
+    assert not plan(bf, 4, 8192, 4080)              # N K < 2^25
+    assert not plan(bf, 5, 8192, 4096)              # 5..8 rows
+    assert plan(f32, 16, 512, 512)                  # 9..16 short rows
+    assert plan(bf, 9, 11008, 768)
+    assert not plan(bf, 9, 11008, 784)              # K > 768
+    assert not plan(f32, 8, 512, 512)
+    assert not plan(bf, 17, 512, 512, fuse=True)    # past the kernel's 16 rows
+    assert plan(bf, 16, 64, 2048, fuse=True)        # 16 rows x 256 chunks: covered
+    assert not plan(bf, 16, 64, 2064, fuse=True)    # past 4096 chunks
+    assert plan(f32, 1, 64, 32768, fuse=True)
+    assert not plan(f32, 1, 64, 32784, fuse=True)
+    assert not plan(bf, 1, 11008, 4096, fuse=False)
+    assert not plan(bf, 0, 11008, 4096) and not plan(bf, 1, 0, 4096)
+    lib = q.load()
+    out = ctypes.c_int(7)
+    assert lib.quantize_gemm_w8a8_plan(2, 4, 16, 100, 0, ctypes.byref(out)) == 2   # SHAPE
+    assert lib.quantize_gemm_w8a8_plan(3, 4, 16, 128, 0, ctypes.byref(out)) == 4   # DTYPE
+    assert lib.quantize_gemm_w8a8_plan(2, 4, 16, 128, 5, ctypes.byref(out)) == 6   # ARG
+    assert lib.quantize_gemm_w8a8_plan(2, 4, 16, 128, 0, None) == 1                # NULL
+    assert out.value == 7                                                         # untouched
 
 
 def test_binding_rejects_host_tensors():

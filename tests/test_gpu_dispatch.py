@@ -132,6 +132,11 @@ FUSED_CASES = [
     (1, 64, 32784, True),     # past that: two kernels even when asked to fuse
     (8, 64, 4096, True),      # fused: 8 rows of 512 chunks
     (8, 64, 4112, True),      # past that: two kernels
+    (16, 64, 2048, True),     # fused: 16 rows of 256 chunks, one row per wave
+    (16, 64, 2064, True),     # past that: two kernels
+    (16, 512, 768, None),     # automatic choice: fused (9..16 rows, K <= 768)
+    (16, 512, 784, None),     # automatic choice: two kernels (K > 768)
+    (8, 512, 512, None),      # automatic choice: two kernels (8 rows, N K < 2^25)
 ]
 
 

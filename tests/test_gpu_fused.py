@@ -42,37 +42,61 @@ def _case(M, N, K, xdt, ydt, seed, fuse=True):
     assert torch.equal(_bits(y), _bits(y2))
 
 
-# inside the fused range (16-bit x, M <= 8, M K <= 32768), one kernel forced:
-# every MR class, ragged K (units past K, a row's chunks split over waves), N
-# tails, and grids of 1, 2 and 4 weight blocks per workgroup
+# inside the fused range (M <= 16, m K <= 32768 with m = M rounded up to a
+# power of two), one kernel forced: every MR class, ragged K (units past K,
+# a row's chunks split over waves), N tails, and grids of 1, 2 and 4 weight
+# blocks per workgroup
 @pytest.mark.parametrize("M,N,K", [(1, 16, 16), (1, 11008, 4096), (2, 17, 512), (3, 100, 4112),
                                    (4, 64, 8192), (5, 1040, 2000), (8, 11008, 4096), (8, 40, 4096),
                                    (7, 33, 1024), (8, 4096, 2048), (2, 5136, 1024), (1, 4096, 11008),
-                                   (6, 10256, 4096)])
-@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+                                   (6, 10256, 4096), (9, 64, 1024), (16, 512, 512), (12, 300, 2048),
+                                   (16, 11008, 768), (13, 1000, 384)])
+@pytest.mark.parametrize("xdt", ["bf16", "f16", "f32"])
 def test_fused_matches_two_steps(M, N, K, xdt):
     _case(M, N, K, xdt, "bf16", seed=M * 1000 + N + K)
 
 
 @pytest.mark.parametrize("ydt", ["f32", "f16", "i32"])
-def test_fused_output_dtypes(ydt):
-    _case(8, 1040, 4096, "bf16", ydt, seed=5)
+@pytest.mark.parametrize("M", [8, 16])
+def test_fused_output_dtypes(ydt, M):
+    _case(M, 1040, 1024, "bf16", ydt, seed=5 + M)
 
 
-# outside it (fp32 activations, M > 8, M K > 32768), or kept out of it
-@pytest.mark.parametrize("M,N,K,xdt", [(8, 64, 4096, "f32"), (9, 64, 1024, "bf16"),
-                                       (16, 100, 4096, "bf16"), (8, 64, 8192, "bf16"),
+# outside it (M > 16, or rows whose codes exceed 4096 chunks), asked to fuse
+# or not: the two kernels
+@pytest.mark.parametrize("M,N,K,xdt", [(17, 64, 512, "bf16"), (16, 100, 4096, "bf16"),
+                                       (8, 64, 8192, "f32"), (16, 64, 2064, "f32"),
                                        (300, 1040, 1024, "bf16")])
 @pytest.mark.parametrize("fuse", [True, False])
 def test_fallback_matches_two_steps(M, N, K, xdt, fuse):
     _case(M, N, K, xdt, "bf16", seed=M + N + K, fuse=fuse)
 
 
-# the library's own choice, on both sides of its threshold
-@pytest.mark.parametrize("M,N,K", [(1, 11008, 4096), (4, 8192, 4096), (4, 8192, 4080),
-                                   (8, 11008, 4096), (2, 64, 512)])
-def test_auto_matches_two_steps(M, N, K):
-    _case(M, N, K, "bf16", "bf16", seed=3 * M + N + K, fuse=None)
+# the library's own choice, on both sides of its thresholds
+@pytest.mark.parametrize("M,N,K,xdt", [(1, 11008, 4096, "bf16"), (4, 8192, 4096, "bf16"),
+                                       (4, 8192, 4080, "bf16"), (8, 11008, 4096, "bf16"),
+                                       (2, 64, 512, "bf16"), (16, 512, 512, "f32"),
+                                       (9, 4096, 768, "bf16"), (9, 4096, 784, "bf16")])
+def test_auto_matches_two_steps(M, N, K, xdt):
+    _case(M, N, K, xdt, "bf16", seed=3 * M + N + K, fuse=None)
+
+
+def test_tiny_workload_fused_against_oracle():
+    """The 16 x 512 x 512 fp32 workload, which the library runs fused."""
+    wl = by_name("w8a8_tiny")
+    d = draw(wl)
+    x = torch.from_numpy(d["x"]).to("cuda")
+    wq, ws = qg.quantize_weight_i8_per_channel(torch.from_numpy(d["w"]).to("cuda"))
+    assert qg.quantize_gemm_w8a8_plan(torch.float32, wl.M, wl.N, wl.K)
+    y, xq, xs = qg.quantize_gemm_w8a8(x, wq, ws, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    xq_ref, xs_ref = oracle.quantize_per_token_i8(d["x"])
+    wq_ref, ws_ref = oracle.quantize_weight_i8_per_channel(d["w"])
+    np.testing.assert_array_equal(to_np(xq), xq_ref)
+    np.testing.assert_array_equal(to_np(xs), xs_ref)
+    np.testing.assert_array_equal(to_np(wq), wq_ref)
+    yref = oracle.gemm_w8a8(xq_ref, xs_ref, wq_ref, ws_ref)
+    assert_close(out_f64(y), yref, "f32", what="fused tiny")
 
 
 def test_headline_workload_against_oracle():

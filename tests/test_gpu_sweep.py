@@ -163,8 +163,8 @@ def _fused_cases(seed, n):
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
-        M = int(rng.integers(1, 9))
-        mr = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
+        M = int(rng.integers(1, 17))
+        mr = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8 if M <= 8 else 16
         K = 16 * int(rng.integers(1, (4096 * 8 // mr) // 16 + 1))   # codes fit the fused kernel
         N = int(rng.integers(4000, 14000)) if rng.random() < 0.5 else int(rng.integers(1, 3000))
         if M * N * K <= 2e8:
@@ -179,10 +179,11 @@ FUSED = _fused_cases(707, 32)
 def test_fused_matches_two_kernels(M, N, K):
     g = torch.Generator(device="cuda")
     g.manual_seed(M * 3 + N + K)
-    x = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+    xdt = [torch.bfloat16, torch.float16, torch.float32][(M + N + K) % 3]
+    x = torch.randn((M, K), generator=g, device="cuda").to(xdt)
     w = torch.randn((K, N), generator=g, device="cuda") * 0.02
     wq, ws = qg.quantize_weight_i8_per_channel(w)
-    print(f"sweep fused M={M} N={N} K={K}", flush=True)
+    print(f"sweep fused M={M} N={N} K={K} x={xdt}", flush=True)
     y, xq, xs = qg.quantize_gemm_w8a8(x, wq, ws, out_dtype=torch.bfloat16, fuse=True)
     y2, xq2, xs2 = qg.quantize_gemm_w8a8(x, wq, ws, out_dtype=torch.bfloat16, fuse=False)
     torch.cuda.synchronize()
