@@ -18,6 +18,9 @@ inline bool is_float_dtype(int d) { return d == QG_F32 || d == QG_F16 || d == QG
 // Largest K for which K * 127 * 127 still fits int32.
 constexpr int64_t kMaxK8 = 2147483647LL / (127 * 127);
 constexpr int64_t kMaxDim = 2147483647LL;
+// Groups per row of the g=128 uint4 paths (what the weight quantizer
+// produces); the kernels' 32-bit buffer offsets are sized for this.
+constexpr int64_t kMaxGroups = 65535;
 // Groups per row of the outlier-retention and 2:4 sparse paths: their kernels
 // stage a 16-row block's scales and zero points in 80 KB of LDS
 // (16 x (G + 1) words).
@@ -81,7 +84,7 @@ qg_status_t quantize_weight_i8_per_channel(const float* w, int64_t K, int64_t N,
 qg_status_t quantize_weight_u4_g128(const float* w, int64_t K, int64_t N, int32_t* wq,
                                     uint16_t* w_scale_f16, uint16_t* w_zero_f16, void* stream) {
   if (qg_status_t s = check_dims(1, N, K)) return s;
-  if (K % 128 || K / 128 > 65535) return QG_ERR_SHAPE;
+  if (K % 128 || K / 128 > kMaxGroups) return QG_ERR_SHAPE;
   if (N == 0) return QG_OK;
   if (!w || !wq || !w_scale_f16 || !w_zero_f16) return QG_ERR_NULL;
   if (!aligned16(w) || !aligned16(wq)) return QG_ERR_ALIGN;
@@ -138,7 +141,7 @@ qg_status_t gemm_w4a8_g128(const int8_t* xq, const float* x_scale, const int32_t
                            const uint16_t* w_scale_f16, const uint16_t* w_zero_f16, int64_t M,
                            int64_t N, int64_t K, void* y, int y_dtype, void* stream) {
   if (qg_status_t s = check_dims(M, N, K)) return s;
-  if (K % 128) return QG_ERR_SHAPE;
+  if (K % 128 || K / 128 > kMaxGroups) return QG_ERR_SHAPE;
   if (y_dtype == QG_I32 && M * (K / 128) * N > kMaxDim) return QG_ERR_SHAPE;
   if (!is_float_dtype(y_dtype) && y_dtype != QG_I32) return QG_ERR_DTYPE;
   if (M == 0 || N == 0) return QG_OK;
@@ -189,7 +192,7 @@ qg_status_t quantize_weight_u4_g128_sparse24(const float* w, int64_t K, int64_t 
                                              uint16_t* w_scale_f16, uint16_t* w_zero_f16,
                                              void* stream) {
   if (qg_status_t s = check_dims(1, N, K)) return s;
-  if (K % 128 || K / 128 > 65535) return QG_ERR_SHAPE;
+  if (K % 128 || K / 128 > kMaxGroups) return QG_ERR_SHAPE;
   if (N == 0) return QG_OK;
   if (!w || !wsp || !w_scale_f16 || !w_zero_f16) return QG_ERR_NULL;
   if (!aligned16(w) || !aligned16(wsp)) return QG_ERR_ALIGN;
@@ -219,7 +222,7 @@ qg_status_t gemm_w4a16_g128(const void* x, int x_dtype, const int32_t* wq,
                             const uint16_t* w_scale_f16, const uint16_t* w_zero_f16, int64_t M,
                             int64_t N, int64_t K, void* y, int y_dtype, void* stream) {
   if (qg_status_t s = check_dims(M, N, K)) return s;
-  if (K % 128) return QG_ERR_SHAPE;
+  if (K % 128 || K / 128 > kMaxGroups) return QG_ERR_SHAPE;
   if (x_dtype != QG_F16 && x_dtype != QG_BF16) return QG_ERR_DTYPE;
   if (!is_float_dtype(y_dtype)) return QG_ERR_DTYPE;
   if (M == 0 || N == 0) return QG_OK;

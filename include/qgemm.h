@@ -118,7 +118,7 @@ qg_status_t quantize_weight_i8_per_channel(const float* w, int64_t K, int64_t N,
  * wq:          [N][K/8] int32 packed codes (format above), written.
  * w_scale_f16: [N][K/128] fp16 bits of s, written.
  * w_zero_f16:  [N][K/128] fp16 bits of z (an integer 0..15), written.
- * K must be a positive multiple of 128.
+ * K must be a positive multiple of 128 with K / 128 <= 65535.
  */
 qg_status_t quantize_weight_u4_g128(const float* w, int64_t K, int64_t N, int32_t* wq,
                                     uint16_t* w_scale_f16, uint16_t* w_zero_f16,
@@ -194,7 +194,8 @@ qg_status_t quantize_gemm_w8a8_plan(int x_dtype, int64_t M, int64_t N, int64_t K
  * w_zero_f16 [N][K/128]: read.
  * y: [M][N] of QG_F32, QG_BF16 or QG_F16; or QG_I32, in which case y is
  *    [M][K/128][N] int32 holding acc[m,g,n] (x_scale and w_scale_f16 unused).
- * K must be a positive multiple of 128.
+ * K must be a positive multiple of 128 with K / 128 <= 65535 (as for
+ * quantize_weight_u4_g128).
  */
 qg_status_t gemm_w4a8_g128(const int8_t* xq, const float* x_scale, const int32_t* wq,
                            const uint16_t* w_scale_f16, const uint16_t* w_zero_f16,
@@ -298,7 +299,8 @@ qg_status_t gemm_w4a8_g128_sparse24(const int8_t* xq, const float* x_scale, cons
  *   p[m,g,n] = sum_{k in g} x[m,k] (q[n,k] - z[n,g]);  y[m,n] = sum_g s[n,g] p[m,g,n]
  * x: [M][K] of x_dtype, QG_F16 (fp16 matrix cores) or QG_BF16 (bf16).
  * y: [M][N] of y_dtype: QG_F16, QG_BF16 or QG_F32.
- * K must be a positive multiple of 128.
+ * K must be a positive multiple of 128 with K / 128 <= 65535 (as for
+ * quantize_weight_u4_g128).
  */
 qg_status_t gemm_w4a16_g128(const void* x, int x_dtype, const int32_t* wq,
                             const uint16_t* w_scale_f16, const uint16_t* w_zero_f16,

@@ -135,6 +135,11 @@ def test_validation_codes():
     assert fq(A, 2, A, A, 8, 16, 4096, A, 2, A, A, 3, None) == 6          # QG_ERR_ARG
     assert fq(A, 2, A, A, 8, 16, 4096, A, 2, A, A, -1, None) == 6
     assert fq(None, 2, None, None, 0, 16, 4096, None, 2, None, None, 2, None) == OK
+    # the g=128 uint4 GEMMs take at most 65535 groups per row, as the quantizer
+    g4, g16 = lib.gemm_w4a8_g128, lib.gemm_w4a16_g128
+    assert g4(A, A, A, A, A, 1, 16, 65536 * 128, A, 2, None) == SHAPE
+    assert g16(A, 1, A, A, A, 1, 16, 65536 * 128, A, 1, None) == SHAPE
+    assert lib.quantize_weight_u4_g128(A, 65536 * 128, 16, A, A, A, None) == SHAPE
     assert "ARG" in lib.qg_status_string(6).decode()
     assert "SHAPE" in lib.qg_status_string(2).decode()
 
