@@ -257,13 +257,9 @@ __device__ __forceinline__ void kv_store8(OutT* p, const float (&x)[8]) {
 }
 
 // x_hat = code * s: the binary32 product (rounded once), then rounded to the
-// output type; each thread converts kDqChunks chunks of 8 channels of one
-// (position, head), one grid-stride apart, all their loads issued before
-// any product (indices past the end are clamped for the loads, their stores
-// skipped).  FAST (fewer than 2^31 chunks): the chunk index is split into
+// output type; one thread per 8 channels of one (position, head),
+// grid-stride.  FAST (fewer than 2^31 chunks): the chunk index is split into
 // (position, head, channel chunk) by multiply-high divisions.
-constexpr int kDqChunks = 2;   // measured on MI355X: 4 gained nothing over 1
-
 template <typename OutT, bool FAST>
 __global__ __launch_bounds__(256) void k_kv_dequant_seg(const int8_t* __restrict__ q,
                                                         const float* __restrict__ scale, int T,
@@ -271,45 +267,34 @@ __global__ __launch_bounds__(256) void k_kv_dequant_seg(const int8_t* __restrict
                                                         u32 cmag, int csh, u32 hmag, int hsh) {
   const int S = (T + kKvSeg - 1) / kKvSeg, cpr = D >> 3;
   const int64_t n8 = (int64_t)T * H * cpr;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x; i0 < n8; i0 += stride * kDqChunks) {
-    uint2 c[kDqChunks];
-    v4i s0[kDqChunks], s1[kDqChunks];
-#pragma unroll
-    for (int u = 0; u < kDqChunks; ++u) {
-      const int64_t i = min(i0 + u * stride, n8 - 1);
-      int cc, t, hh;
-      if constexpr (FAST) {
-        // n8 < 2^31: exact multiply-high divisions by cpr and H
-        const u32 iu = (u32)i;
-        const u32 thu = (u32)(((uint64_t)iu * cmag) >> (31 + csh));
-        cc = (int)(iu - thu * (u32)cpr);
-        t = (int)(((uint64_t)thu * hmag) >> (31 + hsh));
-        hh = (int)thu - t * H;
-      } else {
-        const int64_t th = i / cpr;
-        cc = (int)(i - th * cpr);
-        t = (int)(th / H);
-        hh = (int)(th - (int64_t)t * H);
-      }
-      c[u] = *reinterpret_cast<const uint2*>(q + 8 * i);
-      const float* sp = scale + ((int64_t)hh * S + t / kKvSeg) * D + 8 * cc;
-      s0[u] = ld16(sp);
-      s1[u] = ld16(sp + 4);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    int64_t th;
+    int cc, t, hh;
+    if constexpr (FAST) {
+      // n8 < 2^31: exact multiply-high divisions by cpr and H
+      const u32 iu = (u32)i;
+      const u32 thu = (u32)(((uint64_t)iu * cmag) >> (31 + csh));
+      cc = (int)(iu - thu * (u32)cpr);
+      t = (int)(((uint64_t)thu * hmag) >> (31 + hsh));
+      hh = (int)thu - t * H;
+      th = thu;
+    } else {
+      th = i / cpr;
+      cc = (int)(i - th * cpr);
+      t = (int)(th / H);
+      hh = (int)(th - (int64_t)t * H);
     }
+    const uint2 c = *reinterpret_cast<const uint2*>(q + 8 * i);
+    const float* sp = scale + ((int64_t)hh * S + t / kKvSeg) * D + 8 * cc;
+    const v4i s0 = ld16(sp), s1 = ld16(sp + 4);
+    float x[8];
 #pragma unroll
-    for (int u = 0; u < kDqChunks; ++u) {
-      const int64_t i = i0 + u * stride;
-      if (i >= n8) break;
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int code = (int)(int8_t)(((e < 4 ? c[u].x : c[u].y) >> (8 * (e & 3))) & 0xFFu);
-        const float sv = __int_as_float(e < 4 ? s0[u][e] : s1[u][e - 4]);
-        x[e] = (float)code * sv;
-      }
-      kv_store8<OutT>(out + 8 * i, x);
+    for (int e = 0; e < 8; ++e) {
+      const int code = (int)(int8_t)(((e < 4 ? c.x : c.y) >> (8 * (e & 3))) & 0xFFu);
+      const float sv = __int_as_float(e < 4 ? s0[e] : s1[e - 4]);
+      x[e] = (float)code * sv;
     }
+    kv_store8<OutT>(out + 8 * i, x);
   }
 }
 
@@ -357,8 +342,7 @@ hipError_t launch_kv_quant_seg(const void* kv, int kv_dtype, int64_t T, int64_t 
 template <typename OutT>
 static void kv_dequant_t(const int8_t* kv_q, const float* kv_scale, int T, int H, int D, OutT* out,
                          int64_t n8, hipStream_t st) {
-  const unsigned grid =
-      (unsigned)std::min<int64_t>((n8 + 256 * kDqChunks - 1) / (256 * kDqChunks), 65536);
+  const unsigned grid = (unsigned)std::min<int64_t>((n8 + 255) / 256, 65536);
   int csh, hsh;
   const u32 cmag = kv_magic(D / 8, csh), hmag = kv_magic(H, hsh);
   if (n8 < ((int64_t)1 << 31))   // 32-bit chunk indices: multiply-high divisions
