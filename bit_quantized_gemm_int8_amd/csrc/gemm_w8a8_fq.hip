@@ -18,15 +18,17 @@
 // -- so the separate quantization launch and its dependency disappear -- but
 // only N / (16 BL) workgroups do; each wave works on a single token row (its
 // row index, maximum, scale and reciprocal are wave-uniform scalars), each
-// thread handles at most 4 chunks of 8 values, and each wave's first D weight
-// units are already in flight while it does.  Codes go straight into LDS
+// thread handles at most 4 chunks of 8 values (16 or 32 bytes each), and
+// each wave's first D weight units are already in flight while it does.
+// Codes go straight into LDS
 // (row pitch an odd number of 16-byte chunks); workgroup 0 also writes the
 // codes and scales out.
 //
 // The separate quantization pass costs a launch and a dependency; the fused
 // prologue costs MR K / 8 chunks of work per workgroup.  With 8 token rows
-// the second is the larger (measured), so the library picks this kernel only
-// for few rows and a long weight stream.
+// of K = 4096 the second is the larger (measured), so the library picks
+// this kernel for few rows and a long weight stream, and for 9-16 short
+// rows, where the two-kernel path would take the wide GEMM.
 #include "qg_decode.hpp"
 #include "qg_device.hpp"
 #include "qg_launch.hpp"
