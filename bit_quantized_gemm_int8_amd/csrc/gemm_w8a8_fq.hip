@@ -20,9 +20,8 @@
 // row index, maximum, scale and reciprocal are wave-uniform scalars), each
 // thread handles at most 4 chunks of 8 values (16 or 32 bytes each), and
 // each wave's first D weight units are already in flight while it does.
-// Codes go straight into LDS
-// (row pitch an odd number of 16-byte chunks); workgroup 0 also writes the
-// codes and scales out.
+// Codes go straight into LDS (row pitch an odd number of 16-byte chunks);
+// workgroup 0 also writes the codes and scales out.
 //
 // The separate quantization pass costs a launch and a dependency; the fused
 // prologue costs MR K / 8 chunks of work per workgroup.  With 8 token rows
