@@ -218,6 +218,49 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16(
   }
 }
 
+// Bytes of 16-bit token values that one weight unit (two g=128 groups)
+// multiplies.
+constexpr int kSliceUnitBytes = 2 * 128 * 2;
+
+// A slice of the token rows into LDS, each 16-byte chunk already in the
+// order of the unpacked codes: bytes col0 .. col0 + row_bytes of each of ROWS
+// rows src_stride bytes apart, into rows of pitch bytes.  Chunks past the
+// slice go (as zeros) into the row's padding; rows past the resource's end
+// are zeros.  `after` runs once the first round of loads is issued.
+template <int ROWS, int THREADS, typename A>
+__device__ __forceinline__ void stage_slice_halves(int8_t* dst, int pitch, rsrc_t src,
+                                                   int src_stride, int col0, int row_bytes,
+                                                   A after) {
+  constexpr int CPR = ROWS <= 4 ? 2 : 1;
+  const int kc = row_bytes >> 4;
+  v4i v[ROWS][CPR];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < CPR; ++i) {
+      const int c = c0 + (int)threadIdx.x + i * THREADS;
+#pragma unroll
+      for (int m = 0; m < ROWS; ++m)
+        v[m][i] = bld16(src, c < kc ? (u32)(m * src_stride + col0 + 16 * c) : kOOB);
+    }
+  };
+  auto store = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < CPR; ++i) {
+      const int c = c0 + (int)threadIdx.x + i * THREADS, cc = c < kc ? c : kc;
+#pragma unroll
+      for (int m = 0; m < ROWS; ++m) st16(dst + m * pitch + 16 * cc, shuffle_halves(v[m][i]));
+    }
+  };
+  load(0);
+  __builtin_amdgcn_sched_barrier(0);
+  after();
+  store(0);
+  for (int c0 = CPR * THREADS; c0 < kc; c0 += CPR * THREADS) {
+    load(c0);
+    store(c0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Decode kernel (M <= 16) on whole-line weight units (see qg_decode.hpp): a
 // unit is two g=128 groups of 16 weight rows.  The token rows are staged whole
@@ -234,7 +277,7 @@ template <int MR, int WAVES, int UB, int XDT, bool GEN, typename OutT>
 __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ wq,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
-    OutT* __restrict__ y) {
+    OutT* __restrict__ y, int phases_arg) {
   constexpr int kThreads = 64 * WAVES;
   // LDS: MR token rows (pitch stage_pitch(2K)), then 16 nb x sz_pitch(G) words
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
@@ -251,8 +294,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
   const int n_base = (bb0 + blk) * 16;
   const int G = K >> 7, Kw = K >> 3, RB = Kw * 4;   // RB: packed bytes per weight row
   const int units = (RB + kUnitBytes - 1) / kUnitBytes;
-  const int ub = (int)((int64_t)units * sub / subs), ue = (int)((int64_t)units * (sub + 1) / subs);
-  const int xpitch = stage_pitch(2 * K);
+  // K is walked in `phases` runs of units (one unless the token rows are too
+  // long for LDS); each phase stages its slice of the token rows
+  const int phases = GEN ? phases_arg : 1;
+  const int xpitch =
+      stage_pitch(min(2 * K, kSliceUnitBytes * ((units + phases - 1) / phases)));
   int8_t* xl = smem;
   u32* szl = reinterpret_cast<u32*>(smem + MR * xpitch);
 
@@ -261,74 +307,84 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
   const UnitLanes ul = unit_lanes(lane, RB);
 
   v4i b0[UB][2], b1[UB][2];
-  auto load = [&](v4i (&b)[UB][2], int q0) {
-#pragma unroll
-    for (int v = 0; v < UB; ++v) unit_load(b[v], wr, ul, q0 + v, q0 + v < ue, RB);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // scales and zero points, token rows, and behind them the first weight batch
+  // scales and zero points, then per phase the slice of the token rows and
+  // behind it the phase's first weight batch
   ScaleZeroStage<kThreads, 4> sz;
   const int srows = min(16 * nb, N - 16 * bb0);   // the workgroup's weight rows
   const rsrc_t sr = make_rsrc(wscale + (int64_t)16 * bb0 * G, (u32)(srows * G * 2));
   const rsrc_t zr = make_rsrc(wzero + (int64_t)16 * bb0 * G, (u32)(srows * G * 2));
   sz.load(sr, zr, 16 * nb * G, 0);
-  stage_rows<MR, kThreads>(xl, make_rsrc(x, (u32)(M * K * 2)), 2 * K,
-                           [](v4i v) { return shuffle_halves(v); },
-                           [&]() { load(b0, ub); });
-  sz.finish(sr, zr, szl, G, 16 * nb * G);
-  lds_barrier();
+  const rsrc_t xr = make_rsrc(x, (u32)(M * K * 2));
 
   const int8_t* xrow = xl + (r < MR ? r : 0) * xpitch + 64 * j;
   const u32* szrow = szl + (16 * blk + r) * sz_pitch(G);
   int8_t* tile = tiles[wave];
   v4f yacc = {0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const v4i (&b)[UB][2], int q0) {
+  for (int p = 0; p < phases; ++p) {
+    const int pu0 = (int)((int64_t)units * p / phases), pu1 = (int)((int64_t)units * (p + 1) / phases);
+    const int ub = pu0 + (int)((int64_t)(pu1 - pu0) * sub / subs);
+    const int ue = pu0 + (int)((int64_t)(pu1 - pu0) * (sub + 1) / subs);
+    const int col0 = kSliceUnitBytes * pu0, cols = min(kSliceUnitBytes * pu1, 2 * K) - col0;
+    auto load = [&](v4i (&b)[UB][2], int q0) {
 #pragma unroll
-    for (int v = 0; v < UB; ++v) {
-      v4i f[2];
-      unit_transpose(tile, b[v], ul, f);
-      // units past this wave's run: zero codes; their scale is taken as zero
-      const bool qin = q0 + v < ue;
-      const int q = qin ? q0 + v : 0;
+      for (int v = 0; v < UB; ++v) unit_load(b[v], wr, ul, q0 + v, q0 + v < ue, RB);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (p > 0) __syncthreads();   // every wave is done with the previous slice
+    stage_slice_halves<MR, kThreads>(xl, xpitch, xr, 2 * K, col0, cols, [&]() { load(b0, ub); });
+    if (p == 0) sz.finish(sr, zr, szl, G, 16 * nb * G);
+    lds_barrier();
+
+    auto mma = [&](const v4i (&b)[UB][2], int q0) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int g = 2 * q + s;
-        const u32 szw = qin && g < G ? szrow[g] : 0u;
-        const float sc = f16_bits_to_f32((uint16_t)(szw & 0xFFFFu));
-        const float zf = f16_bits_to_f32((uint16_t)(szw >> 16));
-        v4i bw[4];
-        if constexpr (XDT == F16) {
-          const u32 zh = f32_to_f16_bits(1024.f + zf);
-          const u32 zz = zh | (zh << 16);
+      for (int v = 0; v < UB; ++v) {
+        v4i f[2];
+        unit_transpose(tile, b[v], ul, f);
+        // units past this wave's run: zero codes; their scale is taken as zero
+        const bool qin = q0 + v < ue;
+        const int q = qin ? q0 + v : 0;
 #pragma unroll
-          for (int h = 0; h < 4; ++h) bw[h] = unpack_f16((u32)f[s][h], zz);
-        } else {
-          const float zb = 8388608.f + zf;
+        for (int s = 0; s < 2; ++s) {
+          const int g = 2 * q + s;
+          const u32 szw = qin && g < G ? szrow[g] : 0u;
+          const float sc = f16_bits_to_f32((uint16_t)(szw & 0xFFFFu));
+          const float zf = f16_bits_to_f32((uint16_t)(szw >> 16));
+          v4i bw[4];
+          if constexpr (XDT == F16) {
+            const u32 zh = f32_to_f16_bits(1024.f + zf);
+            const u32 zz = zh | (zh << 16);
 #pragma unroll
-          for (int h = 0; h < 4; ++h) bw[h] = unpack_bf16((u32)f[s][h], zb);
+            for (int h = 0; h < 4; ++h) bw[h] = unpack_f16((u32)f[s][h], zz);
+          } else {
+            const float zb = 8388608.f + zf;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) bw[h] = unpack_bf16((u32)f[s][h], zb);
+          }
+          // groups of this phase sit at 256 (g - 2 pu0) in the slice; a slot
+          // past the run or past G reads the slice's start (its scale is zero)
+          const int8_t* xf = xrow + (qin && g < G ? 256 * g - col0 : 0);
+          v4f pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const v4i a = ld16(xf + 16 * h);
+            if constexpr (XDT == F16)
+              pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
+                                                            __builtin_bit_cast(v8h, bw[h]), pacc, 0, 0, 0);
+            else
+              pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                             __builtin_bit_cast(v8bf, bw[h]), pacc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) yacc[i] = __builtin_fmaf(sc, pacc[i], yacc[i]);
         }
-        const int8_t* xf = xrow + 256 * (g < G ? g : 0);
-        v4f pacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const v4i a = ld16(xf + 16 * h);
-          if constexpr (XDT == F16)
-            pacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
-                                                          __builtin_bit_cast(v8h, bw[h]), pacc, 0, 0, 0);
-          else
-            pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
-                                                           __builtin_bit_cast(v8bf, bw[h]), pacc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) yacc[i] = __builtin_fmaf(sc, pacc[i], yacc[i]);
       }
+    };
+    for (int q0 = ub; q0 < ue; q0 += 2 * UB) {
+      load(b1, q0 + UB);
+      mma(b0, q0);
+      load(b0, q0 + 2 * UB);
+      mma(b1, q0 + UB);
     }
-  };
-  for (int q0 = ub; q0 < ue; q0 += 2 * UB) {
-    load(b1, q0 + UB);
-    mma(b0, q0);
-    load(b0, q0 + 2 * UB);
-    mma(b1, q0 + UB);
   }
 
   red[wave][lane] = yacc;
@@ -505,14 +561,15 @@ static void launch_w4a16_wide(const uint16_t* x, const int32_t* wq, const uint16
 template <int WAVES, bool GEN, int XDT, typename OutT>
 static void dec_w4a16_mr(int mr, const uint16_t* x, const int32_t* wq, const uint16_t* ws,
                          const uint16_t* wz, int M, int N, int K, OutT* y, size_t lds, int groups,
-                         hipStream_t st) {
+                         int phases, hipStream_t st) {
   constexpr int UB = 1;  // measured on MI355X
   const dim3 grid((unsigned)groups), block(64 * WAVES);
   switch (mr) {
-    case 1: k_w4a16_dec<1, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-    case 2: k_w4a16_dec<2, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-    case 4: k_w4a16_dec<4, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-    default: k_w4a16_dec<8, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+    case 1: k_w4a16_dec<1, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y, phases); break;
+    case 2: k_w4a16_dec<2, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y, phases); break;
+    case 4: k_w4a16_dec<4, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y, phases); break;
+    case 8: k_w4a16_dec<8, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y, phases); break;
+    default: k_w4a16_dec<16, WAVES, UB, XDT, GEN, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y, phases); break;
   }
 }
 
@@ -536,16 +593,46 @@ static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint1
       // more blocks than one-block workgroups can be resident at once: one
       // workgroup of 12 waves per CU over 3-4 blocks, the token rows staged
       // once (measured on MI355X: M = 8, K = 4096, N = 12288)
-      dec_w4a16_mr<12, true, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds_multi, kW16CUs, st);
+      dec_w4a16_mr<12, true, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds_multi, kW16CUs, 1, st);
     } else if (nblocks <= 384) {
       // 8 waves split K when few 16-row blocks would leave the chip short of
       // loads in flight (measured on MI355X: K = 11008, N = 4096 takes 8.6 us
       // with 8 waves, 10.4 us with 4; N >= 11008 is best with 4)
-      dec_w4a16_mr<8, false, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds, nblocks, st);
+      dec_w4a16_mr<8, false, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds, nblocks, 1, st);
     } else {
-      dec_w4a16_mr<4, false, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds, nblocks, st);
+      dec_w4a16_mr<4, false, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, lds, nblocks, 1, st);
     }
     return hipGetLastError();
+  }
+  const int nblocks16 = (N + 15) / 16;
+  if (M > 8 && M <= 16 && K >= 1536 && (nblocks16 <= 512 || (nblocks16 <= 768 && K >= 4096))) {
+    // 9-16 token rows: the decode kernel with 16 rows, their tokens staged
+    // in phases of K small enough for the scales of up to 64 weight rows to
+    // fit beside them.  Measured on MI355X against the wide kernel: faster
+    // on layers of up to 512 16-row blocks with K >= 1536 (K = 4096, N = 4096:
+    // 9.9 against 14.9 us) and on 768 blocks at K = 4096 (12.7 against 14.1);
+    // slower at K = 1024, and on 688-1024 blocks with shorter K.
+    const int units = (K / 2 + kUnitBytes - 1) / kUnitBytes;
+    auto tok_lds = [&](int ph) {
+      return (size_t)16 * stage_pitch(std::min(2 * K, kSliceUnitBytes * ((units + ph - 1) / ph)));
+    };
+    const size_t sz64 = (size_t)64 * sz_pitch(G) * 4;
+    int phases = 1;
+    while (phases < units && tok_lds(phases) + sz64 > kDecLdsMaxBytes) ++phases;
+    if (tok_lds(phases) + sz64 <= kDecLdsMaxBytes) {
+      const int nblocks = nblocks16;
+      const size_t lds16 = tok_lds(phases) + (size_t)16 * sz_pitch(G) * 4;
+      const size_t wg_lds = lds16 + 4 * (kTileBytes + 64 * sizeof(v4f));
+      const int per_cu = (int)std::min<size_t>(7, kW16CuLdsBytes / wg_lds);
+      if (nblocks > per_cu * kW16CUs && nblocks <= 4 * kW16CUs)
+        dec_w4a16_mr<12, true, XDT, OutT>(16, x, wq, ws, wz, M, N, K, y, tok_lds(phases) + sz64,
+                                          kW16CUs, phases, st);
+      else if (nblocks <= 384)
+        dec_w4a16_mr<8, true, XDT, OutT>(16, x, wq, ws, wz, M, N, K, y, lds16, nblocks, phases, st);
+      else
+        dec_w4a16_mr<4, true, XDT, OutT>(16, x, wq, ws, wz, M, N, K, y, lds16, nblocks, phases, st);
+      return hipGetLastError();
+    }
   }
   const size_t lds_wide = (size_t)16 * wide_waves(N) * sz_pitch(G) * 4;
   if (M <= 64 && lds_wide <= kDecLdsMaxBytes) {

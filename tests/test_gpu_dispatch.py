@@ -93,7 +93,14 @@ W4A16_CASES = [
     (8, 6160, 1024),     # decode, 4 waves
     (8, 64, 4864),       # decode with token rows near 80 KB
     (8, 64, 4992),       # rows past 80 KB: wide kernel
-    (9, 64, 1024),       # wide kernel (M > 8)
+    (9, 64, 1024),       # wide kernel (9..16 rows, K < 1536)
+    (16, 4096, 1536),    # 16-row decode kernel (K >= 1536, N/16 <= 512)
+    (16, 4096, 1408),    # wide kernel (K < 1536)
+    (16, 8192, 2048),    # 16-row decode kernel, 512 blocks
+    (16, 8208, 2048),    # wide kernel (513 blocks, K < 4096)
+    (12, 12288, 4096),   # 16-row decode kernel, 768 blocks over 12-wave workgroups, 2 phases
+    (12, 12304, 4096),   # wide kernel (769 blocks)
+    (10, 4096, 11008),   # 16-row decode kernel, 7 phases of K
     (65, 40, 256),       # direct-load kernel (M > 64)
 ]
 
