@@ -107,22 +107,43 @@ def _stream() -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _dev(t: torch.Tensor, name: str, dtypes) -> int:
+def _dev(t: torch.Tensor, name: str, dtypes, shape=None, device=None) -> int:
+    """Device pointer of a contiguous GPU tensor, after checking its dtype and,
+    when given, its shape and that it lives on `device` (the kernels index
+    every operand by M, N, K and the group count, so a mis-shaped tensor would
+    be read or written past its allocation)."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
 
 
-def _out(out, shape, dtype, device):
+def _opt(t, name, dtypes, shape, device):
+    """_dev for an operand that may be None (passed to the library as NULL)."""
+    return None if t is None else _dev(t, name, dtypes, shape, device)
+
+
+def _out(out, shape, dtype, device, name="out"):
     if out is None:
         return torch.empty(shape, dtype=dtype, device=device)
+    if not isinstance(out, torch.Tensor) or not out.is_cuda or out.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
     if tuple(out.shape) != tuple(shape) or out.dtype != dtype or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
     return out
+
+
+def _2d(t, name):
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor")
+    return t.shape
 
 
 _FLOATS = (torch.float32, torch.float16, torch.bfloat16)
@@ -131,10 +152,10 @@ _FLOATS = (torch.float32, torch.float16, torch.bfloat16)
 def quantize_per_token_i8(x: torch.Tensor, out=None):
     """x [M, K] (f32/f16/bf16) -> (xq int8 [M, K], x_scale f32 [M])."""
     px = _dev(x, "x", _FLOATS)
-    M, K = x.shape
+    M, K = _2d(x, "x")
     xq, xs = out if out is not None else (None, None)
-    xq = _out(xq, (M, K), torch.int8, x.device)
-    xs = _out(xs, (M,), torch.float32, x.device)
+    xq = _out(xq, (M, K), torch.int8, x.device, "xq out")
+    xs = _out(xs, (M,), torch.float32, x.device, "x_scale out")
     _call("quantize_per_token_i8", px, _DTYPE_CODE[x.dtype], M, K, xq.data_ptr(), xs.data_ptr(),
           _stream())
     return xq, xs
@@ -143,7 +164,7 @@ def quantize_per_token_i8(x: torch.Tensor, out=None):
 def quantize_weight_i8_per_channel(w: torch.Tensor):
     """w f32 [K, N] -> (wq int8 [N, K], w_scale f32 [N])."""
     pw = _dev(w, "w", (torch.float32,))
-    K, N = w.shape
+    K, N = _2d(w, "w")
     wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
     ws = torch.empty((N,), dtype=torch.float32, device=w.device)
     _call("quantize_weight_i8_per_channel", pw, K, N, wq.data_ptr(), ws.data_ptr(), _stream())
@@ -153,7 +174,7 @@ def quantize_weight_i8_per_channel(w: torch.Tensor):
 def quantize_weight_u4_g128(w: torch.Tensor):
     """w f32 [K, N] -> (wq int32 [N, K/8], scale f16 [N, K/128], zero f16 [N, K/128])."""
     pw = _dev(w, "w", (torch.float32,))
-    K, N = w.shape
+    K, N = _2d(w, "w")
     wq = torch.empty((N, K // 8), dtype=torch.int32, device=w.device)
     sc = torch.empty((N, K // 128), dtype=torch.float16, device=w.device)
     zz = torch.empty((N, K // 128), dtype=torch.float16, device=w.device)
@@ -165,14 +186,13 @@ def quantize_weight_u4_g128(w: torch.Tensor):
 def gemm_w8a8(xq, x_scale, wq, w_scale, out_dtype=torch.bfloat16, out=None):
     """y [M, N] = (xq @ wq^T) * x_scale[:, None] * w_scale[None, :] (int32 if out_dtype is int32)."""
     pxq = _dev(xq, "xq", (torch.int8,))
-    pwq = _dev(wq, "wq", (torch.int8,))
-    M, K = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] != K:
-        raise ValueError("xq and wq disagree on K")
-    pxs = _dev(x_scale, "x_scale", (torch.float32,)) if x_scale is not None else None
-    pws = _dev(w_scale, "w_scale", (torch.float32,)) if w_scale is not None else None
-    y = _out(out, (M, N), out_dtype, xq.device)
+    M, K = _2d(xq, "xq")
+    dev = xq.device
+    N = _2d(wq, "wq")[0]
+    pwq = _dev(wq, "wq", (torch.int8,), (N, K), dev)
+    pxs = _opt(x_scale, "x_scale", (torch.float32,), (M,), dev)
+    pws = _opt(w_scale, "w_scale", (torch.float32,), (N,), dev)
+    y = _out(out, (M, N), out_dtype, dev)
     _call("gemm_w8a8", pxq, pxs, pwq, pws, M, N, K, y.data_ptr(), _DTYPE_CODE[out_dtype],
           _stream())
     return y
@@ -187,16 +207,15 @@ def quantize_gemm_w8a8(x, wq, w_scale, out_dtype=torch.bfloat16, out=None, xq_ou
     the library choose, True runs the one-kernel form wherever it covers the
     shape, False the two kernels; the results are the same."""
     px = _dev(x, "x", _FLOATS)
-    pwq = _dev(wq, "wq", (torch.int8,))
-    M, K = x.shape
-    N = wq.shape[0]
-    if wq.shape[1] != K:
-        raise ValueError("x and wq disagree on K")
-    pws = _dev(w_scale, "w_scale", (torch.float32,)) if w_scale is not None else None
-    y = _out(out, (M, N), out_dtype, x.device)
+    M, K = _2d(x, "x")
+    dev = x.device
+    N = _2d(wq, "wq")[0]
+    pwq = _dev(wq, "wq", (torch.int8,), (N, K), dev)
+    pws = _opt(w_scale, "w_scale", (torch.float32,), (N,), dev)
+    y = _out(out, (M, N), out_dtype, dev)
     xq, xs = xq_out if xq_out is not None else (None, None)
-    xq = _out(xq, (M, K), torch.int8, x.device)
-    xs = _out(xs, (M,), torch.float32, x.device)
+    xq = _out(xq, (M, K), torch.int8, dev, "xq out")
+    xs = _out(xs, (M,), torch.float32, dev, "x_scale out")
     _call("quantize_gemm_w8a8", px, _DTYPE_CODE[x.dtype], pwq, pws, M, N, K, y.data_ptr(),
           _DTYPE_CODE[out_dtype], xq.data_ptr(), xs.data_ptr(), _FUSE[fuse], _stream())
     return y, xq, xs
@@ -214,16 +233,15 @@ def quantize_gemm_w8a8_plan(x_dtype, M, N, K, fuse=None) -> bool:
 def gemm_w4a8_g128(xq, x_scale, wq, w_scale, w_zero, out_dtype=torch.bfloat16, out=None):
     """W4A8 with g=128 uint4 weights; int32 out_dtype returns per-group acc [M, K/128, N]."""
     pxq = _dev(xq, "xq", (torch.int8,))
-    pwq = _dev(wq, "wq", (torch.int32,))
-    pwz = _dev(w_zero, "w_zero", (torch.float16,))
-    M, K = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] * 8 != K:
-        raise ValueError("xq and wq disagree on K")
-    pxs = _dev(x_scale, "x_scale", (torch.float32,)) if x_scale is not None else None
-    pws = _dev(w_scale, "w_scale", (torch.float16,)) if w_scale is not None else None
+    M, K = _2d(xq, "xq")
+    dev = xq.device
+    N = _2d(wq, "wq")[0]
+    pwq = _dev(wq, "wq", (torch.int32,), (N, K // 8), dev)
+    pwz = _dev(w_zero, "w_zero", (torch.float16,), (N, K // 128), dev)
+    pxs = _opt(x_scale, "x_scale", (torch.float32,), (M,), dev)
+    pws = _opt(w_scale, "w_scale", (torch.float16,), (N, K // 128), dev)
     shape = (M, K // 128, N) if out_dtype == torch.int32 else (M, N)
-    y = _out(out, shape, out_dtype, xq.device)
+    y = _out(out, shape, out_dtype, dev)
     _call("gemm_w4a8_g128", pxq, pxs, pwq, pws, pwz, M, N, K, y.data_ptr(),
           _DTYPE_CODE[out_dtype], _stream())
     return y
@@ -232,15 +250,14 @@ def gemm_w4a8_g128(xq, x_scale, wq, w_scale, w_zero, out_dtype=torch.bfloat16, o
 def gemm_w4a16_g128(x, wq, w_scale, w_zero, out_dtype=None, out=None):
     """W4A16: x f16/bf16 [M, K]; returns y [M, N] (default dtype: that of x)."""
     px = _dev(x, "x", (torch.float16, torch.bfloat16))
-    pwq = _dev(wq, "wq", (torch.int32,))
-    pws = _dev(w_scale, "w_scale", (torch.float16,))
-    pwz = _dev(w_zero, "w_zero", (torch.float16,))
-    M, K = x.shape
-    N = wq.shape[0]
-    if wq.shape[1] * 8 != K:
-        raise ValueError("x and wq disagree on K")
+    M, K = _2d(x, "x")
+    dev = x.device
+    N = _2d(wq, "wq")[0]
+    pwq = _dev(wq, "wq", (torch.int32,), (N, K // 8), dev)
+    pws = _dev(w_scale, "w_scale", (torch.float16,), (N, K // 128), dev)
+    pwz = _dev(w_zero, "w_zero", (torch.float16,), (N, K // 128), dev)
     out_dtype = out_dtype or x.dtype
-    y = _out(out, (M, N), out_dtype, x.device)
+    y = _out(out, (M, N), out_dtype, dev)
     _call("gemm_w4a16_g128", px, _DTYPE_CODE[x.dtype], pwq, pws, pwz, M, N, K, y.data_ptr(),
           _DTYPE_CODE[out_dtype], _stream())
     return y
@@ -251,7 +268,7 @@ def quantize_weight_u4_g128_outliers(w: torch.Tensor):
     records int64 [N, G] (the uint64 bit patterns), s8 f32 [N]): uint4 groups
     of 128 with each group's 3 largest weights in an INT8 side store."""
     pw = _dev(w, "w", (torch.float32,))
-    K, N = w.shape
+    K, N = _2d(w, "w")
     G = K // 128
     wq = torch.empty((N, K // 8), dtype=torch.int32, device=w.device)
     sc = torch.empty((N, G), dtype=torch.float16, device=w.device)
@@ -268,18 +285,17 @@ def gemm_w4a8_g128_outliers(xq, x_scale, wq, w_scale, w_zero, records, s8,
     """W4A8 g=128 with the INT8 outlier side path; int32 out_dtype returns the
     per-group accumulators and the side sum, [M, K/128 + 1, N]."""
     pxq = _dev(xq, "xq", (torch.int8,))
-    pwq = _dev(wq, "wq", (torch.int32,))
-    pwz = _dev(w_zero, "w_zero", (torch.float16,))
-    prc = _dev(records, "records", (torch.int64,))
-    M, K = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] * 8 != K or tuple(records.shape) != (N, K // 128):
-        raise ValueError("xq, wq and records disagree on K or N")
-    pxs = _dev(x_scale, "x_scale", (torch.float32,)) if x_scale is not None else None
-    pws = _dev(w_scale, "w_scale", (torch.float16,)) if w_scale is not None else None
-    ps8 = _dev(s8, "s8", (torch.float32,)) if s8 is not None else None
+    M, K = _2d(xq, "xq")
+    dev = xq.device
+    N = _2d(wq, "wq")[0]
+    pwq = _dev(wq, "wq", (torch.int32,), (N, K // 8), dev)
+    pwz = _dev(w_zero, "w_zero", (torch.float16,), (N, K // 128), dev)
+    prc = _dev(records, "records", (torch.int64,), (N, K // 128), dev)
+    pxs = _opt(x_scale, "x_scale", (torch.float32,), (M,), dev)
+    pws = _opt(w_scale, "w_scale", (torch.float16,), (N, K // 128), dev)
+    ps8 = _opt(s8, "s8", (torch.float32,), (N,), dev)
     shape = (M, K // 128 + 1, N) if out_dtype == torch.int32 else (M, N)
-    y = _out(out, shape, out_dtype, xq.device)
+    y = _out(out, shape, out_dtype, dev)
     _call("gemm_w4a8_g128_outliers", pxq, pxs, pwq, pws, pwz, prc, ps8, M, N, K, y.data_ptr(),
           _DTYPE_CODE[out_dtype], _stream())
     return y
@@ -289,7 +305,7 @@ def quantize_weight_u4_g128_sparse24(w: torch.Tensor):
     """w f32 [K, N] -> (wsp int32 [ceil(N/16), K/128, 16, 12], scale f16 [N, G],
     zero f16 [N, G]): 2:4 structured-sparse uint4 groups of 128."""
     pw = _dev(w, "w", (torch.float32,))
-    K, N = w.shape
+    K, N = _2d(w, "w")
     G = K // 128
     wsp = torch.empty(((N + 15) // 16, G, 16, 12), dtype=torch.int32, device=w.device)
     sc = torch.empty((N, G), dtype=torch.float16, device=w.device)
@@ -303,16 +319,15 @@ def gemm_w4a8_g128_sparse24(xq, x_scale, wsp, w_scale, w_zero, out_dtype=torch.b
                             out=None):
     """W4A8 on 2:4 sparse uint4 weights; int32 out_dtype returns per-group acc [M, K/128, N]."""
     pxq = _dev(xq, "xq", (torch.int8,))
-    pws_ = _dev(wsp, "wsp", (torch.int32,))
-    pwz = _dev(w_zero, "w_zero", (torch.float16,))
-    M, K = xq.shape
-    N = w_zero.shape[0]
-    if tuple(wsp.shape) != ((N + 15) // 16, K // 128, 16, 12):
-        raise ValueError("xq, wsp and w_zero disagree on K or N")
-    pxs = _dev(x_scale, "x_scale", (torch.float32,)) if x_scale is not None else None
-    pws = _dev(w_scale, "w_scale", (torch.float16,)) if w_scale is not None else None
+    M, K = _2d(xq, "xq")
+    dev = xq.device
+    N = _2d(w_zero, "w_zero")[0]
+    pwz = _dev(w_zero, "w_zero", (torch.float16,), (N, K // 128), dev)
+    pws_ = _dev(wsp, "wsp", (torch.int32,), ((N + 15) // 16, K // 128, 16, 12), dev)
+    pxs = _opt(x_scale, "x_scale", (torch.float32,), (M,), dev)
+    pws = _opt(w_scale, "w_scale", (torch.float16,), (N, K // 128), dev)
     shape = (M, K // 128, N) if out_dtype == torch.int32 else (M, N)
-    y = _out(out, shape, out_dtype, xq.device)
+    y = _out(out, shape, out_dtype, dev)
     _call("gemm_w4a8_g128_sparse24", pxq, pxs, pws_, pws, pwz, M, N, K, y.data_ptr(),
           _DTYPE_CODE[out_dtype], _stream())
     return y
@@ -320,11 +335,9 @@ def gemm_w4a8_g128_sparse24(xq, x_scale, wsp, w_scale, w_zero, out_dtype=torch.b
 
 def _fold(name, x_cal, w):
     pxc = _dev(x_cal, "x_cal", (torch.float32,))
-    pw = _dev(w, "w", (torch.float32,))
-    T, K = x_cal.shape
-    if w.shape[0] != K:
-        raise ValueError("x_cal and w disagree on K")
-    N = w.shape[1]
+    T, K = _2d(x_cal, "x_cal")
+    N = _2d(w, "w")[1]
+    pw = _dev(w, "w", (torch.float32,), (K, N), x_cal.device)
     s = torch.empty((K,), dtype=torch.float32, device=w.device)
     wo = torch.empty_like(w)
     _call(name, pxc, T, pw, K, N, s.data_ptr(), wo.data_ptr(), _stream())
@@ -344,8 +357,8 @@ def awq_fold(x_cal: torch.Tensor, w: torch.Tensor):
 def apply_smoothing(x: torch.Tensor, s: torch.Tensor, out_dtype=torch.bfloat16):
     """x f32 [M, K] / s[K] per column, stored as out_dtype."""
     px = _dev(x, "x", (torch.float32,))
-    ps = _dev(s, "s", (torch.float32,))
-    M, K = x.shape
+    M, K = _2d(x, "x")
+    ps = _dev(s, "s", (torch.float32,), (K,), x.device)
     y = torch.empty((M, K), dtype=out_dtype, device=x.device)
     _call("apply_smoothing", px, M, K, ps, y.data_ptr(), _DTYPE_CODE[out_dtype], _stream())
     return y
@@ -364,8 +377,8 @@ def quantize_kv_i8_segments(kv: torch.Tensor, out=None):
     T, H, D = kv.shape
     S = (T + KV_SEGMENT - 1) // KV_SEGMENT
     kq, ks = out if out is not None else (None, None)
-    kq = _out(kq, (T, H, D), torch.int8, kv.device)
-    ks = _out(ks, (H, S, D), torch.float32, kv.device)
+    kq = _out(kq, (T, H, D), torch.int8, kv.device, "kv_q out")
+    ks = _out(ks, (H, S, D), torch.float32, kv.device, "kv_scale out")
     _call("quantize_kv_i8_segments", pk, _DTYPE_CODE[kv.dtype], T, H, D, kq.data_ptr(),
           ks.data_ptr(), _stream())
     return kq, ks
@@ -375,13 +388,11 @@ def dequantize_kv_i8_segments(kv_q: torch.Tensor, kv_scale: torch.Tensor,
                               out_dtype=torch.bfloat16, out=None):
     """kv_q int8 [T, H, D] * kv_scale [H, t // 128, D] -> [T, H, D] of out_dtype."""
     pq = _dev(kv_q, "kv_q", (torch.int8,))
-    ps = _dev(kv_scale, "kv_scale", (torch.float32,))
     if kv_q.dim() != 3:
         raise ValueError("kv_q must be [T, H, D]")
     T, H, D = kv_q.shape
     S = (T + KV_SEGMENT - 1) // KV_SEGMENT
-    if tuple(kv_scale.shape) != (H, S, D):
-        raise ValueError(f"kv_scale must be [{H}, {S}, {D}]")
+    ps = _dev(kv_scale, "kv_scale", (torch.float32,), (H, S, D), kv_q.device)
     y = _out(out, (T, H, D), out_dtype, kv_q.device)
     _call("dequantize_kv_i8_segments", pq, ps, T, H, D, y.data_ptr(), _DTYPE_CODE[out_dtype],
           _stream())

@@ -134,28 +134,35 @@ __device__ __forceinline__ float block_max(float v, float* red /* LDS, NT/64 flo
 
 // ---- symmetric int8 codes ---------------------------------------------------
 // The code of x under the scale s = fl32(max|x| / 127) > 0 of its slice (row,
-// column, channel) is rint(fl32(x / s)), with x / s the correctly rounded
-// binary32 quotient and rint half to even; for finite x it lies in
-// [-127, 127], so the clamp of the definition never binds.
+// column, channel) is clamp(rint(fl32(x / s)), -127, 127), with x / s the
+// correctly rounded binary32 quotient and rint half to even.  While s is a
+// normal number |x / s| stays within one rounding of 127, but a subnormal s
+// carries fewer significant bits and can come out well below max|x| / 127
+// (max|x| = 316 * 2^-149 gives s = 2 * 2^-149 and max|x| / s = 158): the
+// clamp then binds.
 //
-// sym_code_t forms it from the reciprocal r = fl32(1 / s), computed once per
-// slice.  With q = x / s exact, |q| <= 127 (1 + 2^-21) (a finite r means
-// s >= 2^-128), fl32(q) lies within 2^-24 |q| of q and x * r, rounded once or
-// not at all, within (2^-23 + 2^-48) |q|: the two differ by less than
-// 2.3e-5 < 2^-15.  When x * r is at least 2^-15 away from every
-// half-integer, both round to the same integer; otherwise (and for any x when
-// r is infinite) the correctly rounded division decides.  Adding 1.5 * 2^23
-// rounds to an integer (half to even) and leaves it, two's complement, in the
-// low bits: the returned float's low byte is the code.  r = 0 (an all-zero
-// slice) gives code 0.
+// sym_code_t forms the code from the reciprocal r = fl32(1 / s), computed once
+// per slice.  A finite r means s >= 2^-128, where s has at least 21
+// significant bits: with q = x / s exact, |q| <= 127 (1 + 2^-21), fl32(q) lies
+// within 2^-24 |q| of q and x * r, rounded once or not at all, within
+// (2^-23 + 2^-48) |q|: the two differ by less than 2.3e-5 < 2^-15, and
+// neither leaves [-127.5, 127.5].  When x * r is at least 2^-15 away from
+// every half-integer, both round to the same integer; otherwise (and for any
+// x when r is infinite, i.e. s < 2^-128) the correctly rounded division
+// decides, clamped to [-127, 127] before rounding (the bounds are integers,
+// so clamping first is the same as clamping the rounded code).  Adding
+// 1.5 * 2^23 rounds to an integer (half to even) and leaves it, two's
+// complement, in the low bits: the returned float's low byte is the code.
+// r = 0 (an all-zero slice) gives code 0.
 constexpr float kCodeTie = 0.5f - 1.f / 32768.f;
 constexpr float kRoundMagic = 12582912.f;   // 1.5 * 2^23
 
 __device__ __forceinline__ float sym_code_t(float x, float s, float r) {
   const float a = x * r;
   float t = a + kRoundMagic;
-  // near a tie (or NaN: r infinite): the correctly rounded quotient
-  if (!(fabsf(a - (t - kRoundMagic)) <= kCodeTie)) t = (s > 0.f ? x / s : 0.f) + kRoundMagic;
+  // near a tie (or NaN: r infinite): the correctly rounded quotient, clamped
+  if (!(fabsf(a - (t - kRoundMagic)) <= kCodeTie))
+    t = (s > 0.f ? __builtin_amdgcn_fmed3f(x / s, -127.f, 127.f) : 0.f) + kRoundMagic;
   return t;
 }
 

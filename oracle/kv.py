@@ -13,10 +13,12 @@ Readings (also listed with the other readings of the pages):
     of 「现代AI加速技术全景解析」 §5.2 for one sequence.
   * Symmetric per (head, segment, channel): s = fl32(max|x| / 127) over the
     segment's positions (a last, partial segment uses the positions it has);
-    codes clamp(rne(fl32(x / s)), -127, 127); an all-zero channel of a
-    segment gets s = 0 and zero codes.  The pages' code clamps to [-128, 127];
-    with s = max|x| / 127 the quotient never leaves [-127, 127] up to one
-    rounding, so the clamp never binds either way.
+    codes clamp(rne(fl32(x / s)), -127, 127); a channel of a segment whose
+    s is 0 (all zero, or max|x| / 127 below binary32's range) gets zero
+    codes.  The pages' code clamps to [-128, 127]; while s is a normal number
+    the quotient never leaves [-127, 127] up to one rounding, so either clamp
+    gives the same codes; with a subnormal s the quotient can pass 127.5 and
+    the [-127, 127] clamp binds (the rule of the symmetric quantizer).
   * Scales are fp32, [H][ceil(T / 128)][D].
   * The per-token variant (one scale per position and head, over the head
     dim) is per-token quantization of the [T*H][D] matrix.

@@ -17,8 +17,9 @@ Readings (also listed with the other readings of the pages):
     position gets the code q = z, so it adds nothing to the 4-bit product.
   * Outliers are stored as symmetric INT8 codes with one binary32 scale per
     output channel, s8 = fl32(max |outlier| / 127) over the channel's
-    outliers (「第4章：量化」 §1.2 and §1.3); a channel whose outliers are all
-    zero gets s8 = 0 and zero codes.
+    outliers (「第4章：量化」 §1.2 and §1.3), codes clamped to [-127, 127]; a
+    channel whose s8 is 0 (outliers all zero, or too small for max/127 to
+    stay above 0 in binary32) gets zero codes.
   * Store: per (output channel, group) one 64-bit record of four 16-bit slots
     (index << 8 | code byte), the three outliers by ascending index in slots
     0-2 and 0xFFFF in slot 3.
@@ -92,10 +93,9 @@ def quantize_weight_u4_g128_outliers(w_f32: np.ndarray, n_out: int = N_OUT):
     ov = np.take_along_axis(wg, idx, axis=1)                          # [G, n_out, N]
     amax = np.abs(ov).max(axis=(0, 1))                                # [N]
     s8 = (amax / np.float32(127.0)).astype(np.float32)
-    s8_safe = np.where(amax > 0, s8, np.float32(1.0)).astype(np.float32)
+    s8_safe = np.where(s8 > 0, s8, np.float32(1.0)).astype(np.float32)
     oc = np.clip(np.rint((ov / s8_safe[None, None, :]).astype(np.float32)), -127, 127)
-    oc = np.where(amax[None, None, :] > 0, oc, 0).astype(np.int64)
-    s8 = np.where(amax > 0, s8, np.float32(0.0)).astype(np.float32)
+    oc = np.where(s8[None, None, :] > 0, oc, 0).astype(np.int64)
 
     rec = np.zeros((G, N), np.uint64)
     for i in range(n_out):

@@ -28,21 +28,25 @@ def to_f32(x, dtype: str) -> np.ndarray:
 def _symmetric_i8(x: np.ndarray, axis: int):
     """Symmetric int8 codes of x with one scale per slice along `axis`.
 
-    「第4章：量化」 §1.2: s = max|x| / 127, z = 0; §1.1: x_int = round(x/s).
+    「第4章：量化」 §1.2: s = max|x| / 127, z = 0; §1.1: x_int = round(x/s);
+    「LLM推理降本五要素」 §5.2: round, then clamp to the int8 range.
     Readings: the scale and the quotient are fl32; round is half-to-even;
-    codes are clamped to [-127, 127] (the clamp never binds, because
-    |x|/s <= 127 up to one rounding); a slice whose max|x| is 0 gets s = 0
-    and all-zero codes (no division).
+    codes are clamped to [-127, 127].  With a normal s the clamp never binds
+    (|x|/s <= 127 up to one rounding); a subnormal s has fewer significant
+    bits, so max|x|/s can exceed 127.5 and the clamp binds (max|x| =
+    316 * 2^-149 gives s = 2 * 2^-149 and 158 -> 127).  A slice whose fl32
+    scale is 0 -- all zero, or max|x| so small that max|x|/127 rounds to 0 --
+    gets s = 0 and all-zero codes (no division; x_hat = q s = 0 either way).
     """
     x = np.asarray(x, np.float32)
     amax = np.max(np.abs(x), axis=axis, keepdims=True)            # exact
     s = (amax / np.float32(127.0)).astype(np.float32)               # fl32
-    nz = np.broadcast_to(amax > 0, x.shape)
-    safe = np.where(amax > 0, s, np.float32(1.0)).astype(np.float32)
+    ok = s > 0
+    nz = np.broadcast_to(ok, x.shape)
+    safe = np.where(ok, s, np.float32(1.0)).astype(np.float32)
     quot = (x / safe).astype(np.float32)                            # fl32(x/s)
     q = np.clip(np.rint(quot), -127, 127)
     q = np.where(nz, q, 0).astype(np.int8)
-    s = np.where(amax > 0, s, np.float32(0.0)).astype(np.float32)
     return q, np.squeeze(s, axis=axis)
 
 

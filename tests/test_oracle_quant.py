@@ -7,11 +7,14 @@ What pins what:
     round and +z, clamp ranges, scale formulas (/127, /15);
   * round-trip bound |x - x_hat| <= s/2 (up to one fp32 rounding of x/s),
     which a wrong scale denominator, a wrong sign or a dropped z breaks;
-  * structural invariants: a +-127 code in every nonzero row, q = 0 at the
-    group minimum, the code range;
+  * structural invariants: a +-127 code in every row with a normal scale,
+    q = 0 at the group minimum, the code range;
+  * hand-worked subnormal-scale rows (the clamp binding, a scale that
+    underflows to 0) and exact-rational brute force across that range;
   * the packing order from a hand-written word table.
 """
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -45,9 +48,9 @@ def test_per_token_golden_ties():
 def _brute_per_token(row):
     xs = [frac(v) for v in row]
     amax = max(abs(v) for v in xs)
-    if amax == 0:
-        return [0] * len(xs), 0.0
     s = fl32(amax / 127)
+    if s == 0:
+        return [0] * len(xs), 0.0
     return [max(-127, min(127, rne_int(fl32(v / s)))) for v in xs], float(s)
 
 
@@ -62,6 +65,46 @@ def test_per_token_brute_force_random():
         bq, bs = _brute_per_token(x[m])
         assert q[m].tolist() == bq
         assert float(s[m]) == bs
+
+
+def test_per_token_golden_subnormal_scales():
+    """Hand-worked rows whose scale is subnormal: the clamp binds (158 -> 127,
+    127.5 -> 127), a scale that underflows to 0 gives zero codes."""
+    u = 2.0 ** -149
+    n = 0
+    for (su,), vals, codes in _rows("per_token_subnormal.txt"):
+        x = np.zeros((1, 16), np.float32)
+        x[0, : len(vals)] = np.array([int(v) for v in vals], np.float64) * u
+        q, sc = oracle.quantize_per_token_i8(x)
+        assert float(sc[0]) == int(su) * u
+        assert q[0, : len(vals)].tolist() == [int(c) for c in codes]
+        assert not q[0, len(vals):].any()
+        n += 1
+    assert n == 5
+
+
+def test_per_token_brute_force_subnormal():
+    """Rows with max|x| from 2^-149 to past 127 * 2^-128 (subnormal and
+    underflowing scales, finite and infinite reciprocals) against exact
+    rationals."""
+    rng = np.random.default_rng(11)
+    u = 2.0 ** -149
+    amax_units = [1, 2, 63, 64, 127, 150, 190, 191, 300, 316, 400, 444, 1000, 12345, 2 ** 20, 127 * 2 ** 21,
+                  127 * 2 ** 21 + 12345, 2 ** 23 + 1]
+    rows = []
+    for k in amax_units:
+        v = rng.integers(-k, k + 1, 24).astype(np.float64)
+        v[rng.integers(0, 24)] = k * rng.choice([-1, 1])
+        rows.append(v * u)
+    x = np.array(rows).astype(np.float32)
+    q, s = oracle.quantize_per_token_i8(x)
+    clamped = 0
+    for m in range(x.shape[0]):
+        bq, bs = _brute_per_token(x[m])
+        assert q[m].tolist() == bq
+        assert float(s[m]) == bs
+        clamped += int(bs > 0 and frac(np.max(np.abs(x[m]))) / frac(bs) > Fraction(255, 2))
+    assert clamped >= 6      # the clamp binds on several of these rows
 
 
 def test_per_token_round_trip_and_range():
