@@ -20,7 +20,10 @@ dominant kernel.  `roofline.traffic` is taken from profiles/traffic.json
 (rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a copy-kernel calibration) when
 it was measured on the current kernel sources, else null.
 The cpu_baseline is the CPU oracle timed on the host's cores on a bounded
-sample of the headline workload.
+sample of the headline workload; each of the five core workloads carries its
+own (oracle quantization + GEMM, a few seconds each).  measured_peaks holds
+the ceilings measured in the same run: a plain streaming read of each decode
+GEMM's byte count, the matrix cores on random operands, the empty launch.
 """
 from __future__ import annotations
 
@@ -70,6 +73,11 @@ def parse():
     ap.add_argument("--batch-sweep", action="store_true",
                     help="instead of the benchmark line: time every path at M = 1..64 next to "
                          "an fp16 dense GEMM of the same layer, one JSON record per (path, M)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured_peaks leg")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only the measured_peaks leg (stream read, matrix cores, launch floor)")
+    ap.add_argument("--cpu-seconds-each", type=float, default=3.0,
+                    help="oracle time per non-headline workload in the per-workload cpu baselines")
     ap.add_argument("--ingest-counters", metavar="DIR",
                     help="summarise rocprofv3 output in DIR/{stats,fetch,write} into profiles/")
     return ap.parse_args()
@@ -434,18 +442,101 @@ def copy_calibration():
     print(f"[bench] copy calibration: 3 passes over {COPY_BYTES} bytes", file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the visible cores
+        return os.cpu_count()
+
+
+def cpu_baseline_workload(wl, seconds):
+    """The oracle, as it stands, on the host cores for one workload's step:
+    per-token quantization (O1) and the layer's GEMM with its epilogue
+    (O4 W8A8, O5 W4A8, O6 W4A16 -- which has no activation quantization),
+    repeated for about `seconds` (at least once).  Offline work (fold, weight
+    quantization) is done beforehand, as in the GPU leg.  Reported in the
+    workload's own unit: TB/s of algorithmic bytes, or TOP/s for the
+    compute-bound prefill."""
+    import numpy as np
+    import oracle
+    from workloads import draw
+    d = draw(wl)
+    x, w = d["x"], d["w"]
+    if wl.fold == "smoothquant":
+        s = oracle.smoothquant_scales(d["x_cal"], w)
+        x_t = oracle.to_f32(oracle.fold_activation(x, s, wl.x_dtype), wl.x_dtype)
+        w = oracle.fold_weight(w, s)
+    elif wl.fold == "awq":
+        s = oracle.awq_scales(d["x_cal"])
+        x_t = oracle.to_f32(oracle.fold_activation(x, s, wl.x_dtype), wl.x_dtype)
+        w = oracle.fold_weight(w, s)
+    else:
+        from workloads import f32_to_bf16_bits, f32_to_f16
+        raw = {"bf16": lambda a: f32_to_bf16_bits(a), "f16": f32_to_f16,
+               "f32": lambda a: a}[wl.x_dtype](x)
+        x_t = oracle.to_f32(raw, wl.x_dtype)
+    if wl.path == "w8a8":
+        wq, ws = oracle.quantize_weight_i8_per_channel(w)
+
+        def step():
+            xq, xs = oracle.quantize_per_token_i8(x_t)
+            oracle.gemm_w8a8(xq, xs, wq, ws)
+    elif wl.path == "w4a8":
+        p, sc, zz = oracle.quantize_weight_u4_g128(w)
+
+        def step():
+            xq, xs = oracle.quantize_per_token_i8(x_t)
+            oracle.gemm_w4a8_g128(xq, xs, p, sc, zz)
+    else:
+        p, sc, zz = oracle.quantize_weight_u4_g128(w)
+        x64 = x_t.astype(np.float64)
+
+        def step():
+            oracle.gemm_w4a16_g128(x64, p, sc, zz)
+    gemm_b, quant_b, ops = algorithmic(wl)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        step()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / n
+    res = {"value": None, "unit": None, "cores": _blas_threads(), "cpu_model": cpu_model(),
+           "kind": "oracle", "ms_per_step": round(per * 1e3, 2),
+           "GBps": round((gemm_b + quant_b) / per / 1e9, 3), "GOPS": round(ops / per / 1e9, 3),
+           "sample": f"{n} full step(s) of {wl.name} ({'per-token quantization + ' if wl.path != 'w4a16' else ''}"
+                     f"{wl.M}x{wl.K}x{wl.N} {wl.path.upper()} GEMM and epilogue) in {el:.1f} s"}
+    if wl.path == "w8a8" and wl.M > 64:
+        res["value"], res["unit"] = round(ops / per / 1e12, 6), "TOP/s"
+    else:
+        res["value"], res["unit"] = round((gemm_b + quant_b) / per / 1e12, 6), "TB/s"
+    print(f"[bench] cpu baseline {wl.name}: {res['ms_per_step']} ms per step "
+          f"({res['GBps']} GB/s, {res['GOPS']} GOPS) on {res['cores']} threads", file=sys.stderr,
+          flush=True)
+    return res
+
+
 def cpu_baseline(wl, seconds):
     """The oracle, as it stands, on the host cores: quantize the activations and
     run the W8A8 GEMM + epilogue for the headline workload, repeated for about
     `seconds` (weights quantized once beforehand, like the GPU leg)."""
-    import numpy as np
     import oracle
     from workloads import draw
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: report the visible cores
-        threads = os.cpu_count()
+    threads = _blas_threads()
     d = draw(wl)
     s = oracle.smoothquant_scales(d["x_cal"], d["w"])
     x_t = oracle.to_f32(oracle.fold_activation(d["x"], s, wl.x_dtype), wl.x_dtype)
@@ -461,10 +552,93 @@ def cpu_baseline(wl, seconds):
         if el >= seconds:
             break
     return {"value": round((gemm_b + quant_b) * n / el / 1e12, 6), "unit": "TB/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{n} full steps of {wl.name} (per-token quantization of {wl.M}x{wl.K} "
                       f"+ {wl.M}x{wl.K}x{wl.N} W8A8 GEMM and epilogue) in {el:.1f} s",
             "ms_per_step": round(el / n * 1e3, 2)}
+
+
+# ------------------------------------------------------------ measured peaks
+
+PEAK_READ_BYTES = (("w4a8_ffn_down GEMM bytes", 24260672), ("w4a16_qkv GEMM bytes", 26771456),
+                   ("w8a8_decode_ffn_up GEMM bytes", 45341728))
+PEAK_MFMA = ((0, "i8 v_mfma_i32_32x32x32_i8", INT8_PEAK_TOPS),
+             (1, "i8 v_mfma_i32_16x16x64_i8", INT8_PEAK_TOPS),
+             (2, "f16 v_mfma_f32_32x32x16_f16", F16_PEAK_TFLOPS),
+             (3, "bf16 v_mfma_f32_32x32x16_bf16", F16_PEAK_TFLOPS))
+
+
+def measured_peaks(steps):
+    """The ceilings measured on this GPU in this run, next to the published
+    ones: a plain streaming read of each decode GEMM's algorithmic byte count
+    (rotating over more than 600 MB so every read comes from HBM), each
+    matrix-core instruction on random register operands (with the clock the
+    chip runs under that load, from the per-wave s_memtime / s_memrealtime
+    counters), and the fixed cost of an empty launch.  Timed like the
+    workloads: captured graphs of `steps` launches, median of 5 replays."""
+    import torch
+    import bit_quantized_gemm_int8_amd as qg
+
+    def graph_us(fn, n):
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+
+        def once():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+
+        us = median_replay(once)
+        del g
+        return us
+
+    out = {"method": "captured graphs of K launches timed with HIP events, median of 5 replays; "
+                     "reads rotate over > 600 MB of copies; matrix-core operands random full-range"}
+    reads = []
+    for label, nb in PEAK_READ_BYTES:
+        stride = (nb + 4095) // 4096 * 4096
+        R = max(2, math.ceil(ROTATE_BYTES / stride))
+        buf = torch.randint(0, 255, (R * stride,), dtype=torch.uint8, device="cuda")
+        sink = torch.empty((qg.load().qg_peak_stream_read_sink(nb),), dtype=torch.int32, device="cuda")
+        views = [buf[i * stride:(i + 1) * stride] for i in range(R)]
+        us = graph_us(lambda i: qg.peak_stream_read(views[i % R], nb, sink), steps)
+        gbs = nb / (us * 1e-6) / 1e9
+        reads.append({"what": label, "bytes": nb, "us": round(us, 3), "GBps": round(gbs, 1),
+                      "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        print(f"[bench] peak read {nb} B: {us:.2f} us, {gbs:.0f} GB/s "
+              f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})", file=sys.stderr, flush=True)
+        del buf, views, sink
+        torch.cuda.empty_cache()
+    out["stream_read"] = reads
+    out["empty_launch_us"] = round(graph_us(lambda i: qg.peak_empty(), steps), 3)
+    mf = []
+    WG, ITERS = 1024, 1500
+    clocks = torch.empty((4 * WG, 2), dtype=torch.int64, device="cuda")
+    sink = torch.empty((256 * WG,), dtype=torch.int32, device="cuda")
+    for kind, label, peak in PEAK_MFMA:
+        us = graph_us(lambda i: qg.peak_mfma(kind, ITERS, WG, clocks, sink), 3)
+        ops = qg.peak_mfma_ops(kind, ITERS, WG)
+        rate = ops / (us * 1e-6) / 1e12
+        c = clocks.double()
+        ghz = float((c[:, 0] / c[:, 1].clamp(min=1)).mean()) * 0.1   # memtime ticks per 10 ns
+        mf.append({"instruction": label, "us": round(us, 1), "rate_T": round(rate, 1),
+                   "peak_T": peak, "frac_of_peak": round(rate / peak, 4),
+                   "memtime_per_realtime_GHz": round(ghz, 3)})
+        print(f"[bench] peak {label}: {rate:.0f} T/s ({100 * rate / peak:.1f}% of {peak:.0f}), "
+              f"s_memtime rate {ghz:.2f} GHz", file=sys.stderr, flush=True)
+    out["mfma"] = mf
+    del clocks, sink
+    torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------ batch sweep
@@ -726,6 +900,11 @@ def main():
     if args.batch_sweep:
         batch_sweep(args.steps)
         return
+    if args.peaks:
+        import torch
+        print(json.dumps({"measured_peaks": measured_peaks(args.steps),
+                          "device": torch.cuda.get_device_name(0)}), flush=True)
+        return
     if args.ingest_counters:
         ingest_counters(args.ingest_counters)
         return
@@ -751,10 +930,17 @@ def main():
     if args.copy_calib:
         copy_calibration()
     head = next((r for r in results if r["workload"] == HEADLINE), results[0])
+    peaks = None if args.no_peaks else measured_peaks(args.steps)
     cpu = None
     if not args.no_cpu and head["workload"] == HEADLINE:
         print("[bench] cpu_baseline: timing the oracle", file=sys.stderr, flush=True)
         cpu = cpu_baseline(by_name(HEADLINE), args.cpu_seconds)
+        core = {w.name for w in WORKLOADS}
+        for r in results:
+            if r["workload"] in core:
+                r["cpu_baseline"] = (cpu if r["workload"] == HEADLINE else
+                                     cpu_baseline_workload(by_name(r["workload"]),
+                                                           args.cpu_seconds_each))
     line = {
         "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
@@ -762,6 +948,7 @@ def main():
         "data": "synthetic (seeded; Llama-2-7B-shaped layers, no trained weights)",
         "config": _config(head),
         "roofline": head["roofline"], "cpu_baseline": cpu,
+        "measured_peaks": peaks,
         "workloads": results,
     }
     print(json.dumps(line), flush=True)

@@ -70,6 +70,15 @@ _SIGNATURES = {
     "dequantize_kv_i8_segments": [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
 }
 
+# measurement probes (include/qgemm_peaks.h)
+_PEAK_SIGNATURES = {
+    "qg_peak_stream_read_sink": [_i64],
+    "qg_peak_stream_read": [_vp, _i64, _vp, _vp],
+    "qg_peak_mfma": [_int, _i64, _i64, _vp, _vp, _vp],
+    "qg_peak_mfma_ops": [_int, _i64, _i64],
+    "qg_peak_empty": [_vp],
+}
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -86,6 +95,10 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        for name, args in _PEAK_SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int64 if name.endswith(("_sink", "_ops")) else ctypes.c_int
         lib.qg_status_string.argtypes = [ctypes.c_int]
         lib.qg_status_string.restype = ctypes.c_char_p
         lib.qg_abi_version.restype = ctypes.c_int
@@ -397,3 +410,38 @@ def dequantize_kv_i8_segments(kv_q: torch.Tensor, kv_scale: torch.Tensor,
     _call("dequantize_kv_i8_segments", pq, ps, T, H, D, y.data_ptr(), _DTYPE_CODE[out_dtype],
           _stream())
     return y
+
+
+# ------------------------------------------------------ measurement probes
+# Not part of the layer: the ceilings its kernels are compared against.
+
+def peak_stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor = None):
+    """Read the first `nbytes` bytes of `buf` once (qg_peak_stream_read);
+    returns the int32 sink tensor the kernel writes."""
+    _dev(buf, "buf", (torch.uint8, torch.int8))
+    if nbytes > buf.numel():
+        raise ValueError("nbytes exceeds the buffer")
+    n = load().qg_peak_stream_read_sink(nbytes)
+    sink = _out(sink, (n,), torch.int32, buf.device, "sink")
+    _call("qg_peak_stream_read", buf.data_ptr(), nbytes, sink.data_ptr(), _stream())
+    return sink
+
+
+def peak_mfma(kind: int, iters: int, workgroups: int, clocks=None, sink=None):
+    """Matrix-core loop (qg_peak_mfma); returns (clocks uint64-as-int64
+    [4 * workgroups, 2], sink) -- per wave the shader-clock and 100 MHz
+    real-time counters elapsed over its loop."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    clocks = _out(clocks, (4 * workgroups, 2), torch.int64, dev, "clocks")
+    sink = _out(sink, (256 * workgroups,), torch.int32, dev, "sink")
+    _call("qg_peak_mfma", kind, iters, workgroups, clocks.data_ptr(), sink.data_ptr(), _stream())
+    return clocks, sink
+
+
+def peak_mfma_ops(kind: int, iters: int, workgroups: int) -> int:
+    return int(load().qg_peak_mfma_ops(kind, iters, workgroups))
+
+
+def peak_empty():
+    """One empty workgroup (qg_peak_empty): the fixed cost of a launch."""
+    _call("qg_peak_empty", _stream())

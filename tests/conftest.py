@@ -22,3 +22,25 @@ def _gpu_required(request):
             pytest.fail("test marked gpu but no HIP device is visible")
         print(f"\n[gpu] {request.node.nodeid}", flush=True)
     yield
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """How many outputs of each floating-point check passed only through the
+    binary32 cancellation floor (tests/tolerance.py)."""
+    try:
+        from tests.tolerance import FLOOR_LOG
+    except Exception:
+        return
+    if not FLOOR_LOG:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "outputs within the cancellation floor only")
+    agg = {}
+    for what, fmt, n, size in FLOOR_LOG:
+        a = agg.setdefault((what.split(" ")[0], fmt), [0, 0, 0.0])
+        a[0] += n
+        a[1] += size
+        a[2] = max(a[2], n / max(size, 1))
+    for (what, fmt), (n, size, worst) in sorted(agg.items()):
+        tr.write_line(f"{what:28s} {fmt:5s} {n:9d} of {size:10d} ({100 * n / max(size, 1):.3f}%; "
+                      f"worst single check {100 * worst:.3f}%)")

@@ -1,10 +1,12 @@
-"""The C-ABI library loads without a GPU, exports every function the header
-declares, and rejects bad arguments on the host (nothing is launched).
+"""The C-ABI library loads without a GPU, exports every function the headers
+(include/*.h) declare, and rejects bad arguments on the host (nothing is
+launched).
 
 Failure handling is forced from the host: every call below fails validation
 before any HIP call, so no GPU is needed.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -12,6 +14,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qgemm.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _lib():
@@ -22,14 +25,17 @@ def _lib():
     return q.load()
 
 
-def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)
+def _declared(headers=None):
+    names = []
+    for h in headers or HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)
+    return names
 
 
 def test_header_declares_the_entry_points():
-    names = set(_declared())
+    names = set(_declared([HEADER]))
     for n in ["quantize_per_token_i8", "quantize_weight_i8_per_channel",
               "quantize_weight_u4_g128", "gemm_w8a8", "gemm_w4a8_g128", "gemm_w4a16_g128",
               "smoothquant_fold", "awq_fold", "apply_smoothing", "qg_status_string",
@@ -42,8 +48,10 @@ def test_header_declares_the_entry_points():
 
 def test_library_exports_every_declared_symbol():
     lib = _lib()
-    for name in _declared():
-        assert hasattr(lib, name), f"{name} declared in qgemm.h but not exported"
+    names = _declared()
+    assert {"qg_peak_stream_read", "qg_peak_mfma", "qg_peak_empty"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in include/*.h but not exported"
     assert lib.qg_abi_version() == 1
 
 
@@ -182,3 +190,32 @@ def test_binding_rejects_host_tensors():
     _lib()
     with pytest.raises(TypeError):
         q.quantize_per_token_i8(torch.zeros(4, 16))
+
+
+def test_peak_probe_validation():
+    """The measurement probes check their arguments on the host too."""
+    lib = _lib()
+    NULL, SHAPE, ALIGN, ARG = 1, 2, 3, 6
+    r = lib.qg_peak_stream_read
+    r.argtypes = [P, ctypes.c_int64, P, P]
+    assert r(None, 1024, A, None) == NULL
+    assert r(A, 0, A, None) == SHAPE
+    assert r(A, (1 << 31) + 1, A, None) == SHAPE
+    assert r(MIS, 1024, A, None) == ALIGN
+    sink = lib.qg_peak_stream_read_sink
+    sink.argtypes, sink.restype = [ctypes.c_int64], ctypes.c_int64
+    assert sink(0) == 0
+    # at most 256 workgroups of 8 waves: 24 MB needs 12 KB per wave
+    assert sink(24260672) == 8 * ((24260672 + 8 * 12 * 1024 - 1) // (8 * 12 * 1024))
+    assert sink(24260672) <= 256 * 8
+    m = lib.qg_peak_mfma
+    m.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, P, P, P]
+    assert m(0, 10, 4, None, A, None) == NULL
+    assert m(4, 10, 4, A, A, None) == ARG
+    assert m(0, 0, 4, A, A, None) == SHAPE
+    assert m(0, 10, 65536, A, A, None) == SHAPE
+    ops = lib.qg_peak_mfma_ops
+    ops.argtypes, ops.restype = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64], ctypes.c_int64
+    assert ops(0, 1, 1) == 16 * 2 * 32 * 32 * 32
+    assert ops(2, 3, 5) == 3 * 5 * 16 * 2 * 32 * 32 * 16
+    assert ops(9, 1, 1) == -1

@@ -91,9 +91,10 @@ def test_w8a8_power_of_two_scales_bitwise(M, N, K):
     np.testing.assert_array_equal(out_f64(y), oracle.gemm_w8a8(xq, sx, wq, sw))
 
 
-def test_w8a8_prefill_full_sampled():
-    """4096 x 11008 x 4096 in the launch configuration the benchmark times;
-    the oracle checks 48 sampled rows (all columns), including the last tile."""
+def test_w8a8_prefill_full():
+    """4096 x 11008 x 4096 in the launch configuration the benchmark times,
+    full-range random codes: every int32 accumulator and every bf16 output
+    against the oracle (float64 BLAS on integer operands is exact here)."""
     M, N, K = 4096, 11008, 4096
     g = torch.Generator(device="cuda").manual_seed(1234)
     xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
@@ -102,12 +103,11 @@ def test_w8a8_prefill_full_sampled():
     sw = torch.rand(N, device="cuda", generator=g) * 1e-3 + 1e-5
     acc = qg.gemm_w8a8(xq, None, wq, None, out_dtype=torch.int32)
     y = qg.gemm_w8a8(xq, sx, wq, sw, out_dtype=torch.bfloat16)
-    rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1, M - 2, 255, 256]]))
     xq_n, wq_n = to_np(xq), to_np(wq)
-    ref = oracle.gemm_w8a8_acc(xq_n[rows], wq_n)
-    np.testing.assert_array_equal(to_np(acc)[rows], ref)
-    yref = oracle.gemm_w8a8(xq_n[rows], to_np(sx)[rows], wq_n, to_np(sw))
-    assert_close(out_f64(y)[rows], yref, "bf16", what="prefill bf16")
+    ref = oracle.gemm_w8a8_acc(xq_n, wq_n)
+    np.testing.assert_array_equal(to_np(acc), ref)
+    yref = oracle.gemm_w8a8(xq_n, to_np(sx), wq_n, to_np(sw))
+    assert_close(out_f64(y), yref, "bf16", what="prefill bf16")
     # run-to-run determinism
     y2 = qg.gemm_w8a8(xq, sx, wq, sw, out_dtype=torch.bfloat16)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))

@@ -9,14 +9,23 @@ A result that sums terms of both signs in binary32 (the group sums of W4A8
 and W4A16) may lose relative accuracy near zero; such an output also passes if
   |y - y_exact| <= ulp_out(y_exact) + n * 2^-24 * B,
 with B the sum of the magnitudes of the terms and n the number of binary32
-roundings that can touch the sum (derived per kernel in the test).  The
-tests report how many outputs needed that floor.
+roundings that can touch the sum (derived per kernel in the test).
+
+For fp32 outputs the floor is the working bar whenever |y_exact| is below
+about n / 168 of B (1e-5 is 168 units of 2^-24), which is most outputs of a
+sum over tens of groups: that is what binary32 summation can promise.  For
+bf16 / fp16 outputs one ulp is 2^-8 / 2^-11 relative, so the floor should
+decide only outputs near zero: at most FLOOR_FRAC_16 of them may pass through
+it alone.  Every check is logged in FLOOR_LOG, and the test session prints
+the counts at its end (tests/conftest.py).
 """
 from __future__ import annotations
 
 import numpy as np
 
 _FMT = {"bf16": (8, -126), "f16": (11, -14)}
+FLOOR_FRAC_16 = 0.01   # bf16 / fp16 outputs that may pass through the floor alone
+FLOOR_LOG = []         # (what, fmt, outputs passing only via the floor, outputs checked)
 
 
 def ulp(y_exact: np.ndarray, fmt: str) -> np.ndarray:
@@ -45,8 +54,14 @@ def check(y, y_exact, fmt: str, floor=None):
     return ok, int(np.count_nonzero(ok & ~base))
 
 
-def assert_close(y, y_exact, fmt: str, floor=None, what: str = ""):
+def assert_close(y, y_exact, fmt: str, floor=None, what: str = "", max_floor_frac=None):
     ok, via_floor = check(y, y_exact, fmt, floor)
+    if floor is not None:
+        FLOOR_LOG.append((what, fmt, via_floor, int(np.size(y_exact))))
+        lim = max_floor_frac if max_floor_frac is not None else (None if fmt == "f32" else FLOOR_FRAC_16)
+        if lim is not None and via_floor > lim * np.size(y_exact):
+            raise AssertionError(f"{what}: {via_floor} of {np.size(y_exact)} {fmt} outputs pass only "
+                                 f"through the cancellation floor (limit {lim:.2%})")
     if not ok.all():
         idx = np.argwhere(~ok)[:5]
         yy = np.asarray(y, np.float64)
