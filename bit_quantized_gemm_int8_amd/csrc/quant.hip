@@ -151,11 +151,102 @@ __global__ __launch_bounds__(NT) void k_quant_per_token(const void* __restrict__
   }
 }
 
+// Many rows (prefill): one wave per row, four rows per workgroup.  Lane l
+// holds bytes 1024 c + 16 l of its row for c < NC -- every load of the row
+// in flight at once, each instruction a whole kilobyte -- then the row's
+// maximum is a DPP reduction inside the wave (no LDS, no barrier), and the
+// codes of each 16-byte chunk leave as one 8-byte (16-bit input) or 4-byte
+// (fp32) store, a whole 512 or 256 bytes per instruction.  Chunks past the
+// row read zeros through the buffer resource and their stores fall outside
+// the codes' resource.  The codes are those of k_quant_per_token: the same
+// scale, reciprocal and sym_code_t.
+typedef int v2i_ __attribute__((ext_vector_type(2)));
+
+template <int DT, int NC>
+__global__ __launch_bounds__(256) void k_quant_rows_wave(const void* __restrict__ x, int64_t M,
+                                                         int64_t K, int8_t* __restrict__ xq,
+                                                         float* __restrict__ xs) {
+  constexpr int E = esize<DT>(), VPC = 16 / E;   // input bytes per element, values per chunk
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;   // wave-uniform
+  const rsrc_t xr = make_rsrc(reinterpret_cast<const char*>(x) + row * K * E, (u32)(K * E));
+  const rsrc_t qr = make_rsrc(xq + row * K, (u32)K);
+  v4i raw[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) raw[c] = bld16(xr, (u32)(1024 * c + 16 * lane));
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const u32 u = (u32)raw[c][e];
+      if constexpr (DT == F32) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(u)));
+      } else if constexpr (DT == BF16) {
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(u & 0xFFFFu)), fabsf(bf16_bits_to_f32(u >> 16))));
+      } else {
+        amax = fmaxf(amax, fmaxf(fabsf(f16_bits_to_f32((uint16_t)(u & 0xFFFFu))),
+                                 fabsf(f16_bits_to_f32((uint16_t)(u >> 16)))));
+      }
+    }
+  amax = wave_max_nonneg(amax);
+  const float s = amax / 127.f, r = sym_code_r(amax, s);
+  if (lane == 0) xs[row] = amax > 0.f ? s : 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const u32 u = (u32)raw[c][e];
+      if constexpr (DT == F32) {
+        v[e] = __uint_as_float(u);
+      } else if constexpr (DT == BF16) {
+        v[2 * e] = bf16_bits_to_f32(u & 0xFFFFu);
+        v[2 * e + 1] = bf16_bits_to_f32(u >> 16);
+      } else {
+        v[2 * e] = f16_bits_to_f32((uint16_t)(u & 0xFFFFu));
+        v[2 * e + 1] = f16_bits_to_f32((uint16_t)(u >> 16));
+      }
+    }
+    const u32 off = (u32)((1024 * c + 16 * lane) / E);   // first code of the chunk
+    if constexpr (VPC == 8) {
+      const u32 w0 = pack_code_bytes(sym_code_t(v[0], s, r), sym_code_t(v[1], s, r),
+                                     sym_code_t(v[2], s, r), sym_code_t(v[3], s, r));
+      const u32 w1 = pack_code_bytes(sym_code_t(v[4], s, r), sym_code_t(v[5], s, r),
+                                     sym_code_t(v[6], s, r), sym_code_t(v[7], s, r));
+      __builtin_amdgcn_raw_buffer_store_b64(v2i_{(int)w0, (int)w1}, qr, off, 0, 0);
+    } else {
+      const u32 w0 = pack_code_bytes(sym_code_t(v[0], s, r), sym_code_t(v[1], s, r),
+                                     sym_code_t(v[2], s, r), sym_code_t(v[3], s, r));
+      __builtin_amdgcn_raw_buffer_store_b32((int)w0, qr, off, 0, 0);
+    }
+  }
+}
+
+// rows at or above which the one-wave-per-row form runs (enough rows for
+// every CU to hold several waves of it)
+constexpr int64_t kRowsWaveMinM = 1024;
+
+template <int DT>
+static hipError_t quant_rows_wave(const void* x, int64_t M, int64_t K, int8_t* xq, float* xs,
+                                  hipStream_t st) {
+  const int64_t nc = (K * esize<DT>() + 1023) / 1024;
+  const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+  if (nc <= 4) k_quant_rows_wave<DT, 4><<<grid, block, 0, st>>>(x, M, K, xq, xs);
+  else if (nc <= 8) k_quant_rows_wave<DT, 8><<<grid, block, 0, st>>>(x, M, K, xq, xs);
+  else if (nc <= 12) k_quant_rows_wave<DT, 12><<<grid, block, 0, st>>>(x, M, K, xq, xs);
+  else k_quant_rows_wave<DT, 16><<<grid, block, 0, st>>>(x, M, K, xq, xs);   // rows <= 16 KB
+  return hipGetLastError();
+}
+
 template <int DT>
 static hipError_t quant_per_token_dt(const void* x, int64_t M, int64_t K, int8_t* xq, float* xs,
                                      hipStream_t st) {
   const int64_t nch = K / 16;
   const dim3 grid((unsigned)M);
+  if (M >= kRowsWaveMinM && K * esize<DT>() <= 16 * 1024)
+    return quant_rows_wave<DT>(x, M, K, xq, xs, st);
   if (nch <= 256)
     k_quant_per_token<DT, 1, 256><<<grid, 256, 0, st>>>(x, K, xq, xs);
   else if (nch <= 512)

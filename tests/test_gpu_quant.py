@@ -48,6 +48,24 @@ def test_per_token_parity(fmt, M, K):
     _check_per_token(x, fmt)
 
 
+# many rows: the one-wave-per-row form (M >= 1024, rows of at most 16 KB),
+# ragged K (a row's last kilobyte partly past its end), every input format,
+# zero rows and rows with huge and tiny maxima
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("M,K", [(1024, 4096), (1027, 48), (1500, 1040), (2049, 4112), (1024, 16),
+                                 (1030, 8192), (1024, 2064)])
+def test_per_token_many_rows(fmt, M, K):
+    if fmt == "f32" and K > 4096:
+        K = 4096 - 16          # keep rows within 16 KB
+    rng = np.random.default_rng(M * 7 + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, rng.integers(0, K, 2)] *= 40.0
+    x[3] = 0.0                                          # all-zero token
+    x[5] *= 1e-30 if fmt == "f32" else 1e-3             # tiny maximum (subnormal scale for f32)
+    x[7, -1] = 3e4 if fmt != "bf16" else 3e30           # the maximum in the row's last element
+    _check_per_token(x, fmt)
+
+
 def test_per_token_workload_inputs():
     for name in ("w8a8_tiny", "w4a8_ffn_down"):
         wl = by_name(name)

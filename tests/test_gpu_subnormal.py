@@ -85,6 +85,20 @@ def test_per_token_subnormal(fmt, K):
         assert np.sum(np.abs(xo) / np.where(s_ref > 0, s_ref, 1)[:, None] > 127.5) > 0
 
 
+@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [48, 4096])
+def test_per_token_subnormal_many_rows(fmt, K):
+    """The same rows, repeated past 1024 of them: the one-wave-per-row form."""
+    x = np.tile(_rows(2, K, seed=K + 1), (28, 1))
+    xd, xo = _act(x, fmt)
+    print(f"per-token subnormal many rows M={x.shape[0]} K={K} {fmt}", flush=True)
+    xq, xs = qg.quantize_per_token_i8(xd)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_per_token_i8(xo)
+    np.testing.assert_array_equal(to_np(xs), s_ref)
+    np.testing.assert_array_equal(to_np(xq), q_ref)
+
+
 @pytest.mark.parametrize("K", [64, 4096])
 def test_weight_i8_subnormal(K):
     w = _rows(2, K, seed=K).T.copy()              # [K, N]: one subnormal case per column
