@@ -50,7 +50,7 @@ KERNEL_REPLAYS = 5              # replays of a per-kernel graph; the median is r
 KERNEL_SOURCES = {
     "w8a8": ["gemm_w8a8.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w8a8_fq": ["gemm_w8a8_fq.hip", "qg_decode.hpp", "qg_device.hpp"],
-    "w4a8": ["gemm_w4a8.hip", "qg_decode.hpp", "qg_device.hpp"],
+    "w4a8": ["gemm_w4a8.hip", "gemm_w4a8_fused.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a8_outl": ["gemm_w4a8.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a8_sp24": ["gemm_w4a8_sp24.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a16": ["gemm_w4a16.hip", "qg_decode.hpp", "qg_device.hpp"],
@@ -130,22 +130,28 @@ def algorithmic(wl):
 
 
 def fused_step(wl) -> bool:
-    """Whether the workload's step runs the fused quantize + W8A8 kernel: the
-    library's own choice for these sizes, asked of the library (host only)."""
-    if wl.path != "w8a8":
-        return False
+    """Whether the workload's step runs the one-kernel quantize + W8A8 form,
+    or for W4A8 the panel pair (quantize_per_token_i8_panel +
+    gemm_w4a8_g128_panel): the library's own choice for these sizes, asked of
+    the library (host only)."""
     import torch
     import bit_quantized_gemm_int8_amd as qg
+    if wl.path == "w4a8":
+        return qg.quantize_gemm_w4a8_g128_workspace_bytes(wl.M, wl.N, wl.K) > 0
+    if wl.path != "w8a8":
+        return False
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
     return qg.quantize_gemm_w8a8_plan(tdt[wl.x_dtype], wl.M, wl.N, wl.K)
 
 
 def dominant(wl):
     """(algorithmic bytes, ops, source key) of the workload's dominant kernel:
-    the GEMM, or for a fused step the one kernel, which reads the activations
-    and writes their codes and scales but never reads the codes back."""
+    the GEMM (for W4A8 on the panel pair, the panel GEMM: its token operands
+    are the codes, counted once), or for the one-kernel W8A8 form that
+    kernel, which reads the activations and writes their codes and scales
+    but never reads the codes back."""
     gemm, quant, ops = algorithmic(wl)
-    if fused_step(wl):
+    if fused_step(wl) and wl.path == "w8a8":
         return gemm + quant - (wl.M * wl.K + 4 * wl.M), ops, "w8a8_fq"
     return gemm, ops, wl.path
 
@@ -307,13 +313,26 @@ def run_workload(wl, steps, warmup, traffic_db):
             qg.gemm_w4a16_g128(x_in, w[0], w[1], w[2], out_dtype=y.dtype, out=y)
 
     fused = fused_step(wl)
+    ws_bytes = qg.quantize_gemm_w4a8_g128_workspace_bytes(wl.M, wl.N, wl.K) if wl.path == "w4a8" else 0
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
-    def layer(i):   # the W8A8 layer through its one entry point (the library's choice)
+    def layer(i):   # the layer through its one entry point (the library's choice)
         w = copies[i % R]
-        qg.quantize_gemm_w8a8(x_in, w[0], w[1], out_dtype=y.dtype, out=y, xq_out=(xq, xs))
+        if wl.path == "w8a8":
+            qg.quantize_gemm_w8a8(x_in, w[0], w[1], out_dtype=y.dtype, out=y, xq_out=(xq, xs))
+        else:
+            qg.quantize_gemm_w4a8_g128(x_in, w[0], w[1], w[2], out_dtype=y.dtype, out=y,
+                                       xq_out=(xq, xs), workspace=workspace)
+
+    def panel_quant():   # the panel pair's two kernels, each alone
+        qg.quantize_per_token_i8_panel(x_in, panel=workspace, xq_out=(xq, xs))
+
+    def panel_gemm(i):
+        w = copies[i % R]
+        qg.gemm_w4a8_g128_panel(workspace, xs, w[0], w[1], w[2], wl.M, out_dtype=y.dtype, out=y)
 
     def step(i):
-        if wl.path == "w8a8":
+        if wl.path in ("w8a8", "w4a8"):
             layer(i)
             return
         if wl.path != "w4a16":
@@ -334,9 +353,14 @@ def run_workload(wl, steps, warmup, traffic_db):
 
     g_warm = capture(step, max(warmup, 1))
     g_step = capture(step, steps)
-    # the dominant kernel alone: the fused kernel is the whole step
-    g_gemm = capture(layer if fused else gemm, steps)
-    g_quant = capture(lambda i: quant(), steps) if wl.path != "w4a16" and not fused else None
+    # the dominant kernel alone: the one-kernel W8A8 form is the whole step
+    if fused and wl.path == "w4a8":
+        panel_quant()   # the panel the timed GEMMs read
+        g_gemm = capture(panel_gemm, steps)
+        g_quant = capture(lambda i: panel_quant(), steps)
+    else:
+        g_gemm = capture(layer if fused else gemm, steps)
+        g_quant = capture(lambda i: quant(), steps) if wl.path != "w4a16" and not fused else None
 
     # warmup replays, each checked against the eager result (all copies equal)
     for _ in range(2):
@@ -705,6 +729,8 @@ def batch_sweep(steps):
             x = torch.randn((M, K), generator=gen, device=dev).to(tdt[xd])
             xq = torch.empty((M, K), dtype=torch.int8, device=dev)
             xs = torch.empty((M,), dtype=torch.float32, device=dev)
+            wsp = torch.empty(max(qg.quantize_gemm_w4a8_g128_workspace_bytes(M, N, K), 1),
+                              dtype=torch.uint8, device=dev)
             y = torch.empty((M, N), dtype=tdt[xd], device=dev)
             y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
             x16 = x.to(torch.float16)
@@ -717,8 +743,8 @@ def batch_sweep(steps):
                 if path == "w8a8":
                     qg.quantize_gemm_w8a8(x, c[0], c[1], out_dtype=y.dtype, out=y, xq_out=(xq, xs))
                     return
-                qg.quantize_per_token_i8(x, out=(xq, xs))
-                qg.gemm_w4a8_g128(xq, xs, c[0], c[1], c[2], out_dtype=y.dtype, out=y)
+                qg.quantize_gemm_w4a8_g128(x, c[0], c[1], c[2], out_dtype=y.dtype, out=y,
+                                           xq_out=(xq, xs), workspace=wsp)
 
             def dense(i):
                 torch.matmul(x16, copies16[i % R16], out=y16)
@@ -740,7 +766,7 @@ def batch_sweep(steps):
 KERNEL_OF = {
     "w8a8_decode_ffn_up": [("k_w8a8_dec<8,", "unsigned short>")],
     "w8a8_tiny": [("k_w8a8_fq<16,", "float>")],
-    "w4a8_ffn_down": [("k_w4a8_dec<16, 8, 1, false, unsigned short>",)],
+    "w4a8_ffn_down": [("k_w4a8_fdec<16, 3, unsigned short>",)],
     "w4a8_outl_ffn_down": [("k_w4a8_dec<16, 8, 1, true, unsigned short>",)],
     "w4a8_sp24_ffn_down": [("k_w4a8_sp24<unsigned short>",)],
     "w4a16_qkv": [("k_w4a16_dec<1,", "_Float16>"), ("k_w4a16_decILi1E", "DF16_E")],
@@ -750,7 +776,7 @@ KERNEL_OF = {
 # profile file label of each workload's dominant kernel
 KERNEL_LABEL = {
     "w8a8_decode_ffn_up": "gemm_w8a8_dec", "w8a8_tiny": "gemm_w8a8_fq",
-    "w4a8_ffn_down": "gemm_w4a8_dec", "w4a16_qkv": "gemm_w4a16_dec", "w8a8_prefill": "gemm_w8a8_tiled",
+    "w4a8_ffn_down": "gemm_w4a8_panel", "w4a16_qkv": "gemm_w4a16_dec", "w8a8_prefill": "gemm_w8a8_tiled",
     "kv_llama2_7b_4k": "kv_quant_seg", "w4a8_outl_ffn_down": "gemm_w4a8_outl_dec",
     "w4a8_sp24_ffn_down": "gemm_w4a8_sp24",
 }
@@ -882,7 +908,9 @@ def ingest_counters(d):
 STEP_TEXT = {
     "w8a8": lambda h: "quantize_gemm_w8a8: " + ("one fused kernel" if h["fused"] else
                                                   "quantize_per_token_i8 + gemm_w8a8 kernels"),
-    "w4a8": lambda h: "quantize_per_token_i8 + gemm_w4a8_g128",
+    "w4a8": lambda h: "quantize_gemm_w4a8_g128: " + (
+        "quantize_per_token_i8_panel + gemm_w4a8_g128_panel kernels" if h["fused"] else
+        "quantize_per_token_i8 + gemm_w4a8_g128 kernels"),
     "w4a8_outl": lambda h: "quantize_per_token_i8 + gemm_w4a8_g128_outliers",
     "w4a8_sp24": lambda h: "quantize_per_token_i8 + gemm_w4a8_g128_sparse24",
     "w4a16": lambda h: "gemm_w4a16_g128",

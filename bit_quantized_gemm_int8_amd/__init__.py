@@ -13,6 +13,10 @@ Entry points (same names as the C ABI):
   gemm_w8a8(xq, x_scale, wq, w_scale, out_dtype)
   quantize_gemm_w8a8(x, wq, w_scale, out_dtype)  -> (y, xq, x_scale): both steps in one call
   gemm_w4a8_g128(xq, x_scale, wq, w_scale, w_zero, out_dtype)
+  quantize_per_token_i8_panel(x)                -> (panel uint8, xq, x_scale): codes + W4A8 token panel
+  gemm_w4a8_g128_panel(panel, x_scale, wq, w_scale, w_zero, M, out_dtype)
+  quantize_gemm_w4a8_g128(x, wq, w_scale, w_zero, out_dtype) -> (y, xq, x_scale): both steps in one call
+  quantize_gemm_w4a8_g128_workspace_bytes(M, N, K) -> bytes of device workspace that call needs
   gemm_w4a16_g128(x, wq, w_scale, w_zero, out_dtype)
   smoothquant_fold(x_cal, w) / awq_fold(x_cal, w) -> (s f32 [K], w_folded f32 [K,N])
   apply_smoothing(x, s, out_dtype)
@@ -35,7 +39,9 @@ __all__ = [
     "LIB_PATH", "load", "QG_F32", "QG_F16", "QG_BF16", "QG_I32",
     "quantize_per_token_i8", "quantize_weight_i8_per_channel", "quantize_weight_u4_g128",
     "gemm_w8a8", "gemm_w4a8_g128", "gemm_w4a16_g128", "quantize_gemm_w8a8",
-    "quantize_gemm_w8a8_plan",
+    "quantize_gemm_w8a8_plan", "quantize_gemm_w4a8_g128",
+    "quantize_gemm_w4a8_g128_workspace_bytes", "quantize_per_token_i8_panel",
+    "quantize_per_token_i8_panel_bytes", "gemm_w4a8_g128_panel",
     "smoothquant_fold", "awq_fold", "apply_smoothing", "status_string",
     "quantize_kv_i8_segments", "dequantize_kv_i8_segments", "KV_SEGMENT",
     "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
@@ -57,6 +63,10 @@ _SIGNATURES = {
     "quantize_gemm_w8a8": [_vp, _int, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp, _int, _vp],
     "quantize_gemm_w8a8_plan": [_int, _i64, _i64, _i64, _int, _vp],
     "gemm_w4a8_g128": [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
+    "quantize_gemm_w4a8_g128": [_vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp,
+                                _vp, _i64, _vp],
+    "quantize_per_token_i8_panel": [_vp, _int, _i64, _i64, _vp, _vp, _vp, _i64, _vp],
+    "gemm_w4a8_g128_panel": [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
     "gemm_w4a16_g128": [_vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
     "smoothquant_fold": [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp],
     "awq_fold": [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp],
@@ -99,6 +109,10 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int64 if name.endswith(("_sink", "_ops")) else ctypes.c_int
+        lib.quantize_gemm_w4a8_g128_workspace_bytes.argtypes = [_i64, _i64, _i64]
+        lib.quantize_gemm_w4a8_g128_workspace_bytes.restype = ctypes.c_int64
+        lib.quantize_per_token_i8_panel_bytes.argtypes = [_i64, _i64]
+        lib.quantize_per_token_i8_panel_bytes.restype = ctypes.c_int64
         lib.qg_status_string.argtypes = [ctypes.c_int]
         lib.qg_status_string.restype = ctypes.c_char_p
         lib.qg_abi_version.restype = ctypes.c_int
@@ -258,6 +272,85 @@ def gemm_w4a8_g128(xq, x_scale, wq, w_scale, w_zero, out_dtype=torch.bfloat16, o
     _call("gemm_w4a8_g128", pxq, pxs, pwq, pws, pwz, M, N, K, y.data_ptr(),
           _DTYPE_CODE[out_dtype], _stream())
     return y
+
+
+def quantize_per_token_i8_panel_bytes(M: int, K: int) -> int:
+    """Bytes of the W4A8 token panel for M rows of K (0 where unsupported)."""
+    return int(load().quantize_per_token_i8_panel_bytes(M, K))
+
+
+def quantize_per_token_i8_panel(x, panel=None, xq_out=None, write_xq=True):
+    """x [M, K] (f32/f16/bf16, M <= 16, K <= 16384) -> (panel uint8, xq, x_scale):
+    the codes and scales of quantize_per_token_i8 plus the token panel that
+    gemm_w4a8_g128_panel reads.  write_xq=False skips xq (returned as None)."""
+    px = _dev(x, "x", _FLOATS)
+    M, K = _2d(x, "x")
+    dev = x.device
+    need = quantize_per_token_i8_panel_bytes(M, K)
+    if panel is None:
+        panel = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    pp = _dev(panel, "panel", (torch.uint8,), None, dev)
+    xq, xs = xq_out if xq_out is not None else (None, None)
+    xq = _out(xq, (M, K), torch.int8, dev, "xq out") if write_xq else None
+    xs = _out(xs, (M,), torch.float32, dev, "x_scale out")
+    _call("quantize_per_token_i8_panel", px, _DTYPE_CODE[x.dtype], M, K,
+          xq.data_ptr() if xq is not None else None, xs.data_ptr(), pp, panel.numel(), _stream())
+    return panel, xq, xs
+
+
+def gemm_w4a8_g128_panel(panel, x_scale, wq, w_scale, w_zero, M, out_dtype=torch.bfloat16,
+                         out=None):
+    """W4A8 g=128 on a token panel of M rows (quantize_per_token_i8_panel);
+    int32 out_dtype returns per-group acc [M, K/128, N]."""
+    dev = panel.device
+    pp = _dev(panel, "panel", (torch.uint8,), None, dev)
+    N, K8 = _2d(wq, "wq")
+    K = K8 * 8
+    pwq = _dev(wq, "wq", (torch.int32,), (N, K // 8), dev)
+    pwz = _dev(w_zero, "w_zero", (torch.float16,), (N, K // 128), dev)
+    pxs = _opt(x_scale, "x_scale", (torch.float32,), (M,), dev)
+    pws = _opt(w_scale, "w_scale", (torch.float16,), (N, K // 128), dev)
+    shape = (M, K // 128, N) if out_dtype == torch.int32 else (M, N)
+    y = _out(out, shape, out_dtype, dev)
+    _call("gemm_w4a8_g128_panel", pp, panel.numel(), pxs, pwq, pws, pwz, M, N, K, y.data_ptr(),
+          _DTYPE_CODE[out_dtype], _stream())
+    return y
+
+
+def quantize_gemm_w4a8_g128_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Device workspace (bytes) quantize_gemm_w4a8_g128 needs for these sizes
+    (0: it runs the two kernels in sequence and needs none)."""
+    return int(load().quantize_gemm_w4a8_g128_workspace_bytes(M, N, K))
+
+
+def quantize_gemm_w4a8_g128(x, wq, w_scale, w_zero, out_dtype=torch.bfloat16, out=None,
+                            xq_out=None, workspace=None):
+    """x [M, K] (f32/f16/bf16) -> (y, xq int8 [M, K], x_scale f32 [M]):
+    per-token quantization and the W4A8 g=128 product in one call, the same
+    results as quantize_per_token_i8 then gemm_w4a8_g128.  workspace: a
+    contiguous uint8 device tensor of at least
+    quantize_gemm_w4a8_g128_workspace_bytes(M, N, K) bytes, allocated here
+    when None."""
+    px = _dev(x, "x", _FLOATS)
+    M, K = _2d(x, "x")
+    dev = x.device
+    N = _2d(wq, "wq")[0]
+    pwq = _dev(wq, "wq", (torch.int32,), (N, K // 8), dev)
+    pwz = _dev(w_zero, "w_zero", (torch.float16,), (N, K // 128), dev)
+    pws = _opt(w_scale, "w_scale", (torch.float16,), (N, K // 128), dev)
+    shape = (M, K // 128, N) if out_dtype == torch.int32 else (M, N)
+    y = _out(out, shape, out_dtype, dev)
+    xq, xs = xq_out if xq_out is not None else (None, None)
+    xq = _out(xq, (M, K), torch.int8, dev, "xq out")
+    xs = _out(xs, (M,), torch.float32, dev, "x_scale out")
+    need = quantize_gemm_w4a8_g128_workspace_bytes(M, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    pw = _dev(workspace, "workspace", (torch.uint8,), None, dev)
+    _call("quantize_gemm_w4a8_g128", px, _DTYPE_CODE[x.dtype], pwq, pws, pwz, M, N, K,
+          y.data_ptr(), _DTYPE_CODE[out_dtype], xq.data_ptr(), xs.data_ptr(), pw,
+          workspace.numel(), _stream())
+    return y, xq, xs
 
 
 def gemm_w4a16_g128(x, wq, w_scale, w_zero, out_dtype=None, out=None):

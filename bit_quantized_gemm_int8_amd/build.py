@@ -18,7 +18,7 @@ OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "quant.hip", "fold.hip", "gemm_w8a8.hip", "gemm_w4a8.hip", "gemm_w4a16.hip",
+SOURCES = ["api.hip", "quant.hip", "fold.hip", "gemm_w8a8.hip", "gemm_w4a8.hip", "gemm_w4a8_fused.hip", "gemm_w4a16.hip",
            "kv.hip", "gemm_w4a8_sp24.hip", "gemm_w8a8_fq.hip", "peaks.hip"]
 
 CFLAGS = [

@@ -155,6 +155,76 @@ qg_status_t gemm_w4a8_g128(const int8_t* xq, const float* x_scale, const int32_t
                                          static_cast<hipStream_t>(stream)));
 }
 
+int64_t quantize_per_token_i8_panel_bytes(int64_t M, int64_t K) {
+  if (check_dims(M, 1, K)) return 0;
+  return qg::panel_bytes(M, K);
+}
+
+qg_status_t quantize_per_token_i8_panel(const void* x, int x_dtype, int64_t M, int64_t K,
+                                        int8_t* xq, float* x_scale, void* panel,
+                                        int64_t panel_bytes, void* stream) {
+  if (qg_status_t s = check_dims(M, 1, K)) return s;
+  if (!is_float_dtype(x_dtype)) return QG_ERR_DTYPE;
+  if (M == 0) return QG_OK;
+  const int64_t need = qg::panel_bytes(M, K);
+  if (need == 0 || panel_bytes < need) return QG_ERR_SHAPE;
+  if (!x || !x_scale || !panel) return QG_ERR_NULL;
+  if (!aligned16(x) || (xq && !aligned16(xq)) || !aligned16(panel)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_quant_panel(x, x_dtype, M, K, xq, x_scale, panel,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+qg_status_t gemm_w4a8_g128_panel(const void* panel, int64_t panel_bytes, const float* x_scale,
+                                 const int32_t* wq, const uint16_t* w_scale_f16,
+                                 const uint16_t* w_zero_f16, int64_t M, int64_t N, int64_t K,
+                                 void* y, int y_dtype, void* stream) {
+  if (qg_status_t s = check_dims(M, N, K)) return s;
+  if (!is_float_dtype(y_dtype) && y_dtype != QG_I32) return QG_ERR_DTYPE;
+  if (M == 0 || N == 0) return QG_OK;
+  const int64_t need = qg::panel_bytes(M, K);
+  if (need == 0 || panel_bytes < need || !qg::gemm_w4a8_panel_ok(M, N, K)) return QG_ERR_SHAPE;
+  if (y_dtype == QG_I32 && M * (K / 128) * N > kMaxDim) return QG_ERR_SHAPE;
+  if (!panel || !wq || !w_zero_f16 || !y) return QG_ERR_NULL;
+  if (y_dtype != QG_I32 && (!x_scale || !w_scale_f16)) return QG_ERR_NULL;
+  if (!aligned16(panel) || !aligned16(wq)) return QG_ERR_ALIGN;
+  const uint16_t* ws = w_scale_f16 ? w_scale_f16 : w_zero_f16;   // I32: values unused
+  return hip_status(qg::launch_gemm_w4a8_panel(panel, x_scale, wq, ws, w_zero_f16, M, N, K, y,
+                                               y_dtype, static_cast<hipStream_t>(stream)));
+}
+
+int64_t quantize_gemm_w4a8_g128_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (check_dims(M, N, K) || K % 128 || K / 128 > kMaxGroups) return 0;
+  return qg::quantize_gemm_w4a8_workspace(M, N, K);
+}
+
+qg_status_t quantize_gemm_w4a8_g128(const void* x, int x_dtype, const int32_t* wq,
+                                    const uint16_t* w_scale_f16, const uint16_t* w_zero_f16,
+                                    int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                                    int8_t* xq, float* x_scale, void* workspace,
+                                    int64_t workspace_bytes, void* stream) {
+  if (qg_status_t s = check_dims(M, N, K)) return s;
+  if (K % 128 || K / 128 > kMaxGroups) return QG_ERR_SHAPE;
+  if (y_dtype == QG_I32 && M * (K / 128) * N > kMaxDim) return QG_ERR_SHAPE;
+  if (!is_float_dtype(x_dtype)) return QG_ERR_DTYPE;
+  if (!is_float_dtype(y_dtype) && y_dtype != QG_I32) return QG_ERR_DTYPE;
+  if (workspace_bytes < 0) return QG_ERR_SHAPE;
+  if (M == 0) return QG_OK;
+  const int64_t need = N > 0 ? qg::quantize_gemm_w4a8_workspace(M, N, K) : 0;
+  if (workspace_bytes < need) return QG_ERR_SHAPE;
+  if (!x || !xq || !x_scale) return QG_ERR_NULL;
+  if (N > 0 && (!wq || !w_zero_f16 || !y || (y_dtype != QG_I32 && !w_scale_f16)))
+    return QG_ERR_NULL;
+  if (need > 0 && !workspace) return QG_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xq) || (N > 0 && !aligned16(wq)) ||
+      (need > 0 && !aligned16(workspace)))
+    return QG_ERR_ALIGN;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (N == 0) return hip_status(qg::launch_quant_per_token(x, x_dtype, M, K, xq, x_scale, st));
+  const uint16_t* ws = w_scale_f16 ? w_scale_f16 : w_zero_f16;   // I32: values unused
+  return hip_status(qg::launch_quantize_gemm_w4a8(x, x_dtype, wq, ws, w_zero_f16, M, N, K, y,
+                                                  y_dtype, xq, x_scale, workspace, st));
+}
+
 qg_status_t quantize_weight_u4_g128_outliers(const float* w, int64_t K, int64_t N, int32_t* wq,
                                              uint16_t* w_scale_f16, uint16_t* w_zero_f16,
                                              uint64_t* w_out_rec, float* w_out_scale,

@@ -1,0 +1,453 @@
+// Per-token int8 quantization feeding the W4A8 GEMM through a token panel,
+// for decode (M <= 16 token rows): the panel quantizer, the panel GEMM and
+// the call that runs both.  「LLM推理降本五要素」 §2.2 (W4A8, group size 128,
+// per-group scale and zero point); 「第4章：量化」 §1.1-1.3 (per-token
+// symmetric codes, x_hat = (x_int - z) s) and §3.5 (dequantize inside the
+// GEMM).
+//
+// The plain W4A8 kernel takes row-major codes, so each of its workgroups
+// re-reads the token rows as half-used lines, permutes their bytes into the
+// unpack order and forms the per-group token sums with extra matrix-core
+// instructions -- all of it repeated by every workgroup of the layer.  Here
+// the quantizer does that once: besides the codes and scales it writes
+//   * a token panel: the codes of group g, half h (k = 128 g + 16 h ...) in
+//     MFMA operand order, panel[g][h][j][r] = the 16 codes of row r at
+//     k = 128 g + 32 j + 16 h + [0, 16), bytes permuted to the order in which
+//     the packed weights unpack (even k of each 8 first, then odd k), so a
+//     wave reads one operand as one contiguous kilobyte (whole lines);
+//   * the token sums sums[g][r] = sum_{k in g} xq[r, k] (exact int32), which
+//     carry the zero point: acc = sum xq q - z sum xq.
+// Both live in device memory the caller provides; one panel can feed several
+// GEMMs of the same input (the projections that share a layer's input).
+//
+// The GEMM streams each 16-row weight block with buffer-to-LDS DMA: every
+// unit (16 rows x 128 bytes = two groups) of a wave's run is requested at
+// once, each unit as two whole-line loads (8 rows x 128 B) landing in an
+// XOR-swizzled 2 KB slot, from which the MFMA fragments are read without bank
+// conflicts.  The block's scales and zero points are staged in LDS *before*
+// the weight requests go out: staged after, their few loads waited in the
+// same memory queues as the whole weight stream and held every wave at the
+// staging barrier until the stream had nearly finished (per-wave timestamps
+// on MI355X: barrier at ~7 us of a ~10 us kernel).  A wave whose run is one
+// unit shorter than its ring repeats its last unit's loads (cache hits) with
+// a zero scale instead of issuing out-of-range loads, which measured slow.
+#include "qg_decode.hpp"
+#include "qg_device.hpp"
+#include "qg_launch.hpp"
+#include "qg_quant.hpp"
+
+namespace qg {
+
+namespace {
+
+// bytes [b0..b7] of (lo, hi) -> [b0 b2 b4 b6 | b1 b3 b5 b7]: the order in
+// which w & 0x0F0F0F0F, (w >> 4) & 0x0F0F0F0F unpack 8 codes of a word
+__device__ __forceinline__ v4i panel_order16(v4i x) {
+  v4i r;
+  r[0] = (int)__builtin_amdgcn_perm((u32)x[1], (u32)x[0], 0x06040200u);
+  r[1] = (int)__builtin_amdgcn_perm((u32)x[1], (u32)x[0], 0x07050301u);
+  r[2] = (int)__builtin_amdgcn_perm((u32)x[3], (u32)x[2], 0x06040200u);
+  r[3] = (int)__builtin_amdgcn_perm((u32)x[3], (u32)x[2], 0x07050301u);
+  return r;
+}
+
+__device__ __forceinline__ v4i unpack_pair(u32 w0, u32 w1) {
+  return v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
+             (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+}
+
+// sum of the 16 signed bytes of v (exact)
+__device__ __forceinline__ int byte_sum16(v4i v) {
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_sdot4(v[i], 0x01010101, s, false);
+  return s;
+}
+
+// s_waitcnt vmcnt(n) for n known once the caller's loop is unrolled
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define QG_WAITVM(i) case i: asm volatile("s_waitcnt vmcnt(" #i ")" ::: "memory"); break;
+    QG_WAITVM(0) QG_WAITVM(1) QG_WAITVM(2) QG_WAITVM(3) QG_WAITVM(4) QG_WAITVM(5) QG_WAITVM(6)
+    QG_WAITVM(7) QG_WAITVM(8) QG_WAITVM(9) QG_WAITVM(10) QG_WAITVM(11) QG_WAITVM(12)
+    QG_WAITVM(13) QG_WAITVM(14) QG_WAITVM(15) QG_WAITVM(16) QG_WAITVM(17) QG_WAITVM(18)
+    QG_WAITVM(19) QG_WAITVM(20) QG_WAITVM(21) QG_WAITVM(22) QG_WAITVM(23) QG_WAITVM(24)
+    QG_WAITVM(25) QG_WAITVM(26) QG_WAITVM(27) QG_WAITVM(28) QG_WAITVM(29) QG_WAITVM(30)
+    QG_WAITVM(31) QG_WAITVM(32)
+#undef QG_WAITVM
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+#define QG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// 16-byte buffer load of every lane straight into LDS at lds + 16 lane (lds
+// wave-uniform), non-temporal: the weights are read once per call
+__device__ __forceinline__ void dma16(rsrc_t r, int8_t* lds, u32 voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, QG_LDS(lds), 16, voff, 0, 0, kAuxNonTemporal);
+}
+
+}  // namespace
+
+// Panel layout (both kernels): panel[g][h][j][r], 16 bytes each, r < MR
+// (MR = M rounded up to 1, 2, 4, 8 or 16), then the token sums sums[g][16]
+// int32 at byte offset 2048 G: G (2048 + 64) bytes whatever M.
+constexpr int kPanelRows = 16;
+
+// ---------------------------------------------------------------------------
+// Quantizer: one workgroup of NT threads per panel row (MR of them), the row
+// in registers.  Rows < M get the codes and scales of k_quant_per_token (same
+// loads, scale, reciprocal and sym_code_t) and are written to xq (unless it
+// is NULL), x_scale, the panel and the sums; rows M..MR-1 write zero codes
+// and sums to the panel only (workgroup 0 also zeroes sum rows MR..15), so
+// that every byte of the panel is defined.
+// ---------------------------------------------------------------------------
+template <int DT, int CH, int NT>
+__global__ __launch_bounds__(NT) void k_quant_panel(const void* __restrict__ x, int M, int64_t K,
+                                                    int MR, int8_t* __restrict__ xq,
+                                                    float* __restrict__ xs,
+                                                    int8_t* __restrict__ panel, int* __restrict__ sums) {
+  __shared__ float red[NT / kWave];
+  const int row = blockIdx.x;
+  const bool real = row < M;
+  const char* xr = reinterpret_cast<const char*>(x) + (real ? (int64_t)row * K * esize<DT>() : 0);
+  const int nch = (int)(K >> 4);
+  const rsrc_t rr = make_rsrc(xr, (uint32_t)(K * esize<DT>()));
+  v4i raw[CH][4];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int idx = threadIdx.x + c * NT;
+    load_chunk16_rs<DT>(rr, real && idx < nch, idx, raw[c]);
+  }
+  float v[CH][16];
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    widen16<DT>(raw[c], v[c]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[c][e]));   // zeros past the end
+  }
+  amax = block_max_nonneg_once<NT>(amax, red);
+  const float s = amax / 127.f, r = sym_code_r(amax, s);
+  if (real && threadIdx.x == 0) xs[row] = amax > 0.f ? s : 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int idx = threadIdx.x + c * NT;   // idx % 8 == threadIdx.x % 8 (NT % 8 == 0)
+    const v4i code = codes16(v[c], s, r);
+    // the 8 chunks of a group sit on 8 consecutive lanes (K % 128 == 0)
+    int t = idx < nch ? byte_sum16(code) : 0;
+    t += __shfl_xor(t, 1, kWave);
+    t += __shfl_xor(t, 2, kWave);
+    t += __shfl_xor(t, 4, kWave);
+    if (idx < nch) {
+      if (real && xq) st16(xq + (int64_t)row * K + (int64_t)idx * 16, code);
+      const int g = idx >> 3, j = (idx & 7) >> 1, h = idx & 1;
+      st16(panel + ((((int64_t)g * 2 + h) * 4 + j) * MR + row) * 16, panel_order16(code));
+      if ((idx & 7) == 0) {
+        sums[g * kPanelRows + row] = t;
+        if (row == 0)   // sum rows past the panel rows: zeros too
+          for (int rr = MR; rr < kPanelRows; ++rr) sums[g * kPanelRows + rr] = 0;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM on the panel: one workgroup per 16-row weight block, WAVES waves each
+// owning a contiguous run of units, every unit of the run requested at once
+// (RING >= the longest run).  I32 output: the per-group accumulators.
+// ---------------------------------------------------------------------------
+constexpr int kFdecEpt = 2;   // scale/zero elements per thread: 16 G <= 64 WAVES kFdecEpt
+
+template <int WAVES, int RING, typename OutT>
+__global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
+    const int8_t* __restrict__ panel, const int* __restrict__ tsum, const float* __restrict__ xs,
+    const int32_t* __restrict__ wq, const uint16_t* __restrict__ wscale,
+    const uint16_t* __restrict__ wzero, int M, int MR, int N, int K, OutT* __restrict__ y) {
+  constexpr bool kI32 = __is_same(OutT, int32_t);
+  constexpr int PU = 8;   // loads per unit: 2 weight DMAs, 4 token fragments, 2 token sums
+  static_assert(PU * RING <= 32, "vmcnt budget of wait_vmcnt");
+  extern __shared__ __attribute__((aligned(16))) u32 smem[];
+  __shared__ v4f red[kI32 ? 1 : WAVES][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int n_base = blockIdx.x * 16;
+  const int G = K >> 7, RB = K >> 1;
+  const int units = (RB + kUnitBytes - 1) / kUnitBytes;
+  // the launcher guarantees WAVES <= units: every run holds at least one unit
+  const int ub = (int)((int64_t)units * wave / WAVES), ue = (int)((int64_t)units * (wave + 1) / WAVES);
+  const int szp = sz_pitch(G);
+  u32* szl = smem;
+  int8_t* ring = reinterpret_cast<int8_t*>(smem + ((16 * szp + 3) & ~3)) + wave * RING * 2 * 1024;
+
+  const int rows_n = min(16, N - n_base);
+  const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * (K >> 3), (u32)(rows_n * RB));
+  const rsrc_t xr = make_rsrc(panel, (u32)(G * 128 * MR));
+  const rsrc_t tr = make_rsrc(tsum, (u32)(G * 64));
+  const u32 xoff = r < MR ? (u32)((j * MR + r) * 16) : kOOB;   // rows >= MR: zero tokens
+
+  // 1. scales and zero points of the block into LDS, before any weight load
+  const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  uint16_t s16[kFdecEpt], z16[kFdecEpt];
+#pragma unroll
+  for (int e = 0; e < kFdecEpt; ++e) {
+    const int el = tid + e * 64 * WAVES;
+    s16[e] = bld2(sr, el < 16 * G ? (u32)(2 * el) : kOOB);
+    z16[e] = bld2(zr, el < 16 * G ? (u32)(2 * el) : kOOB);
+  }
+  float sx[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!kI32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * j + i;
+      sx[i] = xs[m < M ? m : M - 1];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kFdecEpt; ++e) {
+    const int el = tid + e * 64 * WAVES;
+    if (el < 16 * G) {
+      const int row = el / G;
+      szl[row * szp + (el - row * G)] = (u32)s16[e] | ((u32)z16[e] << 16);
+    }
+  }
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. every unit of the run: two whole-line DMAs (rows 8h..8h+7, lane l:
+  // row 8h + l/8, chunk (l % 8) ^ f(row)), four token fragments, two sums
+  v4i tk[RING][2][2], ts[RING][2];
+#pragma unroll
+  for (int i = 0; i < RING; ++i) {
+    const int q = min(ub + i, ue - 1);   // past the run: the last unit again
+    int8_t* dst = ring + i * 2048;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * h + (lane >> 3);
+      const int ch = (lane & 7) ^ ((row >> 1) & 7);
+      const u32 o = 128 * q + 16 * ch < RB ? (u32)(row * RB + 128 * q + 16 * ch) : kOOB;
+      dma16(wr, dst + 1024 * h, o);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int g = 2 * q + s;   // g == G (odd G): past both resources, zeros
+#pragma unroll
+      for (int h = 0; h < 2; ++h) tk[i][s][h] = bld16(xr, xoff + (u32)((g * 2 + h) * 64 * MR));
+      ts[i][s] = bld16(tr, (u32)(g * 64 + 16 * j));
+    }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. consume the units in issue order
+  const u32* szrow = szl + r * szp;
+  int rsl[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) rsl[s] = r * 128 + (((4 * s + j) ^ ((r >> 1) & 7)) << 4);
+  v4f yacc = {0.f, 0.f, 0.f, 0.f};
+  const int n = n_base + r;
+#pragma unroll
+  for (int i = 0; i < RING; ++i) {
+    const bool live = ub + i < ue;
+    const int q = min(ub + i, ue - 1);
+    wait_vmcnt(PU * (RING - 1 - i));
+    const int8_t* slot = ring + i * 2048;
+    const v4i f0 = *reinterpret_cast<const v4i*>(slot + rsl[0]);
+    const v4i f1 = *reinterpret_cast<const v4i*>(slot + rsl[1]);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const v4i f = s ? f1 : f0;
+      const int g = 2 * q + s;
+      const bool gin = live && g < G;
+      const u32 szw = szrow[min(g, G - 1)];
+      const int z = (int)f16_bits_to_f32((uint16_t)(szw >> 16));
+      v4i acc;   // |z| <= 15, |token sum| <= 128 * 127: exact 24-bit products
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __mul24(-z, ts[i][s][e]);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(tk[i][s][0], unpack_pair((u32)f[0], (u32)f[1]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(tk[i][s][1], unpack_pair((u32)f[2], (u32)f[3]), acc, 0, 0, 0);
+      if constexpr (kI32) {
+        if (gin && n < N) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = 4 * j + e;
+            if (m < M) y[((int64_t)m * G + g) * N + n] = acc[e];
+          }
+        }
+      } else {
+        const float sc = gin ? f16_bits_to_f32((uint16_t)(szw & 0xFFFFu)) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yacc[e] = __builtin_fmaf(sc, (float)acc[e], yacc[e]);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (!kI32) {
+    red[wave][lane] = yacc;
+    __syncthreads();
+    if (tid < 64 && n < N) {
+      v4f sum = red[0][lane];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 4 * j + e;
+        if (m < M) y[(int64_t)m * N + n] = Out<OutT>::cvt(sum[e] * sx[e]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kPanelMaxK = 16384;   // 64 units of 128 weight bytes: 16 waves x ring 4
+constexpr int kMaxRing = 4;
+
+// Panel rows for M token rows: M rounded up to 1, 2, 4, 8 or 16 (the quantizer
+// and the GEMM both derive it from M).
+int panel_rows(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+
+bool panel_shape(int64_t M, int64_t K) {
+  return M >= 1 && M <= kPanelRows && K >= 128 && K % 128 == 0 && K <= kPanelMaxK;
+}
+
+struct GemmPlan {
+  bool ok = false;
+  int waves = 0, ring = 0;
+  size_t lds = 0;
+};
+
+// Launch shape of the panel GEMM: 16 waves per workgroup while the 16-row
+// blocks fit in one workgroup per CU (256), else 8 (more workgroups resident
+// per CU), 16 again if 8 would need a ring deeper than 4; never more waves
+// than units, so that every run holds at least one.
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+  GemmPlan p;
+  if (!panel_shape(M, K) || N < 1) return p;
+  const int64_t G = K / 128, units = (K / 2 + kUnitBytes - 1) / kUnitBytes;
+  const int64_t nblocks = (N + 15) / 16;
+  int waves = nblocks <= 256 ? 16 : 8;
+  if ((units + waves - 1) / waves > kMaxRing) waves = 16;
+  while (waves > 1 && waves > units) waves /= 2;
+  const int ring = (int)((units + waves - 1) / waves);
+  if (ring > kMaxRing || 16 * G > (int64_t)64 * waves * kFdecEpt) return p;
+  p.lds = (size_t)((16 * sz_pitch((int)G) + 3) & ~3) * 4 + (size_t)waves * ring * 2048;
+  if (p.lds + (size_t)waves * 64 * sizeof(v4f) > 160 * 1024) return p;
+  p.ok = true;
+  p.waves = waves;
+  p.ring = ring;
+  return p;
+}
+
+// When quantize_gemm_w4a8 takes the panel path (measured on MI355X against
+// the per-token quantizer + plain W4A8 kernel: 16 rows of K = 11008,
+// N = 4096 and of K = 4096, N = 11008 12-20% faster, one row of K = 4096,
+// N = 12288 12% faster; one row of K = 11008, N = 4096 slower, so one row
+// on at most 256 weight blocks keeps the plain kernel).
+bool use_panel(int64_t M, int64_t N, int64_t K) {
+  return plan_gemm(M, N, K).ok && !(M == 1 && (N + 15) / 16 <= 256);
+}
+
+template <int DT>
+hipError_t quant_panel_dt(const void* x, int M, int64_t K, int8_t* xq, float* xs, int8_t* panel,
+                          int* sums, hipStream_t st) {
+  const int64_t nch = K / 16;   // K <= 16384: at most 1024 chunks
+  const int MR = panel_rows(M);
+  const dim3 grid((unsigned)MR);
+  if (nch <= 256)
+    k_quant_panel<DT, 1, 256><<<grid, 256, 0, st>>>(x, M, K, MR, xq, xs, panel, sums);
+  else if (nch <= 512)
+    k_quant_panel<DT, 1, 512><<<grid, 512, 0, st>>>(x, M, K, MR, xq, xs, panel, sums);
+  else
+    k_quant_panel<DT, 2, 512><<<grid, 512, 0, st>>>(x, M, K, MR, xq, xs, panel, sums);
+  return hipGetLastError();
+}
+
+template <int WAVES, typename OutT>
+void fdec_ring(int ring, const int8_t* panel, const int* sums, const float* xs, const int32_t* wq,
+               const uint16_t* ws, const uint16_t* wz, int M, int MR, int N, int K, OutT* y,
+               size_t lds, hipStream_t st) {
+  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
+  switch (ring) {
+    case 1: k_w4a8_fdec<WAVES, 1, OutT><<<grid, block, lds, st>>>(panel, sums, xs, wq, ws, wz, M, MR, N, K, y); break;
+    case 2: k_w4a8_fdec<WAVES, 2, OutT><<<grid, block, lds, st>>>(panel, sums, xs, wq, ws, wz, M, MR, N, K, y); break;
+    case 3: k_w4a8_fdec<WAVES, 3, OutT><<<grid, block, lds, st>>>(panel, sums, xs, wq, ws, wz, M, MR, N, K, y); break;
+    default: k_w4a8_fdec<WAVES, 4, OutT><<<grid, block, lds, st>>>(panel, sums, xs, wq, ws, wz, M, MR, N, K, y); break;
+  }
+}
+
+template <typename OutT>
+hipError_t fdec_t(const GemmPlan& p, const int8_t* panel, const int* sums, const float* xs,
+                  const int32_t* wq, const uint16_t* ws, const uint16_t* wz, int M, int N, int K,
+                  OutT* y, hipStream_t st) {
+  const int MR = panel_rows(M);
+  switch (p.waves) {
+    case 16: fdec_ring<16, OutT>(p.ring, panel, sums, xs, wq, ws, wz, M, MR, N, K, y, p.lds, st); break;
+    case 8: fdec_ring<8, OutT>(p.ring, panel, sums, xs, wq, ws, wz, M, MR, N, K, y, p.lds, st); break;
+    case 4: fdec_ring<4, OutT>(p.ring, panel, sums, xs, wq, ws, wz, M, MR, N, K, y, p.lds, st); break;
+    case 2: fdec_ring<2, OutT>(p.ring, panel, sums, xs, wq, ws, wz, M, MR, N, K, y, p.lds, st); break;
+    default: fdec_ring<1, OutT>(p.ring, panel, sums, xs, wq, ws, wz, M, MR, N, K, y, p.lds, st); break;
+  }
+  return hipGetLastError();
+}
+
+int* panel_sums(void* panel, int64_t K) {
+  return reinterpret_cast<int*>(reinterpret_cast<int8_t*>(panel) + K / 128 * 128 * kPanelRows);
+}
+
+}  // namespace
+
+int64_t panel_bytes(int64_t M, int64_t K) {
+  return panel_shape(M, K) ? K / 128 * (128 * kPanelRows + 4 * kPanelRows) : 0;
+}
+
+bool gemm_w4a8_panel_ok(int64_t M, int64_t N, int64_t K) { return plan_gemm(M, N, K).ok; }
+
+int64_t quantize_gemm_w4a8_workspace(int64_t M, int64_t N, int64_t K) {
+  return use_panel(M, N, K) ? panel_bytes(M, K) : 0;
+}
+
+hipError_t launch_quant_panel(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* xq,
+                              float* xs, void* panel, hipStream_t st) {
+  int8_t* pp = reinterpret_cast<int8_t*>(panel);
+  int* sums = panel_sums(panel, K);
+  switch (x_dtype) {
+    case F32: return quant_panel_dt<F32>(x, (int)M, K, xq, xs, pp, sums, st);
+    case F16: return quant_panel_dt<F16>(x, (int)M, K, xq, xs, pp, sums, st);
+    default: return quant_panel_dt<BF16>(x, (int)M, K, xq, xs, pp, sums, st);
+  }
+}
+
+hipError_t launch_gemm_w4a8_panel(const void* panel, const float* xs, const int32_t* wq,
+                                  const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
+                                  int64_t K, void* y, int y_dtype, hipStream_t st) {
+  const GemmPlan p = plan_gemm(M, N, K);
+  const int8_t* pp = reinterpret_cast<const int8_t*>(panel);
+  const int* sums = panel_sums(const_cast<void*>(panel), K);
+  const int m = (int)M, n = (int)N, k = (int)K;
+  switch (y_dtype) {
+    case F32: return fdec_t<float>(p, pp, sums, xs, wq, ws, wz, m, n, k, (float*)y, st);
+    case F16: return fdec_t<_Float16>(p, pp, sums, xs, wq, ws, wz, m, n, k, (_Float16*)y, st);
+    case BF16: return fdec_t<uint16_t>(p, pp, sums, xs, wq, ws, wz, m, n, k, (uint16_t*)y, st);
+    default: return fdec_t<int32_t>(p, pp, sums, xs, wq, ws, wz, m, n, k, (int32_t*)y, st);
+  }
+}
+
+hipError_t launch_quantize_gemm_w4a8(const void* x, int x_dtype, const int32_t* wq,
+                                     const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
+                                     int64_t K, void* y, int y_dtype, int8_t* xq, float* xs,
+                                     void* workspace, hipStream_t st) {
+  if (!use_panel(M, N, K)) {   // the two kernels in sequence
+    if (hipError_t e = launch_quant_per_token(x, x_dtype, M, K, xq, xs, st)) return e;
+    return launch_gemm_w4a8(xq, xs, wq, ws, wz, M, N, K, y, y_dtype, st);
+  }
+  if (hipError_t e = launch_quant_panel(x, x_dtype, M, K, xq, xs, workspace, st)) return e;
+  return launch_gemm_w4a8_panel(workspace, xs, wq, ws, wz, M, N, K, y, y_dtype, st);
+}
+
+}  // namespace qg

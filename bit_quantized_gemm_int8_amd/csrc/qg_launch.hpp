@@ -30,6 +30,23 @@ bool quantize_gemm_w8a8_fused(int x_dtype, int64_t M, int64_t N, int64_t K, int 
 hipError_t launch_gemm_w4a8(const int8_t* xq, const float* xs, const int32_t* wq,
                             const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
                             int64_t K, void* y, int y_dtype, hipStream_t st);
+// Token panel of per-token int8 codes (operand order + per-group sums) for
+// the W4A8 panel GEMM: its bytes for M rows of K (0 where unsupported), the
+// quantizer writing it (xq may be NULL), the GEMM reading it.
+int64_t panel_bytes(int64_t M, int64_t K);
+bool gemm_w4a8_panel_ok(int64_t M, int64_t N, int64_t K);
+hipError_t launch_quant_panel(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* xq,
+                              float* xs, void* panel, hipStream_t st);
+hipError_t launch_gemm_w4a8_panel(const void* panel, const float* xs, const int32_t* wq,
+                                  const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
+                                  int64_t K, void* y, int y_dtype, hipStream_t st);
+// Quantize + W4A8: the panel pair where quantize_gemm_w4a8_workspace > 0
+// (workspace of that size), else the two plain kernels in sequence.
+hipError_t launch_quantize_gemm_w4a8(const void* x, int x_dtype, const int32_t* wq,
+                                     const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
+                                     int64_t K, void* y, int y_dtype, int8_t* xq, float* xs,
+                                     void* workspace, hipStream_t st);
+int64_t quantize_gemm_w4a8_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_quant_weight_u4_outl(const float* w, int64_t K, int64_t N, int32_t* wq,
                                        uint16_t* ws, uint16_t* wz, uint64_t* rec, float* s8,
                                        hipStream_t st);

@@ -203,6 +203,93 @@ qg_status_t gemm_w4a8_g128(const int8_t* xq, const float* x_scale, const int32_t
                            void* stream);
 
 /*
+ * Per-token int8 quantization that also writes a token panel: the codes laid
+ * out as the W4A8 kernel's matrix-core operands, and their per-group sums.
+ * 「第4章：量化」 §1.1-1.3 (per-token symmetric codes); 「LLM推理降本五要素」
+ * §2.2 (W4A8, group 128, zero point: acc = sum xq q - z sum xq needs the
+ * token sums per group).
+ *   xq, x_scale: as quantize_per_token_i8(x), bit for bit (xq may be NULL:
+ *     then only the panel and x_scale are written).
+ *   panel: device memory of panel_bytes bytes, 16-byte aligned, owned by the
+ *     caller, written (contents on entry ignored).  Layout, for G = K / 128
+ *     and m = M rounded up to 1, 2, 4, 8 or 16: bytes [0, 128 m G) hold
+ *     16-byte entries [g][h][j][r] (g < G, h < 2, j < 4, r < m), entry =
+ *     codes of row r at k = 128 g + 32 j + 16 h + i in the order
+ *     i = 0 2 4 6 1 3 5 7 8 10 12 14 9 11 13 15 (the order in which a packed
+ *     word's eight codes unpack; rows M..m-1: zeros); bytes
+ *     [128 m G, 2048 G) are not used; bytes [2048 G, 2112 G) hold int32
+ *     sums [g][16] (row r of group g: sum of its 128 codes; rows >= M: 0).
+ * 1 <= M <= 16; K a multiple of 128 with K <= 16384 (else QG_ERR_SHAPE);
+ * panel_bytes >= quantize_per_token_i8_panel_bytes(M, K) (else QG_ERR_SHAPE).
+ * M == 0: nothing is done.
+ */
+qg_status_t quantize_per_token_i8_panel(const void* x, int x_dtype, int64_t M, int64_t K,
+                                        int8_t* xq, float* x_scale, void* panel,
+                                        int64_t panel_bytes, void* stream);
+
+/* Bytes of the token panel for M rows of K: (K / 128) * 2112 for the sizes
+ * quantize_per_token_i8_panel takes, else 0.  Host only. */
+int64_t quantize_per_token_i8_panel_bytes(int64_t M, int64_t K);
+
+/*
+ * W4A8 g=128 GEMM reading the token panel instead of xq.
+ * 「LLM推理降本五要素」 §2.2; 「第4章：量化」 §1.1, §3.5.
+ *   acc and y exactly as gemm_w4a8_g128(xq, x_scale, ...) for the xq the
+ *   panel was written from: acc bit for bit, y within the same rounding
+ *   bound (the groups' scaled terms may be summed in another order).
+ * panel: written by quantize_per_token_i8_panel with the same M and K, read.
+ * x_scale [M], wq, w_scale_f16, w_zero_f16, y, y_dtype: as gemm_w4a8_g128.
+ * Sizes as quantize_per_token_i8_panel; N >= 0.
+ * The weight rows of each 16-channel block are streamed into on-chip memory
+ * by direct buffer-to-LDS loads, every load of a wave issued before the
+ * first is used.
+ */
+qg_status_t gemm_w4a8_g128_panel(const void* panel, int64_t panel_bytes, const float* x_scale,
+                                 const int32_t* wq, const uint16_t* w_scale_f16,
+                                 const uint16_t* w_zero_f16, int64_t M, int64_t N, int64_t K,
+                                 void* y, int y_dtype, void* stream);
+
+/*
+ * Per-token int8 quantization of X and the W4A8 g=128 GEMM in one call.
+ * 「第4章：量化」 §1.1-1.3 (per-token symmetric codes), §3.5 (dequantize
+ * inside the GEMM); 「LLM推理降本五要素」 §2.2 (W4A8, group 128, per-group
+ * scale and zero).
+ *   xq, x_scale as quantize_per_token_i8(x), bit for bit; y as
+ *   gemm_w4a8_g128(xq, x_scale, wq, w_scale_f16, w_zero_f16): the int32
+ *   accumulators bit for bit, the scaled outputs within the same rounding
+ *   bound (the groups' scaled terms may be summed in another order).
+ * x [M][K] of x_dtype (QG_F32, QG_F16 or QG_BF16), wq, w_scale_f16,
+ *   w_zero_f16 as gemm_w4a8_g128: read.
+ * y: [M][N] of QG_F32, QG_BF16 or QG_F16, or QG_I32 ([M][K/128][N] int32
+ *    acc[m,g,n]; w_scale_f16 then unused and may be NULL), written.
+ * xq [M][K] int8, x_scale [M] float: written.
+ * workspace: device memory of workspace_bytes bytes (16-byte aligned), owned
+ *   by the caller; contents on entry ignored, on return unspecified.  Calls
+ *   that share a workspace must not overlap.  Its required size is
+ *   quantize_gemm_w4a8_g128_workspace_bytes(M, N, K): where that is > 0 the
+ *   call runs quantize_per_token_i8_panel then gemm_w4a8_g128_panel with the
+ *   workspace as the panel, where it is 0 quantize_per_token_i8 then
+ *   gemm_w4a8_g128, and workspace may be NULL.  Smaller than required:
+ *   QG_ERR_SHAPE; NULL while required: QG_ERR_NULL.
+ * The panel pair runs for 1 <= M <= 16 and K <= 16384, except one token row
+ * on N <= 4096 (measured faster with the plain kernel).
+ * K must be a positive multiple of 128 with K / 128 <= 65535.  N == 0
+ * computes xq and x_scale only.
+ */
+qg_status_t quantize_gemm_w4a8_g128(const void* x, int x_dtype, const int32_t* wq,
+                                    const uint16_t* w_scale_f16, const uint16_t* w_zero_f16,
+                                    int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                                    int8_t* xq, float* x_scale, void* workspace,
+                                    int64_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes quantize_gemm_w4a8_g128 needs for these sizes: 0 when it
+ * runs the two plain kernels (and for sizes it rejects), else
+ * quantize_per_token_i8_panel_bytes(M, K).  Host only.
+ */
+int64_t quantize_gemm_w4a8_g128_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * Group-wise (g = 128) uint4 weights with the largest weights of every group
  * kept in an INT8 side store (offline).
  * 「LLM推理降本五要素」 §2.2 (the top 2% of each group by magnitude stored at

@@ -42,7 +42,8 @@ def test_header_declares_the_entry_points():
               "qg_abi_version", "quantize_kv_i8_segments", "dequantize_kv_i8_segments",
               "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
               "quantize_weight_u4_g128_sparse24", "gemm_w4a8_g128_sparse24",
-              "quantize_gemm_w8a8", "quantize_gemm_w8a8_plan"]:
+              "quantize_gemm_w8a8", "quantize_gemm_w8a8_plan", "quantize_gemm_w4a8_g128",
+              "quantize_gemm_w4a8_g128_workspace_bytes"]:
         assert n in names, n
 
 
@@ -143,6 +144,22 @@ def test_validation_codes():
     assert fq(A, 2, A, A, 8, 16, 4096, A, 2, A, A, 3, None) == 6          # QG_ERR_ARG
     assert fq(A, 2, A, A, 8, 16, 4096, A, 2, A, A, -1, None) == 6
     assert fq(None, 2, None, None, 0, 16, 4096, None, 2, None, None, 2, None) == OK
+    f4 = lib.quantize_gemm_w4a8_g128
+    f4.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P,
+                   ctypes.c_int, P, P, P, ctypes.c_int64, P]
+    ws = 32 * 2112                                                   # 16 x 12288 x 4096 needs it
+    assert f4(A, 2, A, A, A, 16, 12288, 4096, A, 2, A, A, A, ws - 16, None) == SHAPE
+    assert f4(A, 2, A, A, A, 16, 12288, 4096, A, 2, A, A, None, ws, None) == NULL
+    assert f4(A, 2, A, A, A, 16, 12288, 4096, A, 2, A, A, MIS, ws, None) == ALIGN
+    assert f4(A, 2, A, A, A, 16, 12288, 4096, A, 2, A, A, A, -1, None) == SHAPE
+    assert f4(A, 2, A, A, A, 8, 16, 192, A, 2, A, A, A, ws, None) == SHAPE      # K % 128
+    assert f4(A, 3, A, A, A, 8, 16, 4096, A, 2, A, A, A, ws, None) == DTYPE
+    assert f4(A, 2, A, A, A, 8, 16, 4096, A, 9, A, A, A, ws, None) == DTYPE
+    assert f4(A, 2, A, None, A, 8, 16, 4096, A, 2, A, A, A, ws, None) == NULL   # scales unless I32
+    assert f4(A, 2, A, A, None, 8, 16, 4096, A, 2, A, A, A, ws, None) == NULL   # zero points
+    assert f4(A, 2, A, A, A, 8, 16, 4096, A, 2, None, A, A, ws, None) == NULL   # xq
+    assert f4(MIS, 2, A, A, A, 8, 16, 4096, A, 2, A, A, A, ws, None) == ALIGN
+    assert f4(None, 2, None, None, None, 0, 16, 4096, None, 2, None, None, None, 0, None) == OK
     # the g=128 uint4 GEMMs take at most 65535 groups per row, as the quantizer
     g4, g16 = lib.gemm_w4a8_g128, lib.gemm_w4a16_g128
     assert g4(A, A, A, A, A, 1, 16, 65536 * 128, A, 2, None) == SHAPE
@@ -182,6 +199,59 @@ def test_fused_plan_on_the_host():
     assert lib.quantize_gemm_w8a8_plan(2, 4, 16, 128, 5, ctypes.byref(out)) == 6   # ARG
     assert lib.quantize_gemm_w8a8_plan(2, 4, 16, 128, 0, None) == 1                # NULL
     assert out.value == 7                                                         # untouched
+
+
+def test_w4a8_workspace_on_the_host():
+    """quantize_gemm_w4a8_g128_workspace_bytes: (K / 128) x 2112 bytes where
+    the panel pair runs (1..16 rows, K <= 16384, except one row on N <= 4096),
+    0 where the call runs the two plain kernels; the panel's own size."""
+    import bit_quantized_gemm_int8_amd as q
+    _lib()
+    wb = q.quantize_gemm_w4a8_g128_workspace_bytes
+    assert wb(16, 4096, 11008) == 86 * 2112
+    assert wb(16, 11008, 4096) == 32 * 2112
+    assert wb(1, 12288, 4096) == 32 * 2112           # one row, more than 256 weight blocks
+    assert wb(1, 4112, 4096) == 32 * 2112
+    assert wb(1, 4096, 11008) == 0                    # one row, 256 blocks: the plain kernel
+    assert wb(2, 4096, 11008) == 86 * 2112
+    assert wb(3, 100, 2048) == 16 * 2112
+    assert wb(9, 40, 640) == 5 * 2112
+    assert wb(2, 48, 16384) == 128 * 2112             # the longest K
+    assert wb(2, 48, 16512) == 0
+    assert wb(17, 4096, 4096) == 0                    # past 16 rows
+    assert wb(0, 4096, 4096) == 0 and wb(4, 0, 4096) == 0
+    assert wb(4, 64, 200) == 0 and wb(-1, 64, 256) == 0
+    pb = q.quantize_per_token_i8_panel_bytes
+    assert pb(1, 128) == 2112 and pb(16, 16384) == 128 * 2112 and pb(5, 4096) == 32 * 2112
+    assert pb(17, 4096) == 0 and pb(0, 4096) == 0 and pb(4, 16512) == 0 and pb(4, 200) == 0
+
+
+def test_panel_validation_codes():
+    lib = _lib()
+    OK, NULL, SHAPE, ALIGN, DTYPE = 0, 1, 2, 3, 4
+    I64 = ctypes.c_int64
+    qp = lib.quantize_per_token_i8_panel
+    qp.argtypes = [P, ctypes.c_int, I64, I64, P, P, P, I64, P]
+    pbytes = 32 * 2112
+    assert qp(A, 2, 4, 4096, A, A, A, pbytes - 1, None) == SHAPE
+    assert qp(A, 2, 17, 4096, A, A, A, 10 ** 7, None) == SHAPE        # past 16 rows
+    assert qp(A, 2, 4, 16512, A, A, A, 10 ** 7, None) == SHAPE        # K > 16384
+    assert qp(A, 2, 4, 4000, A, A, A, 10 ** 7, None) == SHAPE         # K % 128
+    assert qp(A, 3, 4, 4096, A, A, A, pbytes, None) == DTYPE
+    assert qp(A, 2, 4, 4096, A, None, A, pbytes, None) == NULL        # x_scale
+    assert qp(A, 2, 4, 4096, A, A, None, pbytes, None) == NULL        # panel
+    assert qp(A, 2, 4, 4096, MIS, A, A, pbytes, None) == ALIGN
+    assert qp(A, 2, 4, 4096, A, A, MIS, pbytes, None) == ALIGN
+    assert qp(None, 2, 0, 4096, None, None, None, 0, None) == OK
+    gp = lib.gemm_w4a8_g128_panel
+    gp.argtypes = [P, I64, P, P, P, P, I64, I64, I64, P, ctypes.c_int, P]
+    assert gp(A, pbytes - 16, A, A, A, A, 4, 64, 4096, A, 2, None) == SHAPE
+    assert gp(A, 10 ** 7, A, A, A, A, 17, 64, 4096, A, 2, None) == SHAPE
+    assert gp(A, pbytes, A, A, A, A, 4, 64, 4096, A, 9, None) == DTYPE
+    assert gp(A, pbytes, None, A, A, A, 4, 64, 4096, A, 2, None) == NULL   # x_scale unless I32
+    assert gp(A, pbytes, A, A, A, None, 4, 64, 4096, A, 2, None) == NULL   # zero points
+    assert gp(MIS, pbytes, A, A, A, A, 4, 64, 4096, A, 2, None) == ALIGN
+    assert gp(None, 0, None, None, None, None, 4, 0, 4096, None, 2, None) == OK
 
 
 def test_binding_rejects_host_tensors():
