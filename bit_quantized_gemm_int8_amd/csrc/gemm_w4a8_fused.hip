@@ -24,13 +24,21 @@
 // unit (16 rows x 128 bytes = two groups) of a wave's run is requested at
 // once, each unit as two whole-line loads (8 rows x 128 B) landing in an
 // XOR-swizzled 2 KB slot, from which the MFMA fragments are read without bank
-// conflicts.  The block's scales and zero points are staged in LDS *before*
-// the weight requests go out: staged after, their few loads waited in the
-// same memory queues as the whole weight stream and held every wave at the
-// staging barrier until the stream had nearly finished (per-wave timestamps
-// on MI355X: barrier at ~7 us of a ~10 us kernel).  A wave whose run is one
-// unit shorter than its ring repeats its last unit's loads (cache hits) with
-// a zero scale instead of issuing out-of-range loads, which measured slow.
+// conflicts.  The block's scales and zero points and the token sums reach LDS
+// the same way, requested ahead of the weights and waited for after them.
+// Staged through registers instead, their loads must complete before the
+// LDS stores: written after the weight requests, the compiler sank the loads
+// behind them and waited for the whole stream; written before, every wave
+// paid the loads' latency before its first weight request.  A wave whose run
+// is one unit shorter than its ring repeats its last unit's loads (cache
+// hits) with a zero scale instead of issuing out-of-range loads, which
+// measured slow.
+//
+// At 16 token rows the panel a workgroup reads (16 K bytes) is twice its
+// weight block (16 x K/2 bytes); that token traffic through each CU's
+// vector-memory path, not HBM, bounds the kernel there (MI355X, 16 x 11008 x
+// 4096: 9.4 us, 6.6 us with the token loads left out).
+
 #include "qg_decode.hpp"
 #include "qg_device.hpp"
 #include "qg_launch.hpp"
@@ -156,8 +164,16 @@ __global__ __launch_bounds__(NT) void k_quant_panel(const void* __restrict__ x, 
 // GEMM on the panel: one workgroup per 16-row weight block, WAVES waves each
 // owning a contiguous run of units, every unit of the run requested at once
 // (RING >= the longest run).  I32 output: the per-group accumulators.
+//
+// LDS: the block's scales [16][G] and zero points [16][G] (fp16) and the
+// token sums [G][16] (int32), each in whole kilobytes, then each wave's ring
+// of 2 KB unit slots.  The three small arrays arrive by buffer-to-LDS loads
+// issued before any weight request, one kilobyte per wave-instruction; each
+// wave then issues its whole run and only afterwards waits for the small
+// arrays (older than its run, so a wait that leaves the run's requests in
+// flight) and meets the others at a barrier.
 // ---------------------------------------------------------------------------
-constexpr int kFdecEpt = 2;   // scale/zero elements per thread: 16 G <= 64 WAVES kFdecEpt
+__host__ __device__ constexpr int kb_of_chunks(int chunks) { return (chunks + 63) / 64; }
 
 template <int WAVES, int RING, typename OutT>
 __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
@@ -165,7 +181,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
     const int32_t* __restrict__ wq, const uint16_t* __restrict__ wscale,
     const uint16_t* __restrict__ wzero, int M, int MR, int N, int K, OutT* __restrict__ y) {
   constexpr bool kI32 = __is_same(OutT, int32_t);
-  constexpr int PU = 8;   // loads per unit: 2 weight DMAs, 4 token fragments, 2 token sums
+  constexpr int PU = 6;   // loads per unit: 2 weight DMAs, 4 token fragments
   static_assert(PU * RING <= 32, "vmcnt budget of wait_vmcnt");
   extern __shared__ __attribute__((aligned(16))) u32 smem[];
   __shared__ v4f red[kI32 ? 1 : WAVES][64];
@@ -175,27 +191,49 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
   const int n_base = blockIdx.x * 16;
   const int G = K >> 7, RB = K >> 1;
   const int units = (RB + kUnitBytes - 1) / kUnitBytes;
-  // the launcher guarantees WAVES <= units: every run holds at least one unit
-  const int ub = (int)((int64_t)units * wave / WAVES), ue = (int)((int64_t)units * (wave + 1) / WAVES);
-  const int szp = sz_pitch(G);
-  u32* szl = smem;
-  int8_t* ring = reinterpret_cast<int8_t*>(smem + ((16 * szp + 3) & ~3)) + wave * RING * 2 * 1024;
+  // run of units of this wave, the mapping rotated from one workgroup to the
+  // next of the same XCD (workgroups are dealt to the 8 XCDs in turn), so
+  // that they do not all read the same token lines at once; the launcher
+  // guarantees WAVES <= units: every run holds at least one unit
+  const int run = (wave + (int)(blockIdx.x >> 3)) % WAVES;
+  const int ub = (int)((int64_t)units * run / WAVES), ue = (int)((int64_t)units * (run + 1) / WAVES);
+  const int kb_sz = kb_of_chunks(2 * G), kb_sum = kb_of_chunks(4 * G);
+  int8_t* lds = reinterpret_cast<int8_t*>(smem);
+  const uint16_t* sl = reinterpret_cast<const uint16_t*>(lds);
+  const uint16_t* zl = reinterpret_cast<const uint16_t*>(lds + 1024 * kb_sz);
+  const int8_t* suml = lds + 2048 * kb_sz;
+  int8_t* ring = lds + 1024 * (2 * kb_sz + kb_sum) + wave * RING * 2048;
 
   const int rows_n = min(16, N - n_base);
   const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * (K >> 3), (u32)(rows_n * RB));
   const rsrc_t xr = make_rsrc(panel, (u32)(G * 128 * MR));
-  const rsrc_t tr = make_rsrc(tsum, (u32)(G * 64));
   const u32 xoff = r < MR ? (u32)((j * MR + r) * 16) : kOOB;   // rows >= MR: zero tokens
 
-  // 1. scales and zero points of the block into LDS, before any weight load
-  const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
-  const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
-  uint16_t s16[kFdecEpt], z16[kFdecEpt];
-#pragma unroll
-  for (int e = 0; e < kFdecEpt; ++e) {
-    const int el = tid + e * 64 * WAVES;
-    s16[e] = bld2(sr, el < 16 * G ? (u32)(2 * el) : kOOB);
-    z16[e] = bld2(zr, el < 16 * G ? (u32)(2 * el) : kOOB);
+  // 1. scales, zero points and token sums into LDS: kilobyte t of the three
+  // arrays by wave t mod WAVES.  A 16-byte load that runs past the end of
+  // its buffer range reads zeros for bytes inside it too (seen on MI355X),
+  // so the scales and zero points of a block cut short by N (2 G (N mod 16)
+  // bytes, not always a multiple of 16) go through registers element by
+  // element instead.
+  {
+    const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+    const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+    const rsrc_t tr = make_rsrc(tsum, (u32)(G * 64));
+    const int t0 = rows_n == 16 ? 0 : 2 * kb_sz;
+    for (int t = t0 + wave; t < 2 * kb_sz + kb_sum; t += WAVES) {
+      const u32 o = (u32)(1024 * (t < kb_sz ? t : t < 2 * kb_sz ? t - kb_sz : t - 2 * kb_sz) + 16 * lane);
+      if (t < kb_sz) dma16(sr, lds + 1024 * t, o);
+      else if (t < 2 * kb_sz) dma16(zr, lds + 1024 * t, o);
+      else dma16(tr, lds + 1024 * t, o);
+    }
+    if (rows_n < 16) {   // rows past N: zeros
+      uint16_t* sw = reinterpret_cast<uint16_t*>(lds);
+      uint16_t* zw = reinterpret_cast<uint16_t*>(lds + 1024 * kb_sz);
+      for (int el = tid; el < 16 * G; el += 64 * WAVES) {
+        sw[el] = bld2(sr, (u32)(2 * el));
+        zw[el] = bld2(zr, (u32)(2 * el));
+      }
+    }
   }
   float sx[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (!kI32) {
@@ -205,20 +243,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
       sx[i] = xs[m < M ? m : M - 1];
     }
   }
-#pragma unroll
-  for (int e = 0; e < kFdecEpt; ++e) {
-    const int el = tid + e * 64 * WAVES;
-    if (el < 16 * G) {
-      const int row = el / G;
-      szl[row * szp + (el - row * G)] = (u32)s16[e] | ((u32)z16[e] << 16);
-    }
-  }
-  lds_barrier();
+  // every wave's small-array requests ahead of any weight request
+  __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. every unit of the run: two whole-line DMAs (rows 8h..8h+7, lane l:
-  // row 8h + l/8, chunk (l % 8) ^ f(row)), four token fragments, two sums
-  v4i tk[RING][2][2], ts[RING][2];
+  // row 8h + l/8, chunk (l % 8) ^ f(row)) and four token fragments
+  v4i tk[RING][2][2];
 #pragma unroll
   for (int i = 0; i < RING; ++i) {
     const int q = min(ub + i, ue - 1);   // past the run: the last unit again
@@ -232,17 +263,17 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int g = 2 * q + s;   // g == G (odd G): past both resources, zeros
+      const int g = 2 * q + s;   // g == G (odd G): past the panel, zeros
 #pragma unroll
       for (int h = 0; h < 2; ++h) tk[i][s][h] = bld16(xr, xoff + (u32)((g * 2 + h) * 64 * MR));
-      ts[i][s] = bld16(tr, (u32)(g * 64 + 16 * j));
     }
   }
-
   __builtin_amdgcn_sched_barrier(0);
+  // the small arrays are older than every request of the run
+  wait_vmcnt(PU * RING);
+  lds_barrier();
 
   // 3. consume the units in issue order
-  const u32* szrow = szl + r * szp;
   int rsl[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) rsl[s] = r * 128 + (((4 * s + j) ^ ((r >> 1) & 7)) << 4);
@@ -260,16 +291,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
     for (int s = 0; s < 2; ++s) {
       const v4i f = s ? f1 : f0;
       const int g = 2 * q + s;
-      const bool gin = live && g < G;
-      const u32 szw = szrow[min(g, G - 1)];
-      const int z = (int)f16_bits_to_f32((uint16_t)(szw >> 16));
+      const bool gin = g < G;
+      const int gg = gin ? g : G - 1;   // g == G: zero tokens, zero sums below
+      const int z = (int)f16_bits_to_f32(zl[r * G + gg]);
+      v4i ts = *reinterpret_cast<const v4i*>(suml + 64 * gg + 16 * j);
+      if (!gin) ts = v4i{0, 0, 0, 0};
       v4i acc;   // |z| <= 15, |token sum| <= 128 * 127: exact 24-bit products
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __mul24(-z, ts[i][s][e]);
+      for (int e = 0; e < 4; ++e) acc[e] = __mul24(-z, ts[e]);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(tk[i][s][0], unpack_pair((u32)f[0], (u32)f[1]), acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(tk[i][s][1], unpack_pair((u32)f[2], (u32)f[3]), acc, 0, 0, 0);
       if constexpr (kI32) {
-        if (gin && n < N) {
+        if (live && gin && n < N) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int m = 4 * j + e;
@@ -277,7 +310,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
           }
         }
       } else {
-        const float sc = gin ? f16_bits_to_f32((uint16_t)(szw & 0xFFFFu)) : 0.f;
+        const float sc = live && gin ? f16_bits_to_f32(sl[r * G + gg]) : 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) yacc[e] = __builtin_fmaf(sc, (float)acc[e], yacc[e]);
       }
@@ -335,8 +368,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   if ((units + waves - 1) / waves > kMaxRing) waves = 16;
   while (waves > 1 && waves > units) waves /= 2;
   const int ring = (int)((units + waves - 1) / waves);
-  if (ring > kMaxRing || 16 * G > (int64_t)64 * waves * kFdecEpt) return p;
-  p.lds = (size_t)((16 * sz_pitch((int)G) + 3) & ~3) * 4 + (size_t)waves * ring * 2048;
+  if (ring > kMaxRing) return p;
+  p.lds = (size_t)1024 * (2 * kb_of_chunks((int)(2 * G)) + kb_of_chunks((int)(4 * G))) +
+          (size_t)waves * ring * 2048;
   if (p.lds + (size_t)waves * 64 * sizeof(v4f) > 160 * 1024) return p;
   p.ok = true;
   p.waves = waves;
