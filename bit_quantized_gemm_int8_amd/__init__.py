@@ -17,6 +17,7 @@ Entry points (same names as the C ABI):
   gemm_w4a8_g128_panel(panel, x_scale, wq, w_scale, w_zero, M, out_dtype)
   quantize_gemm_w4a8_g128(x, wq, w_scale, w_zero, out_dtype) -> (y, xq, x_scale): both steps in one call
   quantize_gemm_w4a8_g128_workspace_bytes(M, N, K) -> bytes of device workspace that call needs
+  quantize_gemm_w4a8_g128_noalloc(x, wq, w_scale, w_zero, out_dtype) -> (y, xq, x_scale): the library's own panel
   gemm_w4a16_g128(x, wq, w_scale, w_zero, out_dtype)
   smoothquant_fold(x_cal, w) / awq_fold(x_cal, w) -> (s f32 [K], w_folded f32 [K,N])
   apply_smoothing(x, s, out_dtype)
@@ -42,6 +43,7 @@ __all__ = [
     "quantize_gemm_w8a8_plan", "quantize_gemm_w4a8_g128",
     "quantize_gemm_w4a8_g128_workspace_bytes", "quantize_per_token_i8_panel",
     "quantize_per_token_i8_panel_bytes", "gemm_w4a8_g128_panel",
+    "quantize_gemm_w4a8_g128_noalloc",
     "smoothquant_fold", "awq_fold", "apply_smoothing", "status_string",
     "quantize_kv_i8_segments", "dequantize_kv_i8_segments", "KV_SEGMENT",
     "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
@@ -66,6 +68,8 @@ _SIGNATURES = {
     "quantize_gemm_w4a8_g128": [_vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _vp,
                                 _vp, _i64, _vp],
     "quantize_per_token_i8_panel": [_vp, _int, _i64, _i64, _vp, _vp, _vp, _i64, _vp],
+    "quantize_gemm_w4a8_g128_noalloc": [_vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int,
+                                        _vp, _vp, _vp],
     "gemm_w4a8_g128_panel": [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
     "gemm_w4a16_g128": [_vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
     "smoothquant_fold": [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp],
@@ -350,6 +354,28 @@ def quantize_gemm_w4a8_g128(x, wq, w_scale, w_zero, out_dtype=torch.bfloat16, ou
     _call("quantize_gemm_w4a8_g128", px, _DTYPE_CODE[x.dtype], pwq, pws, pwz, M, N, K,
           y.data_ptr(), _DTYPE_CODE[out_dtype], xq.data_ptr(), xs.data_ptr(), pw,
           workspace.numel(), _stream())
+    return y, xq, xs
+
+
+def quantize_gemm_w4a8_g128_noalloc(x, wq, w_scale, w_zero, out_dtype=torch.bfloat16, out=None,
+                                    xq_out=None):
+    """quantize_gemm_w4a8_g128 with the library's own per-GPU panel array
+    instead of a workspace: the C call allocates nothing (outputs given as
+    out / xq_out are filled in place; calls overlapping on one GPU race)."""
+    px = _dev(x, "x", _FLOATS)
+    M, K = _2d(x, "x")
+    dev = x.device
+    N = _2d(wq, "wq")[0]
+    pwq = _dev(wq, "wq", (torch.int32,), (N, K // 8), dev)
+    pwz = _dev(w_zero, "w_zero", (torch.float16,), (N, K // 128), dev)
+    pws = _opt(w_scale, "w_scale", (torch.float16,), (N, K // 128), dev)
+    shape = (M, K // 128, N) if out_dtype == torch.int32 else (M, N)
+    y = _out(out, shape, out_dtype, dev)
+    xq, xs = xq_out if xq_out is not None else (None, None)
+    xq = _out(xq, (M, K), torch.int8, dev, "xq out")
+    xs = _out(xs, (M,), torch.float32, dev, "x_scale out")
+    _call("quantize_gemm_w4a8_g128_noalloc", px, _DTYPE_CODE[x.dtype], pwq, pws, pwz, M, N, K,
+          y.data_ptr(), _DTYPE_CODE[out_dtype], xq.data_ptr(), xs.data_ptr(), _stream())
     return y, xq, xs
 
 

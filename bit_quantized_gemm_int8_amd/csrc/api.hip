@@ -225,6 +225,31 @@ qg_status_t quantize_gemm_w4a8_g128(const void* x, int x_dtype, const int32_t* w
                                                   y_dtype, xq, x_scale, workspace, st));
 }
 
+qg_status_t quantize_gemm_w4a8_g128_noalloc(const void* x, int x_dtype, const int32_t* wq,
+                                            const uint16_t* w_scale_f16,
+                                            const uint16_t* w_zero_f16, int64_t M, int64_t N,
+                                            int64_t K, void* y, int y_dtype, int8_t* xq,
+                                            float* x_scale, void* stream) {
+  if (qg_status_t s = check_dims(M, N, K)) return s;
+  if (K % 128 || K / 128 > kMaxGroups) return QG_ERR_SHAPE;
+  if (y_dtype == QG_I32 && M * (K / 128) * N > kMaxDim) return QG_ERR_SHAPE;
+  if (!is_float_dtype(x_dtype)) return QG_ERR_DTYPE;
+  if (!is_float_dtype(y_dtype) && y_dtype != QG_I32) return QG_ERR_DTYPE;
+  if (M == 0) return QG_OK;
+  // the panel the call needs must fit the library's array
+  if (N > 0 && qg::quantize_gemm_w4a8_workspace(M, N, K) > qg::noalloc_scratch_bytes())
+    return QG_ERR_SHAPE;
+  if (!x || !xq || !x_scale) return QG_ERR_NULL;
+  if (N > 0 && (!wq || !w_zero_f16 || !y || (y_dtype != QG_I32 && !w_scale_f16)))
+    return QG_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xq) || (N > 0 && !aligned16(wq))) return QG_ERR_ALIGN;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (N == 0) return hip_status(qg::launch_quant_per_token(x, x_dtype, M, K, xq, x_scale, st));
+  const uint16_t* ws = w_scale_f16 ? w_scale_f16 : w_zero_f16;   // I32: values unused
+  return hip_status(qg::launch_quantize_gemm_w4a8_noalloc(x, x_dtype, wq, ws, w_zero_f16, M, N,
+                                                          K, y, y_dtype, xq, x_scale, st));
+}
+
 qg_status_t quantize_weight_u4_g128_outliers(const float* w, int64_t K, int64_t N, int32_t* wq,
                                              uint16_t* w_scale_f16, uint16_t* w_zero_f16,
                                              uint64_t* w_out_rec, float* w_out_scale,

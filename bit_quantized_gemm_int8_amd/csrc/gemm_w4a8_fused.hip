@@ -44,6 +44,8 @@
 #include "qg_launch.hpp"
 #include "qg_quant.hpp"
 
+#include <mutex>
+
 namespace qg {
 
 namespace {
@@ -482,6 +484,65 @@ hipError_t launch_quantize_gemm_w4a8(const void* x, int x_dtype, const int32_t* 
   }
   if (hipError_t e = launch_quant_panel(x, x_dtype, M, K, xq, xs, workspace, st)) return e;
   return launch_gemm_w4a8_panel(workspace, xs, wq, ws, wz, M, N, K, y, y_dtype, st);
+}
+
+// ---------------------------------------------------------------------------
+// The library's own panel, for the entry point that allocates nothing: a
+// fixed array in device memory, one per GPU (each device holds its own copy
+// until the process ends), large enough for the biggest panel (K = 16384).
+// In host code the name `scratch` is only a stand-in, not a device address:
+// kernels and copies get the address hipGetSymbolAddress returns for the
+// device, looked up once per device with that device current and kept.
+// Every call on a GPU shares its array; calls that overlap on one GPU race.
+// No part of it needs to start at zero: the panel quantizer writes every
+// byte the panel GEMM reads.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = (int64_t)(kPanelMaxK / 128) * (128 * kPanelRows + 4 * kPanelRows);
+static __device__ __align__(256) int8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the device `st` belongs to (the current
+// device for the null stream).
+hipError_t scratch_address(hipStream_t st, void** out) {
+  int cur = 0, dev = 0;
+  if (hipError_t e = hipGetDevice(&cur)) return e;
+  dev = cur;
+  if (st)
+    if (hipError_t e = hipStreamGetDevice(st, &dev)) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur)
+      if (hipError_t e = hipSetDevice(dev)) return e;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+int64_t noalloc_scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_quantize_gemm_w4a8_noalloc(const void* x, int x_dtype, const int32_t* wq,
+                                             const uint16_t* ws, const uint16_t* wz, int64_t M,
+                                             int64_t N, int64_t K, void* y, int y_dtype,
+                                             int8_t* xq, float* xs, hipStream_t st) {
+  const int64_t need = quantize_gemm_w4a8_workspace(M, N, K);
+  void* panel = nullptr;
+  if (need > 0) {
+    if (need > kScratchBytes) return hipErrorInvalidValue;   // the API rejects this first
+    if (hipError_t e = scratch_address(st, &panel)) return e;
+  }
+  return launch_quantize_gemm_w4a8(x, x_dtype, wq, ws, wz, M, N, K, y, y_dtype, xq, xs, panel, st);
 }
 
 }  // namespace qg

@@ -47,6 +47,13 @@ hipError_t launch_quantize_gemm_w4a8(const void* x, int x_dtype, const int32_t* 
                                      int64_t K, void* y, int y_dtype, int8_t* xq, float* xs,
                                      void* workspace, hipStream_t st);
 int64_t quantize_gemm_w4a8_workspace(int64_t M, int64_t N, int64_t K);
+// The same with the library's own per-device panel array (no allocation,
+// no workspace argument), and that array's size.
+hipError_t launch_quantize_gemm_w4a8_noalloc(const void* x, int x_dtype, const int32_t* wq,
+                                             const uint16_t* ws, const uint16_t* wz, int64_t M,
+                                             int64_t N, int64_t K, void* y, int y_dtype,
+                                             int8_t* xq, float* xs, hipStream_t st);
+int64_t noalloc_scratch_bytes();
 hipError_t launch_quant_weight_u4_outl(const float* w, int64_t K, int64_t N, int32_t* wq,
                                        uint16_t* ws, uint16_t* wz, uint64_t* rec, float* s8,
                                        hipStream_t st);

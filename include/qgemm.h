@@ -290,6 +290,26 @@ qg_status_t quantize_gemm_w4a8_g128(const void* x, int x_dtype, const int32_t* w
 int64_t quantize_gemm_w4a8_g128_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * quantize_gemm_w4a8_g128 for callers that cannot allocate device memory or
+ * hand over a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and checks
+ * without workspace / workspace_bytes: where the panel pair runs, the panel
+ * lives in a fixed array inside the library, 270336 bytes per GPU (the
+ * panel of K = 16384), held by each GPU the library runs on until the
+ * process ends.  A panel larger than that array is rejected with
+ * QG_ERR_SHAPE (no size the panel pair takes needs more).  The call
+ * allocates nothing; on its first call on a device it looks up that
+ * device's copy of the array (a failure there returns QG_ERR_HIP).  All
+ * calls on one GPU share the array: calls that overlap on one GPU (several
+ * streams, several host threads) race and must be serialised by the caller.
+ */
+qg_status_t quantize_gemm_w4a8_g128_noalloc(const void* x, int x_dtype, const int32_t* wq,
+                                            const uint16_t* w_scale_f16,
+                                            const uint16_t* w_zero_f16, int64_t M, int64_t N,
+                                            int64_t K, void* y, int y_dtype, int8_t* xq,
+                                            float* x_scale, void* stream);
+
+/*
  * Group-wise (g = 128) uint4 weights with the largest weights of every group
  * kept in an INT8 side store (offline).
  * 「LLM推理降本五要素」 §2.2 (the top 2% of each group by magnitude stored at

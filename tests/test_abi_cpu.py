@@ -43,7 +43,7 @@ def test_header_declares_the_entry_points():
               "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
               "quantize_weight_u4_g128_sparse24", "gemm_w4a8_g128_sparse24",
               "quantize_gemm_w8a8", "quantize_gemm_w8a8_plan", "quantize_gemm_w4a8_g128",
-              "quantize_gemm_w4a8_g128_workspace_bytes"]:
+              "quantize_gemm_w4a8_g128_workspace_bytes", "quantize_gemm_w4a8_g128_noalloc"]:
         assert n in names, n
 
 
@@ -224,6 +224,23 @@ def test_w4a8_workspace_on_the_host():
     pb = q.quantize_per_token_i8_panel_bytes
     assert pb(1, 128) == 2112 and pb(16, 16384) == 128 * 2112 and pb(5, 4096) == 32 * 2112
     assert pb(17, 4096) == 0 and pb(0, 4096) == 0 and pb(4, 16512) == 0 and pb(4, 200) == 0
+
+
+def test_noalloc_validation_codes():
+    lib = _lib()
+    OK, NULL, SHAPE, ALIGN, DTYPE = 0, 1, 2, 3, 4
+    I64 = ctypes.c_int64
+    na = lib.quantize_gemm_w4a8_g128_noalloc
+    na.argtypes = [P, ctypes.c_int, P, P, P, I64, I64, I64, P, ctypes.c_int, P, P, P]
+    assert na(A, 2, A, A, A, 8, 16, 192, A, 2, A, A, None) == SHAPE       # K % 128
+    assert na(A, 2, A, A, A, -1, 16, 4096, A, 2, A, A, None) == SHAPE
+    assert na(A, 3, A, A, A, 8, 16, 4096, A, 2, A, A, None) == DTYPE
+    assert na(A, 2, A, A, A, 8, 16, 4096, A, 9, A, A, None) == DTYPE
+    assert na(A, 2, A, None, A, 8, 16, 4096, A, 2, A, A, None) == NULL    # scales unless I32
+    assert na(A, 2, A, A, A, 8, 16, 4096, A, 2, None, A, None) == NULL    # xq
+    assert na(A, 2, A, A, None, 8, 16, 4096, A, 2, A, A, None) == NULL    # zero points
+    assert na(MIS, 2, A, A, A, 8, 16, 4096, A, 2, A, A, None) == ALIGN
+    assert na(None, 2, None, None, None, 0, 16, 4096, None, 2, None, None, None) == OK
 
 
 def test_panel_validation_codes():
