@@ -51,7 +51,7 @@ KERNEL_SOURCES = {
     "w8a8": ["gemm_w8a8.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w8a8_fq": ["gemm_w8a8_fq.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a8": ["gemm_w4a8.hip", "gemm_w4a8_fused.hip", "qg_decode.hpp", "qg_device.hpp"],
-    "w4a8_outl": ["gemm_w4a8.hip", "qg_decode.hpp", "qg_device.hpp"],
+    "w4a8_outl": ["gemm_w4a8.hip", "gemm_w4a8_fused.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a8_sp24": ["gemm_w4a8_sp24.hip", "qg_decode.hpp", "qg_device.hpp"],
     "w4a16": ["gemm_w4a16.hip", "qg_decode.hpp", "qg_device.hpp"],
     "quant": ["quant.hip", "qg_device.hpp"],
@@ -131,13 +131,17 @@ def algorithmic(wl):
 
 def fused_step(wl) -> bool:
     """Whether the workload's step runs the one-kernel quantize + W8A8 form,
-    or for W4A8 the panel pair (quantize_per_token_i8_panel +
-    gemm_w4a8_g128_panel): the library's own choice for these sizes, asked of
-    the library (host only)."""
+    or for W4A8 (with or without outliers) the panel pair
+    (quantize_per_token_i8_panel + gemm_w4a8_g128[_outliers]_panel): the
+    library's own choice for these sizes, asked of the library (host only)."""
     import torch
     import bit_quantized_gemm_int8_amd as qg
     if wl.path == "w4a8":
         return qg.quantize_gemm_w4a8_g128_workspace_bytes(wl.M, wl.N, wl.K) > 0
+    if wl.path == "w4a8_outl":
+        # the panel pair where it measured faster than the plain outlier kernel
+        # (MI355X: 1-8 rows 20-27% faster; 16 rows of K = 11008 slower)
+        return wl.M <= 8 and qg.quantize_per_token_i8_panel_bytes(wl.M, wl.K) > 0
     if wl.path != "w8a8":
         return False
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -313,7 +317,9 @@ def run_workload(wl, steps, warmup, traffic_db):
             qg.gemm_w4a16_g128(x_in, w[0], w[1], w[2], out_dtype=y.dtype, out=y)
 
     fused = fused_step(wl)
-    ws_bytes = qg.quantize_gemm_w4a8_g128_workspace_bytes(wl.M, wl.N, wl.K) if wl.path == "w4a8" else 0
+    ws_bytes = (qg.quantize_gemm_w4a8_g128_workspace_bytes(wl.M, wl.N, wl.K) if wl.path == "w4a8"
+                else qg.quantize_per_token_i8_panel_bytes(wl.M, wl.K) if wl.path == "w4a8_outl"
+                else 0)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def layer(i):   # the layer through its one entry point (the library's choice)
@@ -329,11 +335,18 @@ def run_workload(wl, steps, warmup, traffic_db):
 
     def panel_gemm(i):
         w = copies[i % R]
-        qg.gemm_w4a8_g128_panel(workspace, xs, w[0], w[1], w[2], wl.M, out_dtype=y.dtype, out=y)
+        if wl.path == "w4a8_outl":
+            qg.gemm_w4a8_g128_outliers_panel(workspace, xs, *w, wl.M, out_dtype=y.dtype, out=y)
+        else:
+            qg.gemm_w4a8_g128_panel(workspace, xs, w[0], w[1], w[2], wl.M, out_dtype=y.dtype, out=y)
 
     def step(i):
         if wl.path in ("w8a8", "w4a8"):
             layer(i)
+            return
+        if wl.path == "w4a8_outl" and fused:
+            panel_quant()
+            panel_gemm(i)
             return
         if wl.path != "w4a16":
             quant()
@@ -354,7 +367,7 @@ def run_workload(wl, steps, warmup, traffic_db):
     g_warm = capture(step, max(warmup, 1))
     g_step = capture(step, steps)
     # the dominant kernel alone: the one-kernel W8A8 form is the whole step
-    if fused and wl.path == "w4a8":
+    if fused and wl.path in ("w4a8", "w4a8_outl"):
         panel_quant()   # the panel the timed GEMMs read
         g_gemm = capture(panel_gemm, steps)
         g_quant = capture(lambda i: panel_quant(), steps)
@@ -766,7 +779,7 @@ def batch_sweep(steps):
 KERNEL_OF = {
     "w8a8_decode_ffn_up": [("k_w8a8_dec<8,", "unsigned short>")],
     "w8a8_tiny": [("k_w8a8_fq<16,", "float>")],
-    "w4a8_ffn_down": [("k_w4a8_fdec<16, 3, unsigned short>",)],
+    "w4a8_ffn_down": [("k_w4a8_fdec<16, 3, false, unsigned short>",)],
     "w4a8_outl_ffn_down": [("k_w4a8_dec<16, 8, 1, true, unsigned short>",)],
     "w4a8_sp24_ffn_down": [("k_w4a8_sp24<unsigned short>",)],
     "w4a16_qkv": [("k_w4a16_dec<1,", "_Float16>"), ("k_w4a16_decILi1E", "DF16_E")],
@@ -911,7 +924,8 @@ STEP_TEXT = {
     "w4a8": lambda h: "quantize_gemm_w4a8_g128: " + (
         "quantize_per_token_i8_panel + gemm_w4a8_g128_panel kernels" if h["fused"] else
         "quantize_per_token_i8 + gemm_w4a8_g128 kernels"),
-    "w4a8_outl": lambda h: "quantize_per_token_i8 + gemm_w4a8_g128_outliers",
+    "w4a8_outl": lambda h: ("quantize_per_token_i8_panel + gemm_w4a8_g128_outliers_panel"
+                            if h["fused"] else "quantize_per_token_i8 + gemm_w4a8_g128_outliers"),
     "w4a8_sp24": lambda h: "quantize_per_token_i8 + gemm_w4a8_g128_sparse24",
     "w4a16": lambda h: "gemm_w4a16_g128",
 }

@@ -23,6 +23,7 @@ Entry points (same names as the C ABI):
   apply_smoothing(x, s, out_dtype)
   quantize_weight_u4_g128_outliers(w)           -> (wq, scale, zero, records int64 [N,G], s8 f32 [N])
   gemm_w4a8_g128_outliers(xq, x_scale, wq, w_scale, w_zero, records, s8, out_dtype)
+  gemm_w4a8_g128_outliers_panel(panel, x_scale, wq, w_scale, w_zero, records, s8, M, out_dtype)
   quantize_weight_u4_g128_sparse24(w)           -> (wsp int32 [N/16,G,16,12], scale f16 [N,G], zero f16 [N,G])
   gemm_w4a8_g128_sparse24(xq, x_scale, wsp, w_scale, w_zero, out_dtype)
   quantize_kv_i8_segments(kv)                   -> (kv_q int8 [T,H,D], kv_scale f32 [H,ceil(T/128),D])
@@ -43,6 +44,7 @@ __all__ = [
     "quantize_gemm_w8a8_plan", "quantize_gemm_w4a8_g128",
     "quantize_gemm_w4a8_g128_workspace_bytes", "quantize_per_token_i8_panel",
     "quantize_per_token_i8_panel_bytes", "gemm_w4a8_g128_panel",
+    "gemm_w4a8_g128_outliers_panel",
     "quantize_gemm_w4a8_g128_noalloc",
     "smoothquant_fold", "awq_fold", "apply_smoothing", "status_string",
     "quantize_kv_i8_segments", "dequantize_kv_i8_segments", "KV_SEGMENT",
@@ -71,6 +73,8 @@ _SIGNATURES = {
     "quantize_gemm_w4a8_g128_noalloc": [_vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int,
                                         _vp, _vp, _vp],
     "gemm_w4a8_g128_panel": [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
+    "gemm_w4a8_g128_outliers_panel": [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                      _vp, _int, _vp],
     "gemm_w4a16_g128": [_vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp],
     "smoothquant_fold": [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp],
     "awq_fold": [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp],
@@ -430,6 +434,27 @@ def gemm_w4a8_g128_outliers(xq, x_scale, wq, w_scale, w_zero, records, s8,
     y = _out(out, shape, out_dtype, dev)
     _call("gemm_w4a8_g128_outliers", pxq, pxs, pwq, pws, pwz, prc, ps8, M, N, K, y.data_ptr(),
           _DTYPE_CODE[out_dtype], _stream())
+    return y
+
+
+def gemm_w4a8_g128_outliers_panel(panel, x_scale, wq, w_scale, w_zero, records, s8, M,
+                                  out_dtype=torch.bfloat16, out=None):
+    """gemm_w4a8_g128_outliers on a token panel of M rows
+    (quantize_per_token_i8_panel); int32 out_dtype returns [M, K/128 + 1, N]."""
+    dev = panel.device
+    pp = _dev(panel, "panel", (torch.uint8,), None, dev)
+    N, K8 = _2d(wq, "wq")
+    K = K8 * 8
+    pwq = _dev(wq, "wq", (torch.int32,), (N, K // 8), dev)
+    pwz = _dev(w_zero, "w_zero", (torch.float16,), (N, K // 128), dev)
+    prc = _dev(records, "records", (torch.int64,), (N, K // 128), dev)
+    pxs = _opt(x_scale, "x_scale", (torch.float32,), (M,), dev)
+    pws = _opt(w_scale, "w_scale", (torch.float16,), (N, K // 128), dev)
+    ps8 = _opt(s8, "s8", (torch.float32,), (N,), dev)
+    shape = (M, K // 128 + 1, N) if out_dtype == torch.int32 else (M, N)
+    y = _out(out, shape, out_dtype, dev)
+    _call("gemm_w4a8_g128_outliers_panel", pp, panel.numel(), pxs, pwq, pws, pwz, prc, ps8, M, N,
+          K, y.data_ptr(), _DTYPE_CODE[out_dtype], _stream())
     return y
 
 

@@ -283,6 +283,27 @@ qg_status_t gemm_w4a8_g128_outliers(const int8_t* xq, const float* x_scale, cons
                                               static_cast<hipStream_t>(stream)));
 }
 
+qg_status_t gemm_w4a8_g128_outliers_panel(const void* panel, int64_t panel_bytes,
+                                          const float* x_scale, const int32_t* wq,
+                                          const uint16_t* w_scale_f16,
+                                          const uint16_t* w_zero_f16, const uint64_t* w_out_rec,
+                                          const float* w_out_scale, int64_t M, int64_t N,
+                                          int64_t K, void* y, int y_dtype, void* stream) {
+  if (qg_status_t s = check_dims(M, N, K)) return s;
+  if (!is_float_dtype(y_dtype) && y_dtype != QG_I32) return QG_ERR_DTYPE;
+  if (M == 0 || N == 0) return QG_OK;
+  const int64_t need = qg::panel_bytes(M, K);
+  if (need == 0 || panel_bytes < need || !qg::gemm_w4a8_panel_ok(M, N, K)) return QG_ERR_SHAPE;
+  if (y_dtype == QG_I32 && M * (K / 128 + 1) * N > kMaxDim) return QG_ERR_SHAPE;
+  if (!panel || !wq || !w_zero_f16 || !w_out_rec || !y) return QG_ERR_NULL;
+  if (y_dtype != QG_I32 && (!x_scale || !w_scale_f16 || !w_out_scale)) return QG_ERR_NULL;
+  if (!aligned16(panel) || !aligned16(wq) || !aligned16(w_out_rec)) return QG_ERR_ALIGN;
+  const uint16_t* ws = w_scale_f16 ? w_scale_f16 : w_zero_f16;   // I32: values unused
+  return hip_status(qg::launch_gemm_w4a8_outl_panel(panel, x_scale, wq, ws, w_zero_f16, w_out_rec,
+                                                    w_out_scale, M, N, K, y, y_dtype,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 qg_status_t quantize_weight_u4_g128_sparse24(const float* w, int64_t K, int64_t N, int32_t* wsp,
                                              uint16_t* w_scale_f16, uint16_t* w_zero_f16,
                                              void* stream) {

@@ -66,35 +66,33 @@ __device__ __forceinline__ v4i unpack_pair(u32 w0, u32 w1) {
              (int)((w1 >> 4) & 0x0F0F0F0Fu)};
 }
 
+// Outlier-retention side path (「LLM推理降本五要素」 §2.2) on the panel: a
+// group's record holds three (index << 8 | code byte) slots; lane (row r,
+// k-block j) of an MFMA covers the inputs k = 32 j + 16 h + [0, 16) of the
+// group, held in the panel's byte order (within each 8: even k, then odd).
+// The slots falling there are placed at the byte their k takes in that
+// order, giving a sparse int8 operand whose product with the panel fragment
+// accumulates sum_k x_q[m, k] * code exactly in int32.
+__device__ __forceinline__ v4i outlier_operand_panel(u32 lo, u32 hi, int kb) {
+  uint64_t b0 = 0, b1 = 0;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const u32 slot = (i == 0 ? lo : i == 1 ? lo >> 16 : hi) & 0xFFFFu;
+    const int pos = (int)(slot >> 8) - kb;   // k offset in the lane's 16, if in range
+    const int at = (pos & 8) | ((pos & 1) << 2) | ((pos >> 1) & 3);   // its byte in the panel order
+    const uint64_t v = (uint64_t)(slot & 0xFFu) << (8 * (at & 7));
+    b0 |= (u32)pos < 8u ? v : 0;
+    b1 |= (u32)(pos - 8) < 8u ? v : 0;
+  }
+  return v4i{(int)(u32)b0, (int)(u32)(b0 >> 32), (int)(u32)b1, (int)(u32)(b1 >> 32)};
+}
+
 // sum of the 16 signed bytes of v (exact)
 __device__ __forceinline__ int byte_sum16(v4i v) {
   int s = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_sdot4(v[i], 0x01010101, s, false);
   return s;
-}
-
-// s_waitcnt vmcnt(n) for n known once the caller's loop is unrolled
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-#define QG_WAITVM(i) case i: asm volatile("s_waitcnt vmcnt(" #i ")" ::: "memory"); break;
-    QG_WAITVM(0) QG_WAITVM(1) QG_WAITVM(2) QG_WAITVM(3) QG_WAITVM(4) QG_WAITVM(5) QG_WAITVM(6)
-    QG_WAITVM(7) QG_WAITVM(8) QG_WAITVM(9) QG_WAITVM(10) QG_WAITVM(11) QG_WAITVM(12)
-    QG_WAITVM(13) QG_WAITVM(14) QG_WAITVM(15) QG_WAITVM(16) QG_WAITVM(17) QG_WAITVM(18)
-    QG_WAITVM(19) QG_WAITVM(20) QG_WAITVM(21) QG_WAITVM(22) QG_WAITVM(23) QG_WAITVM(24)
-    QG_WAITVM(25) QG_WAITVM(26) QG_WAITVM(27) QG_WAITVM(28) QG_WAITVM(29) QG_WAITVM(30)
-    QG_WAITVM(31) QG_WAITVM(32)
-#undef QG_WAITVM
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
-}
-
-#define QG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// 16-byte buffer load of every lane straight into LDS at lds + 16 lane (lds
-// wave-uniform), non-temporal: the weights are read once per call
-__device__ __forceinline__ void dma16(rsrc_t r, int8_t* lds, u32 voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, QG_LDS(lds), 16, voff, 0, 0, kAuxNonTemporal);
 }
 
 }  // namespace
@@ -175,23 +173,27 @@ __global__ __launch_bounds__(NT) void k_quant_panel(const void* __restrict__ x, 
 // arrays (older than its run, so a wait that leaves the run's requests in
 // flight) and meets the others at a barrier.
 // ---------------------------------------------------------------------------
-__host__ __device__ constexpr int kb_of_chunks(int chunks) { return (chunks + 63) / 64; }
-
-template <int WAVES, int RING, typename OutT>
+// OUTL: the INT8 outlier side path as in k_w4a8_dec, its records loaded with
+// each unit and its operand laid out in the panel's byte order.
+template <int WAVES, int RING, bool OUTL, typename OutT>
 __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
     const int8_t* __restrict__ panel, const int* __restrict__ tsum, const float* __restrict__ xs,
     const int32_t* __restrict__ wq, const uint16_t* __restrict__ wscale,
-    const uint16_t* __restrict__ wzero, int M, int MR, int N, int K, OutT* __restrict__ y) {
+    const uint16_t* __restrict__ wzero, const uint64_t* __restrict__ orec,
+    const float* __restrict__ os8, int M, int MR, int N, int K, OutT* __restrict__ y) {
   constexpr bool kI32 = __is_same(OutT, int32_t);
-  constexpr int PU = 6;   // loads per unit: 2 weight DMAs, 4 token fragments
-  static_assert(PU * RING <= 32, "vmcnt budget of wait_vmcnt");
+  // loads per unit: 2 weight DMAs, 4 token fragments (, 1 outlier record load)
+  constexpr int PU = OUTL ? 7 : 6;
+  static_assert(PU * RING <= 63, "vmcnt budget of wait_vmcnt");
   extern __shared__ __attribute__((aligned(16))) u32 smem[];
   __shared__ v4f red[kI32 ? 1 : WAVES][64];
+  __shared__ v4i redo[OUTL ? WAVES : 1][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int n_base = blockIdx.x * 16;
   const int G = K >> 7, RB = K >> 1;
+  const int GY = OUTL ? G + 1 : G;   // int32 output slices per token: groups (+ side sum)
   const int units = (RB + kUnitBytes - 1) / kUnitBytes;
   // run of units of this wave, the mapping rotated from one workgroup to the
   // next of the same XCD (workgroups are dealt to the 8 XCDs in turn), so
@@ -210,33 +212,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
   const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * (K >> 3), (u32)(rows_n * RB));
   const rsrc_t xr = make_rsrc(panel, (u32)(G * 128 * MR));
   const u32 xoff = r < MR ? (u32)((j * MR + r) * 16) : kOOB;   // rows >= MR: zero tokens
+  // outlier records of weight row r: unit q's two groups are 16 bytes at 16 q
+  const rsrc_t orr = OUTL ? make_rsrc(orec + (int64_t)n_base * G, (u32)(rows_n * G * 8)) : wr;
 
-  // 1. scales, zero points and token sums into LDS: kilobyte t of the three
-  // arrays by wave t mod WAVES.  A 16-byte load that runs past the end of
-  // its buffer range reads zeros for bytes inside it too (seen on MI355X),
-  // so the scales and zero points of a block cut short by N (2 G (N mod 16)
-  // bytes, not always a multiple of 16) go through registers element by
-  // element instead.
-  {
-    const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
-    const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
-    const rsrc_t tr = make_rsrc(tsum, (u32)(G * 64));
-    const int t0 = rows_n == 16 ? 0 : 2 * kb_sz;
-    for (int t = t0 + wave; t < 2 * kb_sz + kb_sum; t += WAVES) {
-      const u32 o = (u32)(1024 * (t < kb_sz ? t : t < 2 * kb_sz ? t - kb_sz : t - 2 * kb_sz) + 16 * lane);
-      if (t < kb_sz) dma16(sr, lds + 1024 * t, o);
-      else if (t < 2 * kb_sz) dma16(zr, lds + 1024 * t, o);
-      else dma16(tr, lds + 1024 * t, o);
-    }
-    if (rows_n < 16) {   // rows past N: zeros
-      uint16_t* sw = reinterpret_cast<uint16_t*>(lds);
-      uint16_t* zw = reinterpret_cast<uint16_t*>(lds + 1024 * kb_sz);
-      for (int el = tid; el < 16 * G; el += 64 * WAVES) {
-        sw[el] = bld2(sr, (u32)(2 * el));
-        zw[el] = bld2(zr, (u32)(2 * el));
-      }
-    }
-  }
+  // 1. scales, zero points and token sums into LDS
+  stage_block_sz<WAVES>(lds, make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2)),
+                        make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2)), rows_n, G,
+                        make_rsrc(tsum, (u32)(G * 64)), kb_sum);
   float sx[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (!kI32) {
 #pragma unroll
@@ -250,30 +232,66 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. every unit of the run: two whole-line DMAs (rows 8h..8h+7, lane l:
-  // row 8h + l/8, chunk (l % 8) ^ f(row)) and four token fragments
-  v4i tk[RING][2][2];
-#pragma unroll
-  for (int i = 0; i < RING; ++i) {
+  // row 8h + l/8, chunk (l % 8) ^ f(row)) and four token fragments.  With
+  // the outlier side path, whose operand building is VALU-heavy and needs no
+  // weights, the tokens and records of the whole run go first and the side
+  // sums are formed while the weights are still on their way.
+  v4i tk[RING][2][2], orc[OUTL ? RING : 1];
+  auto weights = [&](int i) {
     const int q = min(ub + i, ue - 1);   // past the run: the last unit again
-    int8_t* dst = ring + i * 2048;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 8 * h + (lane >> 3);
       const int ch = (lane & 7) ^ ((row >> 1) & 7);
       const u32 o = 128 * q + 16 * ch < RB ? (u32)(row * RB + 128 * q + 16 * ch) : kOOB;
-      dma16(wr, dst + 1024 * h, o);
+      dma16(wr, ring + i * 2048 + 1024 * h, o);
     }
+  };
+  auto tokens = [&](int i) {
+    const int q = min(ub + i, ue - 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int g = 2 * q + s;   // g == G (odd G): past the panel, zeros
 #pragma unroll
       for (int h = 0; h < 2; ++h) tk[i][s][h] = bld16(xr, xoff + (u32)((g * 2 + h) * 64 * MR));
     }
+    if constexpr (OUTL) orc[i] = bld16(orr, (u32)(r * G * 8 + 16 * q));
+  };
+#pragma unroll
+  for (int i = 0; i < RING; ++i) {
+    if constexpr (OUTL) {
+      tokens(i);
+    } else {
+      weights(i);
+      tokens(i);
+    }
+  }
+  if constexpr (OUTL) {
+#pragma unroll
+    for (int i = 0; i < RING; ++i) weights(i);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // the small arrays are older than every request of the run
-  wait_vmcnt(PU * RING);
+  // the small arrays are older than every request of the run (with the side
+  // path: than every weight request, the tokens and records too)
+  wait_vmcnt(OUTL ? 2 * RING : PU * RING);
   lds_barrier();
+  v4i oacc = {0, 0, 0, 0};
+  if constexpr (OUTL) {
+    // a repeated unit past the run adds nothing; a group past G has zero tokens
+#pragma unroll
+    for (int i = 0; i < RING; ++i) {
+      if (ub + i < ue) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const u32 lo = (u32)orc[i][2 * s], hi = (u32)orc[i][2 * s + 1];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            oacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                tk[i][s][h], outlier_operand_panel(lo, hi, 32 * j + 16 * h), oacc, 0, 0, 0);
+        }
+      }
+    }
+  }
 
   // 3. consume the units in issue order
   int rsl[2];
@@ -285,7 +303,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
   for (int i = 0; i < RING; ++i) {
     const bool live = ub + i < ue;
     const int q = min(ub + i, ue - 1);
-    wait_vmcnt(PU * (RING - 1 - i));
+    wait_vmcnt((OUTL ? 2 : PU) * (RING - 1 - i));
     const int8_t* slot = ring + i * 2048;
     const v4i f0 = *reinterpret_cast<const v4i*>(slot + rsl[0]);
     const v4i f1 = *reinterpret_cast<const v4i*>(slot + rsl[1]);
@@ -308,7 +326,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int m = 4 * j + e;
-            if (m < M) y[((int64_t)m * G + g) * N + n] = acc[e];
+            if (m < M) y[((int64_t)m * GY + g) * N + n] = acc[e];
           }
         }
       } else {
@@ -319,17 +337,34 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if constexpr (!kI32) {
-    red[wave][lane] = yacc;
+  if constexpr (!kI32) red[wave][lane] = yacc;
+  if constexpr (OUTL) redo[wave][lane] = oacc;
+  if constexpr (!kI32 || OUTL) {
     __syncthreads();
     if (tid < 64 && n < N) {
-      v4f sum = red[0][lane];
+      v4i osum = {0, 0, 0, 0};
+      if constexpr (OUTL) {
 #pragma unroll
-      for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+        for (int w = 0; w < WAVES; ++w) osum += redo[w][lane];
+      }
+      if constexpr (kI32) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 4 * j + e;
-        if (m < M) y[(int64_t)m * N + n] = Out<OutT>::cvt(sum[e] * sx[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int m = 4 * j + e;
+          if (m < M) y[((int64_t)m * GY + G) * N + n] = osum[e];
+        }
+      } else {
+        v4f sum = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+        const float s8 = OUTL ? os8[n] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 4 * j + e;
+          // y = s_x (sum_g s_g acc_g + s8 acc_o)
+          const float t = OUTL ? __builtin_fmaf(s8, (float)osum[e], sum[e]) : sum[e];
+          if (m < M) y[(int64_t)m * N + n] = Out<OutT>::cvt(t * sx[e]);
+        }
       }
     }
   }
@@ -404,32 +439,56 @@ hipError_t quant_panel_dt(const void* x, int M, int64_t K, int8_t* xq, float* xs
   return hipGetLastError();
 }
 
-template <int WAVES, typename OutT>
-void fdec_ring(int ring, const int8_t* panel, const int* sums, const float* xs, const int32_t* wq,
-               const uint16_t* ws, const uint16_t* wz, int M, int MR, int N, int K, OutT* y,
-               size_t lds, hipStream_t st) {
-  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * WAVES);
+// Operands of one panel GEMM launch (orec and os8 only for the outlier form).
+struct FdecArgs {
+  const int8_t* panel;
+  const int* sums;
+  const float* xs;
+  const int32_t* wq;
+  const uint16_t* ws;
+  const uint16_t* wz;
+  const uint64_t* orec;
+  const float* os8;
+  int M, N, K;
+};
+
+template <int WAVES, bool OUTL, typename OutT>
+void fdec_ring(int ring, const FdecArgs& a, OutT* y, size_t lds, hipStream_t st) {
+  const dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * WAVES);
+  const int MR = panel_rows(a.M);
+#define QG_FDEC(R)                                                                              \
+  k_w4a8_fdec<WAVES, R, OUTL, OutT><<<grid, block, lds, st>>>(a.panel, a.sums, a.xs, a.wq, a.ws, \
+                                                              a.wz, a.orec, a.os8, a.M, MR, a.N, \
+                                                              a.K, y)
   switch (ring) {
-    case 1: k_w4a8_fdec<WAVES, 1, OutT><<<grid, block, lds, st>>>(panel, sums, xs, wq, ws, wz, M, MR, N, K, y); break;
-    case 2: k_w4a8_fdec<WAVES, 2, OutT><<<grid, block, lds, st>>>(panel, sums, xs, wq, ws, wz, M, MR, N, K, y); break;
-    case 3: k_w4a8_fdec<WAVES, 3, OutT><<<grid, block, lds, st>>>(panel, sums, xs, wq, ws, wz, M, MR, N, K, y); break;
-    default: k_w4a8_fdec<WAVES, 4, OutT><<<grid, block, lds, st>>>(panel, sums, xs, wq, ws, wz, M, MR, N, K, y); break;
+    case 1: QG_FDEC(1); break;
+    case 2: QG_FDEC(2); break;
+    case 3: QG_FDEC(3); break;
+    default: QG_FDEC(4); break;
   }
+#undef QG_FDEC
 }
 
-template <typename OutT>
-hipError_t fdec_t(const GemmPlan& p, const int8_t* panel, const int* sums, const float* xs,
-                  const int32_t* wq, const uint16_t* ws, const uint16_t* wz, int M, int N, int K,
-                  OutT* y, hipStream_t st) {
-  const int MR = panel_rows(M);
+template <bool OUTL, typename OutT>
+hipError_t fdec_t(const GemmPlan& p, const FdecArgs& a, OutT* y, hipStream_t st) {
   switch (p.waves) {
-    case 16: fdec_ring<16, OutT>(p.ring, panel, sums, xs, wq, ws, wz, M, MR, N, K, y, p.lds, st); break;
-    case 8: fdec_ring<8, OutT>(p.ring, panel, sums, xs, wq, ws, wz, M, MR, N, K, y, p.lds, st); break;
-    case 4: fdec_ring<4, OutT>(p.ring, panel, sums, xs, wq, ws, wz, M, MR, N, K, y, p.lds, st); break;
-    case 2: fdec_ring<2, OutT>(p.ring, panel, sums, xs, wq, ws, wz, M, MR, N, K, y, p.lds, st); break;
-    default: fdec_ring<1, OutT>(p.ring, panel, sums, xs, wq, ws, wz, M, MR, N, K, y, p.lds, st); break;
+    case 16: fdec_ring<16, OUTL, OutT>(p.ring, a, y, p.lds, st); break;
+    case 8: fdec_ring<8, OUTL, OutT>(p.ring, a, y, p.lds, st); break;
+    case 4: fdec_ring<4, OUTL, OutT>(p.ring, a, y, p.lds, st); break;
+    case 2: fdec_ring<2, OUTL, OutT>(p.ring, a, y, p.lds, st); break;
+    default: fdec_ring<1, OUTL, OutT>(p.ring, a, y, p.lds, st); break;
   }
   return hipGetLastError();
+}
+
+template <bool OUTL>
+hipError_t fdec_y(const GemmPlan& p, const FdecArgs& a, void* y, int y_dtype, hipStream_t st) {
+  switch (y_dtype) {
+    case F32: return fdec_t<OUTL, float>(p, a, (float*)y, st);
+    case F16: return fdec_t<OUTL, _Float16>(p, a, (_Float16*)y, st);
+    case BF16: return fdec_t<OUTL, uint16_t>(p, a, (uint16_t*)y, st);
+    default: return fdec_t<OUTL, int32_t>(p, a, (int32_t*)y, st);
+  }
 }
 
 int* panel_sums(void* panel, int64_t K) {
@@ -462,16 +521,19 @@ hipError_t launch_quant_panel(const void* x, int x_dtype, int64_t M, int64_t K, 
 hipError_t launch_gemm_w4a8_panel(const void* panel, const float* xs, const int32_t* wq,
                                   const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
                                   int64_t K, void* y, int y_dtype, hipStream_t st) {
-  const GemmPlan p = plan_gemm(M, N, K);
-  const int8_t* pp = reinterpret_cast<const int8_t*>(panel);
-  const int* sums = panel_sums(const_cast<void*>(panel), K);
-  const int m = (int)M, n = (int)N, k = (int)K;
-  switch (y_dtype) {
-    case F32: return fdec_t<float>(p, pp, sums, xs, wq, ws, wz, m, n, k, (float*)y, st);
-    case F16: return fdec_t<_Float16>(p, pp, sums, xs, wq, ws, wz, m, n, k, (_Float16*)y, st);
-    case BF16: return fdec_t<uint16_t>(p, pp, sums, xs, wq, ws, wz, m, n, k, (uint16_t*)y, st);
-    default: return fdec_t<int32_t>(p, pp, sums, xs, wq, ws, wz, m, n, k, (int32_t*)y, st);
-  }
+  const FdecArgs a{reinterpret_cast<const int8_t*>(panel), panel_sums(const_cast<void*>(panel), K),
+                   xs, wq, ws, wz, nullptr, nullptr, (int)M, (int)N, (int)K};
+  return fdec_y<false>(plan_gemm(M, N, K), a, y, y_dtype, st);
+}
+
+hipError_t launch_gemm_w4a8_outl_panel(const void* panel, const float* xs, const int32_t* wq,
+                                       const uint16_t* ws, const uint16_t* wz,
+                                       const uint64_t* orec, const float* os8, int64_t M,
+                                       int64_t N, int64_t K, void* y, int y_dtype,
+                                       hipStream_t st) {
+  const FdecArgs a{reinterpret_cast<const int8_t*>(panel), panel_sums(const_cast<void*>(panel), K),
+                   xs, wq, ws, wz, orec, os8, (int)M, (int)N, (int)K};
+  return fdec_y<true>(plan_gemm(M, N, K), a, y, y_dtype, st);
 }
 
 hipError_t launch_quantize_gemm_w4a8(const void* x, int x_dtype, const int32_t* wq,

@@ -218,6 +218,76 @@ inline int wide_waves(int N) {
   return nb < 1 ? 1 : nb > 4 ? 4 : nb;
 }
 
+// s_waitcnt vmcnt(n) for an n known once the caller's loop is unrolled (the
+// switch folds to one case); n > 63 waits for everything.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define QG_WAITVM(i) case i: asm volatile("s_waitcnt vmcnt(" #i ")" ::: "memory"); break;
+    QG_WAITVM(0) QG_WAITVM(1) QG_WAITVM(2) QG_WAITVM(3) QG_WAITVM(4) QG_WAITVM(5) QG_WAITVM(6)
+    QG_WAITVM(7) QG_WAITVM(8) QG_WAITVM(9) QG_WAITVM(10) QG_WAITVM(11) QG_WAITVM(12)
+    QG_WAITVM(13) QG_WAITVM(14) QG_WAITVM(15) QG_WAITVM(16) QG_WAITVM(17) QG_WAITVM(18)
+    QG_WAITVM(19) QG_WAITVM(20) QG_WAITVM(21) QG_WAITVM(22) QG_WAITVM(23) QG_WAITVM(24)
+    QG_WAITVM(25) QG_WAITVM(26) QG_WAITVM(27) QG_WAITVM(28) QG_WAITVM(29) QG_WAITVM(30)
+    QG_WAITVM(31) QG_WAITVM(32) QG_WAITVM(33) QG_WAITVM(34) QG_WAITVM(35) QG_WAITVM(36)
+    QG_WAITVM(37) QG_WAITVM(38) QG_WAITVM(39) QG_WAITVM(40) QG_WAITVM(41) QG_WAITVM(42)
+    QG_WAITVM(43) QG_WAITVM(44) QG_WAITVM(45) QG_WAITVM(46) QG_WAITVM(47) QG_WAITVM(48)
+    QG_WAITVM(49) QG_WAITVM(50) QG_WAITVM(51) QG_WAITVM(52) QG_WAITVM(53) QG_WAITVM(54)
+    QG_WAITVM(55) QG_WAITVM(56) QG_WAITVM(57) QG_WAITVM(58) QG_WAITVM(59) QG_WAITVM(60)
+    QG_WAITVM(61) QG_WAITVM(62) QG_WAITVM(63)
+#undef QG_WAITVM
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// 16-byte buffer loads of every lane straight into LDS at lds + 16 lane (lds
+// wave-uniform).  dma16: non-temporal, for data read once per call (the
+// weights, their scales); dma16_keep: the default policy, for data other
+// workgroups read too.  The builtin sits in plain device functions so that
+// the host pass keeps the kernels that use it.
+#define QG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+__device__ __forceinline__ void dma16(rsrc_t r, int8_t* lds, u32 voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, QG_LDS(lds), 16, voff, 0, 0, kAuxNonTemporal);
+}
+__device__ __forceinline__ void dma16_keep(rsrc_t r, int8_t* lds, u32 voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, QG_LDS(lds), 16, voff, 0, 0, 0);
+}
+
+// Kilobytes of LDS that `chunks` 16-byte chunks take.
+__host__ __device__ constexpr int kb_of_chunks(int chunks) { return (chunks + 63) / 64; }
+
+// Scales and zero points of a 16-row weight block (rows_n rows of G fp16
+// values each, contiguous; rows past rows_n read as zeros) into LDS as
+// [16][G] arrays at lds and lds + 1024 kb (kb = kb_of_chunks(2 G)), then
+// extra_kb kilobytes of the resource xr at lds + 2048 kb; kilobyte t by wave
+// t mod WAVES with buffer-to-LDS loads, whose completion the caller waits
+// for (vmcnt) before its barrier.  Buffer range checks work per dword: a
+// dword only partly inside the range reads as zero, bytes inside it too
+// (seen on MI355X).  A block cut short by N (2 G rows_n bytes, not always a
+// multiple of 4) therefore stages its scales and zero points element by
+// element; the caller's barrier must then also wait for LDS stores
+// (lds_barrier).
+template <int WAVES>
+__device__ __forceinline__ void stage_block_sz(int8_t* lds, rsrc_t sr, rsrc_t zr, int rows_n,
+                                               int G, rsrc_t xr, int extra_kb) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = kb_of_chunks(2 * G);
+  const int t0 = rows_n == 16 ? 0 : 2 * kb;
+  for (int t = t0 + wave; t < 2 * kb + extra_kb; t += WAVES) {
+    const u32 o = (u32)(1024 * (t < kb ? t : t < 2 * kb ? t - kb : t - 2 * kb) + 16 * lane);
+    if (t < kb) dma16(sr, lds + 1024 * t, o);
+    else if (t < 2 * kb) dma16(zr, lds + 1024 * t, o);
+    else dma16(xr, lds + 1024 * t, o);
+  }
+  if (rows_n < 16) {
+    uint16_t* sw = reinterpret_cast<uint16_t*>(lds);
+    uint16_t* zw = reinterpret_cast<uint16_t*>(lds + 1024 * kb);
+    for (int el = (int)threadIdx.x; el < 16 * G; el += 64 * WAVES) {
+      sw[el] = bld2(sr, (u32)(2 * el));
+      zw[el] = bld2(zr, (u32)(2 * el));
+    }
+  }
+}
+
 // Barrier for LDS data written by the workgroup: waits for this wave's LDS
 // accesses only, leaving its global loads in flight.
 __device__ __forceinline__ void lds_barrier() {

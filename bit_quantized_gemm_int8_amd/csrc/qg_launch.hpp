@@ -40,6 +40,11 @@ hipError_t launch_quant_panel(const void* x, int x_dtype, int64_t M, int64_t K, 
 hipError_t launch_gemm_w4a8_panel(const void* panel, const float* xs, const int32_t* wq,
                                   const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
                                   int64_t K, void* y, int y_dtype, hipStream_t st);
+hipError_t launch_gemm_w4a8_outl_panel(const void* panel, const float* xs, const int32_t* wq,
+                                       const uint16_t* ws, const uint16_t* wz,
+                                       const uint64_t* orec, const float* os8, int64_t M,
+                                       int64_t N, int64_t K, void* y, int y_dtype,
+                                       hipStream_t st);
 // Quantize + W4A8: the panel pair where quantize_gemm_w4a8_workspace > 0
 // (workspace of that size), else the two plain kernels in sequence.
 hipError_t launch_quantize_gemm_w4a8(const void* x, int x_dtype, const int32_t* wq,

@@ -359,6 +359,28 @@ qg_status_t gemm_w4a8_g128_outliers(const int8_t* xq, const float* x_scale, cons
                                     void* stream);
 
 /*
+ * gemm_w4a8_g128_outliers reading the token panel of
+ * quantize_per_token_i8_panel instead of xq.
+ * 「LLM推理降本五要素」 §2.2 (INT8 outlier side path); 「第4章：量化」 §1.1, §3.5.
+ *   acc, acc_o and y exactly as gemm_w4a8_g128_outliers(xq, x_scale, ...)
+ *   for the xq the panel was written from: acc and acc_o bit for bit, y
+ *   within the same rounding bound.
+ * panel: written by quantize_per_token_i8_panel with the same M and K, read;
+ *   panel_bytes its size.
+ * Other arguments as gemm_w4a8_g128_outliers; sizes as
+ * quantize_per_token_i8_panel (1 <= M <= 16, K <= 16384; else QG_ERR_SHAPE);
+ * N >= 0.  Measured on MI355X against gemm_w4a8_g128_outliers: 20-27%
+ * faster at 1-8 token rows; at 16 rows of K = 11008 slower (14.6 against
+ * 12.8 us), where building the outlier operands bounds it.
+ */
+qg_status_t gemm_w4a8_g128_outliers_panel(const void* panel, int64_t panel_bytes,
+                                          const float* x_scale, const int32_t* wq,
+                                          const uint16_t* w_scale_f16,
+                                          const uint16_t* w_zero_f16, const uint64_t* w_out_rec,
+                                          const float* w_out_scale, int64_t M, int64_t N,
+                                          int64_t K, void* y, int y_dtype, void* stream);
+
+/*
  * 2:4 structured-sparse uint4 weights (offline): of every 4 consecutive input
  * channels of an output channel the 2 of largest |w| are kept (equal
  * magnitudes to the lower index), and the 64 kept weights of each group of 128

@@ -43,7 +43,9 @@ def test_header_declares_the_entry_points():
               "quantize_weight_u4_g128_outliers", "gemm_w4a8_g128_outliers",
               "quantize_weight_u4_g128_sparse24", "gemm_w4a8_g128_sparse24",
               "quantize_gemm_w8a8", "quantize_gemm_w8a8_plan", "quantize_gemm_w4a8_g128",
-              "quantize_gemm_w4a8_g128_workspace_bytes", "quantize_gemm_w4a8_g128_noalloc"]:
+              "quantize_gemm_w4a8_g128_workspace_bytes", "quantize_gemm_w4a8_g128_noalloc",
+              "quantize_per_token_i8_panel", "gemm_w4a8_g128_panel",
+              "gemm_w4a8_g128_outliers_panel"]:
         assert n in names, n
 
 
@@ -269,6 +271,15 @@ def test_panel_validation_codes():
     assert gp(A, pbytes, A, A, A, None, 4, 64, 4096, A, 2, None) == NULL   # zero points
     assert gp(MIS, pbytes, A, A, A, A, 4, 64, 4096, A, 2, None) == ALIGN
     assert gp(None, 0, None, None, None, None, 4, 0, 4096, None, 2, None) == OK
+    go = lib.gemm_w4a8_g128_outliers_panel
+    go.argtypes = [P, I64, P, P, P, P, P, P, I64, I64, I64, P, ctypes.c_int, P]
+    assert go(A, pbytes - 16, A, A, A, A, A, A, 4, 64, 4096, A, 2, None) == SHAPE
+    assert go(A, 10 ** 7, A, A, A, A, A, A, 4, 64, 16512, A, 2, None) == SHAPE   # K > 16384
+    assert go(A, pbytes, A, A, A, A, A, A, 4, 64, 4096, A, 9, None) == DTYPE
+    assert go(A, pbytes, A, A, A, A, None, A, 4, 64, 4096, A, 2, None) == NULL   # records
+    assert go(A, pbytes, A, A, A, A, A, None, 4, 64, 4096, A, 2, None) == NULL   # s8 unless I32
+    assert go(A, pbytes, A, A, A, A, MIS, A, 4, 64, 4096, A, 2, None) == ALIGN
+    assert go(None, 0, None, None, None, None, None, None, 0, 64, 4096, None, 2, None) == OK
 
 
 def test_binding_rejects_host_tensors():

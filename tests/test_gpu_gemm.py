@@ -186,7 +186,12 @@ def _w4a16_floor(x64, packed, sc, zz):
                                    (2, 48, 14336), (48, 10256, 512), (64, 512, 4096),
                                    # 12-wave workgroups over 3 and 4 weight blocks
                                    # (more blocks than 2 per CU), the last ragged
-                                   (8, 12288, 4096), (6, 11000, 4096), (7, 16384, 4096)])
+                                   (8, 12288, 4096), (6, 11000, 4096), (7, 16384, 4096),
+                                   # 1-4 rows: one group, odd group counts, a ragged
+                                   # last block past 256 blocks, long K
+                                   (1, 17, 128), (3, 40, 640), (4, 4100, 4096),
+                                   (1, 4096, 11008), (2, 1000, 4224), (1, 40, 12288),
+                                   (4, 64, 1152)])
 def test_w4a16(xfmt, fmt, M, N, K):
     rng = np.random.default_rng(M * 5 + N + K)
     packed, sc, zz = _u4_weights(rng, K, N)

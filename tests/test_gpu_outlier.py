@@ -161,3 +161,52 @@ def test_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+
+
+# the panel form: the same accumulators (and side sum) bit for bit, from the
+# token panel of quantize_per_token_i8_panel
+PANEL_SHAPES = [(1, 16, 128), (3, 33, 384), (16, 64, 1024), (5, 100, 2048), (16, 4096, 11008),
+                (2, 4100, 4096), (8, 40, 16384), (1, 12288, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", PANEL_SHAPES)
+def test_panel_gemm_acc_bitwise(M, N, K):
+    w = _weights(M + N + K + 1, K, N)
+    p, s, z, r, s8 = oracle.quantize_weight_u4_g128_outliers(w)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(M * 7 + K)
+    x = (torch.randn((M, K), generator=g, device="cuda") * 3).to(torch.bfloat16)
+    print(f"outlier panel gemm acc M={M} N={N} K={K}", flush=True)
+    panel, xq, xs = qg.quantize_per_token_i8_panel(x)
+    acc = qg.gemm_w4a8_g128_outliers_panel(panel, None, to_dev(p), None, to_dev(z),
+                                           to_dev(r.view(np.int64)), None, M,
+                                           out_dtype=torch.int32)
+    acc2 = qg.gemm_w4a8_g128_outliers(xq, None, to_dev(p), None, to_dev(z),
+                                      to_dev(r.view(np.int64)), None, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    assert torch.equal(acc, acc2)
+    if M * N * K <= 16 * 4096 * 4096:
+        got, xq_np = to_np(acc), to_np(xq)
+        G = K // 128
+        np.testing.assert_array_equal(got[:, :G, :], oracle.gemm_w4a8_g128_acc(xq_np, p, z))
+        np.testing.assert_array_equal(got[:, G, :], oracle.gemm_w4a8_g128_outlier_acc(xq_np, r))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(3, 33, 384), (16, 4096, 11008)])
+def test_panel_gemm_scaled(fmt, M, N, K):
+    w = _weights(M + 2 * N + K, K, N)
+    p, s, z, r, s8 = oracle.quantize_weight_u4_g128_outliers(w)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(M + K)
+    x = (torch.randn((M, K), generator=g, device="cuda") * 3).to(torch.bfloat16)
+    print(f"outlier panel gemm scaled M={M} N={N} K={K} {fmt}", flush=True)
+    panel, xq, xs = qg.quantize_per_token_i8_panel(x)
+    out = {"bf16": torch.bfloat16, "f32": torch.float32}[fmt]
+    y = qg.gemm_w4a8_g128_outliers_panel(panel, xs, to_dev(p), to_dev(s), to_dev(z),
+                                         to_dev(r.view(np.int64)), to_dev(s8), M, out_dtype=out)
+    torch.cuda.synchronize()
+    xq_np, xs_np = to_np(xq), to_np(xs)
+    yref = oracle.gemm_w4a8_g128_outliers(xq_np, xs_np, p, s, z, r, s8)
+    assert_close(out_f64(y), yref, fmt, floor=_floor(xq_np, xs_np, p, s, z, r, s8),
+                 what=f"outlier panel {fmt}")
