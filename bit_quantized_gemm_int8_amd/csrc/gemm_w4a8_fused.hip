@@ -11,10 +11,11 @@
 // instructions -- all of it repeated by every workgroup of the layer.  Here
 // the quantizer does that once: besides the codes and scales it writes
 //   * a token panel: the codes of group g, half h (k = 128 g + 16 h ...) in
-//     MFMA operand order, panel[g][h][j][r] = the 16 codes of row r at
+//     MFMA operand order, panel[g][h][r][j] = the 16 codes of row r at
 //     k = 128 g + 32 j + 16 h + [0, 16), bytes permuted to the order in which
 //     the packed weights unpack (even k of each 8 first, then odd k), so a
-//     wave reads one operand as one contiguous kilobyte (whole lines);
+//     wave reads one operand as one contiguous kilobyte (whole lines) and a
+//     row's codes of one (g, h) are 64 contiguous bytes;
 //   * the token sums sums[g][r] = sum_{k in g} xq[r, k] (exact int32), which
 //     carry the zero point: acc = sum xq q - z sum xq.
 // Both live in device memory the caller provides; one panel can feed several
@@ -97,18 +98,24 @@ __device__ __forceinline__ int byte_sum16(v4i v) {
 
 }  // namespace
 
-// Panel layout (both kernels): panel[g][h][j][r], 16 bytes each, r < MR
+// Panel layout (both kernels): panel[g][h][r][j], 16 bytes each, r < MR
 // (MR = M rounded up to 1, 2, 4, 8 or 16), then the token sums sums[g][16]
 // int32 at byte offset 2048 G: G (2048 + 64) bytes whatever M.
 constexpr int kPanelRows = 16;
 
 // ---------------------------------------------------------------------------
-// Quantizer: one workgroup of NT threads per panel row (MR of them), the row
-// in registers.  Rows < M get the codes and scales of k_quant_per_token (same
+// Quantizer: one workgroup of NT threads per panel row, the row in
+// registers.  Rows < M get the codes and scales of k_quant_per_token (same
 // loads, scale, reciprocal and sym_code_t) and are written to xq (unless it
 // is NULL), x_scale, the panel and the sums; rows M..MR-1 write zero codes
-// and sums to the panel only (workgroup 0 also zeroes sum rows MR..15), so
-// that every byte of the panel is defined.
+// and sums to the panel only (row 0 also zeroes sum rows MR..15), so that
+// every byte of the panel is defined.  The grid is 16 workgroups whatever
+// MR, workgroup b taking row 2 (b mod 8) + b / 8 (those past MR exit): the
+// two rows that share each 128-byte panel line then run on one XCD
+// (workgroups are dealt to the 8 XCDs in turn) and the line is completed in
+// that XCD's L2 instead of being written in pieces from two.  Measured on
+// MI355X (16 rows of K = 11008), 16-byte stores from rows spread over all
+// XCDs made this kernel 0.6 us slower than the plain quantizer.
 // ---------------------------------------------------------------------------
 template <int DT, int CH, int NT>
 __global__ __launch_bounds__(NT) void k_quant_panel(const void* __restrict__ x, int M, int64_t K,
@@ -116,7 +123,8 @@ __global__ __launch_bounds__(NT) void k_quant_panel(const void* __restrict__ x, 
                                                     float* __restrict__ xs,
                                                     int8_t* __restrict__ panel, int* __restrict__ sums) {
   __shared__ float red[NT / kWave];
-  const int row = blockIdx.x;
+  const int row = 2 * (int)(blockIdx.x & 7) + (int)(blockIdx.x >> 3);
+  if (row >= MR) return;   // the whole workgroup: before any barrier
   const bool real = row < M;
   const char* xr = reinterpret_cast<const char*>(x) + (real ? (int64_t)row * K * esize<DT>() : 0);
   const int nch = (int)(K >> 4);
@@ -150,7 +158,7 @@ __global__ __launch_bounds__(NT) void k_quant_panel(const void* __restrict__ x, 
     if (idx < nch) {
       if (real && xq) st16(xq + (int64_t)row * K + (int64_t)idx * 16, code);
       const int g = idx >> 3, j = (idx & 7) >> 1, h = idx & 1;
-      st16(panel + ((((int64_t)g * 2 + h) * 4 + j) * MR + row) * 16, panel_order16(code));
+      st16(panel + ((((int64_t)g * 2 + h) * MR + row) * 4 + j) * 16, panel_order16(code));
       if ((idx & 7) == 0) {
         sums[g * kPanelRows + row] = t;
         if (row == 0)   // sum rows past the panel rows: zeros too
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_fdec(
   const int rows_n = min(16, N - n_base);
   const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * (K >> 3), (u32)(rows_n * RB));
   const rsrc_t xr = make_rsrc(panel, (u32)(G * 128 * MR));
-  const u32 xoff = r < MR ? (u32)((j * MR + r) * 16) : kOOB;   // rows >= MR: zero tokens
+  const u32 xoff = r < MR ? (u32)((r * 4 + j) * 16) : kOOB;   // rows >= MR: zero tokens
   // outlier records of weight row r: unit q's two groups are 16 bytes at 16 q
   const rsrc_t orr = OUTL ? make_rsrc(orec + (int64_t)n_base * G, (u32)(rows_n * G * 8)) : wr;
 
@@ -415,13 +423,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
-// When quantize_gemm_w4a8 takes the panel path (measured on MI355X against
-// the per-token quantizer + plain W4A8 kernel: 16 rows of K = 11008,
-// N = 4096 and of K = 4096, N = 11008 12-20% faster, one row of K = 4096,
-// N = 12288 12% faster; one row of K = 11008, N = 4096 slower, so one row
-// on at most 256 weight blocks keeps the plain kernel).
+// When quantize_gemm_w4a8 takes the panel pair: on layers of more than 256
+// 16-row weight blocks.  Measured on MI355X, whole steps (quantizer + GEMM)
+// against the per-token quantizer + plain W4A8 kernel, weights rotated
+// through 600 MB: K = 4096, N = 11008: 1-8 rows 7-9% faster, 16 rows level;
+// N = 12288, 1 row 7% faster.  On 256 blocks or fewer the pair was slower
+// at every size tried (K = 11008, N = 4096: 6-11%; K = 4096, N = 4096: 2-6%):
+// the panel quantizer costs ~0.4 us more than the plain one, more than the
+// panel GEMM gains there.
 bool use_panel(int64_t M, int64_t N, int64_t K) {
-  return plan_gemm(M, N, K).ok && !(M == 1 && (N + 15) / 16 <= 256);
+  return plan_gemm(M, N, K).ok && (N + 15) / 16 > 256;
 }
 
 template <int DT>
@@ -429,7 +440,7 @@ hipError_t quant_panel_dt(const void* x, int M, int64_t K, int8_t* xq, float* xs
                           int* sums, hipStream_t st) {
   const int64_t nch = K / 16;   // K <= 16384: at most 1024 chunks
   const int MR = panel_rows(M);
-  const dim3 grid((unsigned)MR);
+  const dim3 grid((unsigned)kPanelRows);
   if (nch <= 256)
     k_quant_panel<DT, 1, 256><<<grid, 256, 0, st>>>(x, M, K, MR, xq, xs, panel, sums);
   else if (nch <= 512)

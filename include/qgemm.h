@@ -213,7 +213,7 @@ qg_status_t gemm_w4a8_g128(const int8_t* xq, const float* x_scale, const int32_t
  *   panel: device memory of panel_bytes bytes, 16-byte aligned, owned by the
  *     caller, written (contents on entry ignored).  Layout, for G = K / 128
  *     and m = M rounded up to 1, 2, 4, 8 or 16: bytes [0, 128 m G) hold
- *     16-byte entries [g][h][j][r] (g < G, h < 2, j < 4, r < m), entry =
+ *     16-byte entries [g][h][r][j] (g < G, h < 2, r < m, j < 4), entry =
  *     codes of row r at k = 128 g + 32 j + 16 h + i in the order
  *     i = 0 2 4 6 1 3 5 7 8 10 12 14 9 11 13 15 (the order in which a packed
  *     word's eight codes unpack; rows M..m-1: zeros); bytes
@@ -271,8 +271,9 @@ qg_status_t gemm_w4a8_g128_panel(const void* panel, int64_t panel_bytes, const f
  *   workspace as the panel, where it is 0 quantize_per_token_i8 then
  *   gemm_w4a8_g128, and workspace may be NULL.  Smaller than required:
  *   QG_ERR_SHAPE; NULL while required: QG_ERR_NULL.
- * The panel pair runs for 1 <= M <= 16 and K <= 16384, except one token row
- * on N <= 4096 (measured faster with the plain kernel).
+ * The panel pair runs for 1 <= M <= 16 and K <= 16384 on N > 4096 (more than
+ * 256 blocks of 16 output channels); on narrower layers the plain kernels
+ * measured faster per call.
  * K must be a positive multiple of 128 with K / 128 <= 65535.  N == 0
  * computes xq and x_scale only.
  */

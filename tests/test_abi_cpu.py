@@ -205,24 +205,22 @@ def test_fused_plan_on_the_host():
 
 def test_w4a8_workspace_on_the_host():
     """quantize_gemm_w4a8_g128_workspace_bytes: (K / 128) x 2112 bytes where
-    the panel pair runs (1..16 rows, K <= 16384, except one row on N <= 4096),
-    0 where the call runs the two plain kernels; the panel's own size."""
+    the panel pair runs (1..16 rows, K <= 16384, more than 256 blocks of 16
+    channels), 0 where the call runs the two plain kernels; the panel's own
+    size."""
     import bit_quantized_gemm_int8_amd as q
     _lib()
     wb = q.quantize_gemm_w4a8_g128_workspace_bytes
-    assert wb(16, 4096, 11008) == 86 * 2112
+    assert wb(16, 4112, 11008) == 86 * 2112           # 257 weight blocks: the panel pair
     assert wb(16, 11008, 4096) == 32 * 2112
-    assert wb(1, 12288, 4096) == 32 * 2112           # one row, more than 256 weight blocks
-    assert wb(1, 4112, 4096) == 32 * 2112
-    assert wb(1, 4096, 11008) == 0                    # one row, 256 blocks: the plain kernel
-    assert wb(2, 4096, 11008) == 86 * 2112
-    assert wb(3, 100, 2048) == 16 * 2112
-    assert wb(9, 40, 640) == 5 * 2112
-    assert wb(2, 48, 16384) == 128 * 2112             # the longest K
-    assert wb(2, 48, 16512) == 0
-    assert wb(17, 4096, 4096) == 0                    # past 16 rows
-    assert wb(0, 4096, 4096) == 0 and wb(4, 0, 4096) == 0
-    assert wb(4, 64, 200) == 0 and wb(-1, 64, 256) == 0
+    assert wb(1, 12288, 4096) == 32 * 2112
+    assert wb(2, 4112, 16384) == 128 * 2112           # the longest K
+    assert wb(2, 4112, 16512) == 0
+    assert wb(16, 4096, 11008) == 0                   # 256 blocks: the plain kernels
+    assert wb(1, 4096, 4096) == 0 and wb(3, 100, 2048) == 0
+    assert wb(17, 8192, 4096) == 0                    # past 16 rows
+    assert wb(0, 8192, 4096) == 0 and wb(4, 0, 4096) == 0
+    assert wb(4, 8192, 200) == 0 and wb(-1, 8192, 256) == 0
     pb = q.quantize_per_token_i8_panel_bytes
     assert pb(1, 128) == 2112 and pb(16, 16384) == 128 * 2112 and pb(5, 4096) == 32 * 2112
     assert pb(17, 4096) == 0 and pb(0, 4096) == 0 and pb(4, 16512) == 0 and pb(4, 200) == 0

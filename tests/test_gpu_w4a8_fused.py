@@ -1,11 +1,13 @@
 """GPU parity of the quantize + W4A8 call (quantize_gemm_w4a8_g128).
 
 Its codes and scales must be those of quantize_per_token_i8 and its int32
-per-group accumulators those of gemm_w4a8_g128, bit for bit, on the panel
-pair (quantize_per_token_i8_panel + gemm_w4a8_g128_panel, the workspace as
-the panel) and on the two-kernel fallback; scaled outputs are held to the
-oracle with the W4A8 rounding bound.  The panel's layout is checked byte for
-byte against its documented definition.
+per-group accumulators those of gemm_w4a8_g128, bit for bit, whichever form
+the library picks (the panel pair quantize_per_token_i8_panel +
+gemm_w4a8_g128_panel on layers of more than 256 weight blocks, the plain
+kernels otherwise); the panel pair is also run explicitly on every shape the
+panel takes.  Scaled outputs are held to the oracle with the W4A8 rounding
+bound.  The panel's layout is checked byte for byte against its documented
+definition.
 """
 import numpy as np
 import pytest
@@ -44,11 +46,10 @@ def _floor(xq, sx, packed, sc, zz):
     return (acc.shape[1] + 10) * 2.0 ** -24 * B
 
 
-# panel shapes: every panel row class (1, 2, 4, 8, 16 rows), 16, 8, 4, 2 and
-# 1 waves, runs of 1..4 units, odd group counts (a unit's second group past
-# K), half a unit (K = 128), more than 256 weight blocks, ragged N, the
-# longest K (16384); two-kernel shapes: one row on at most 256 blocks, 17
-# rows, K > 16384
+# every panel row class (1, 2, 4, 8, 16 rows), 16, 8, 4, 2 and 1 waves,
+# runs of 1..4 units, odd group counts (a unit's second group past K), half a
+# unit (K = 128), more and fewer than 256 weight blocks, ragged N, the longest
+# K the panel takes (16384); past it: 17 rows, K > 16384
 SHAPES = [(16, 4096, 11008), (16, 11008, 4096), (1, 12288, 4096), (3, 100, 2048),
           (5, 17, 1152), (2, 48, 14336), (8, 33, 16384), (4, 8200, 16384), (12, 300, 1024),
           (7, 1000, 896), (9, 520, 4224), (6, 16, 2432), (9, 40, 640), (3, 40, 256),
@@ -72,13 +73,19 @@ def test_codes_and_group_acc_bitwise(M, N, K, xdt):
     assert torch.equal(xs, xs2)
     assert torch.equal(xq, xq2)
     assert torch.equal(acc, acc2)
+    if qg.quantize_per_token_i8_panel_bytes(M, K):   # the panel pair, whatever the choice
+        panel, xq3, xs3 = qg.quantize_per_token_i8_panel(x)
+        acc3 = qg.gemm_w4a8_g128_panel(panel, None, wq, None, z_d, M, out_dtype=torch.int32)
+        torch.cuda.synchronize()
+        assert torch.equal(xq3, xq2) and torch.equal(xs3, xs2)
+        assert torch.equal(acc3, acc2)
     if M * N * K <= 16 * 4096 * 4096:
         np.testing.assert_array_equal(to_np(acc), oracle.gemm_w4a8_g128_acc(to_np(xq), packed, zz))
 
 
 @pytest.mark.parametrize("ydt", ["bf16", "f32", "f16"])
-@pytest.mark.parametrize("M,N,K", [(16, 4096, 11008), (1, 12288, 4096), (5, 17, 1152),
-                                   (4, 8200, 16384), (9, 40, 640)])
+@pytest.mark.parametrize("M,N,K", [(8, 11008, 4096), (1, 12288, 4096), (4, 8200, 16384),
+                                   (16, 4096, 11008), (9, 40, 640)])
 def test_scaled_against_oracle(ydt, M, N, K):
     rng = np.random.default_rng(3 * M + N + K)
     packed, sc, zz = _weights(rng, K, N)
@@ -113,23 +120,30 @@ def test_input_dtypes(xdt):
 def test_dirty_workspace_and_smaller_second_call():
     """Panel rows past M are written by the quantizer, not left over: a
     workspace full of stale bytes, then reused by a call with fewer rows,
-    gives the same accumulators."""
-    N, K = 2048, 4096
+    gives the same accumulators (one-call form and the explicit pair)."""
+    N, K = 4160, 4096
     rng = np.random.default_rng(5)
     packed, sc, zz = _weights(rng, K, N)
     wq, z_d = to_dev(packed), to_dev(zz)
-    ws = torch.randint(0, 256, (qg.quantize_gemm_w4a8_g128_workspace_bytes(16, N, K),),
-                       dtype=torch.uint8, device="cuda")
+    nbytes = qg.quantize_gemm_w4a8_g128_workspace_bytes(16, N, K)
+    assert nbytes == qg.quantize_per_token_i8_panel_bytes(16, K) > 0
+    ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
     for M in (16, 3):
         x = _x(40 + M, M, K, "bf16")
         acc, xq, _ = qg.quantize_gemm_w4a8_g128(x, wq, None, z_d, out_dtype=torch.int32,
                                                 workspace=ws)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(to_np(acc), oracle.gemm_w4a8_g128_acc(to_np(xq), packed, zz))
+        ref = oracle.gemm_w4a8_g128_acc(to_np(xq), packed, zz)
+        np.testing.assert_array_equal(to_np(acc), ref)
+        ws.random_(0, 256)
+        qg.quantize_per_token_i8_panel(x, panel=ws)
+        acc2 = qg.gemm_w4a8_g128_panel(ws, None, wq, None, z_d, M, out_dtype=torch.int32)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(acc2), ref)
 
 
 def test_workspace_too_small_is_rejected():
-    M, N, K = 4, 4096, 4096
+    M, N, K = 4, 8192, 4096
     x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
     wq = torch.zeros((N, K // 8), dtype=torch.int32, device="cuda")
     z = torch.zeros((N, K // 128), dtype=torch.float16, device="cuda")
@@ -151,7 +165,7 @@ def test_codes_only_when_n_is_zero():
 
 
 def test_graph_replay():
-    M, N, K = 16, 4096, 11008
+    M, N, K = 8, 11008, 4096
     rng = np.random.default_rng(9)
     packed, sc, zz = _weights(rng, K, N)
     wq, s_d, z_d = to_dev(packed), to_dev(sc), to_dev(zz)
@@ -175,7 +189,7 @@ def test_graph_replay():
 
 def _panel_expected(xq, M, K):
     """The documented panel layout, assembled from the codes: entries
-    [g][h][j][r] of the 16 codes at k = 128 g + 32 j + 16 h + i in the order
+    [g][h][r][j] of the 16 codes at k = 128 g + 32 j + 16 h + i in the order
     i = 0 2 4 6 1 3 5 7 8 10 12 14 9 11 13 15, rows up to M rounded to a
     power of two (zeros past M), then int32 sums [g][16]."""
     G = K // 128
@@ -184,7 +198,7 @@ def _panel_expected(xq, M, K):
     rows = np.zeros((m, K), np.int8)
     rows[:M] = xq
     t = rows.reshape(m, G, 4, 2, 16)[..., order]           # [r][g][j][h][i]
-    panel = t.transpose(1, 3, 2, 0, 4).reshape(-1)          # [g][h][j][r][i]
+    panel = t.transpose(1, 3, 0, 2, 4).reshape(-1)          # [g][h][r][j][i]
     sums = np.zeros((G, 16), np.int32)
     sums[:, :M] = xq.astype(np.int32).reshape(M, G, 128).sum(axis=2).T
     return panel.view(np.uint8), sums
