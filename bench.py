@@ -687,13 +687,14 @@ def measured_peaks(steps):
 # ------------------------------------------------------------ batch sweep
 
 SWEEP_LAYERS = (("w8a8", 4096, 11008, "bf16"), ("w4a8", 11008, 4096, "bf16"),
-                ("w4a16", 4096, 12288, "f16"))
+                ("w4a8", 4096, 11008, "bf16"), ("w4a16", 4096, 12288, "f16"))
 SWEEP_M = (1, 2, 4, 8, 16, 32, 64)
 
 
 def batch_sweep(steps):
     """Decode-to-prefill crossover: each path's linear layer (activation
-    quantization + GEMM; W4A16 the GEMM alone) at M = 1..64 tokens, next to an
+    quantization + GEMM through the library's one-call entry points; W4A16
+    the GEMM alone) at M = 1..64 tokens, next to an
     fp16 dense GEMM of the same K x N layer (torch.matmul, i.e. the vendor
     BLAS) on fp16 weights.  Seeded random inputs; weights rotate over more
     than 600 MB of copies in both cases so they stream from HBM."""
