@@ -303,7 +303,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
   u32* szl = reinterpret_cast<u32*>(smem + MR * xpitch);
 
   const int rows_n = min(16, N - n_base);
-  const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * Kw, (u32)(rows_n * RB));
+  const rsrc_t wr = make_rsrc_uniform(wq + (int64_t)n_base * Kw, (u32)(rows_n * RB));
   const UnitLanes ul = unit_lanes(lane, RB);
 
   v4i b0[UB][2], b1[UB][2];
@@ -311,8 +311,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
   // behind it the phase's first weight batch
   ScaleZeroStage<kThreads, 4> sz;
   const int srows = min(16 * nb, N - 16 * bb0);   // the workgroup's weight rows
-  const rsrc_t sr = make_rsrc(wscale + (int64_t)16 * bb0 * G, (u32)(srows * G * 2));
-  const rsrc_t zr = make_rsrc(wzero + (int64_t)16 * bb0 * G, (u32)(srows * G * 2));
+  const rsrc_t sr = make_rsrc_uniform(wscale + (int64_t)16 * bb0 * G, (u32)(srows * G * 2));
+  const rsrc_t zr = make_rsrc_uniform(wzero + (int64_t)16 * bb0 * G, (u32)(srows * G * 2));
   sz.load(sr, zr, 16 * nb * G, 0);
   const rsrc_t xr = make_rsrc(x, (u32)(M * K * 2));
 
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(64 * NB) void k_w4a16_wide(
   const int phases = (units + PU - 1) / PU;
 
   const int rows_n = max(0, min(16, N - n_base));
-  const rsrc_t wr = make_rsrc(wq + (int64_t)min(n_base, N - 1) * Kw, (u32)(rows_n * RB));
+  const rsrc_t wr = make_rsrc_uniform(wq + (int64_t)min(n_base, N - 1) * Kw, (u32)(rows_n * RB));
   const rsrc_t xr = make_rsrc(x, (u32)(M * K * 2));
   const UnitLanes ul = unit_lanes(lane, RB);
 
@@ -457,8 +457,8 @@ __global__ __launch_bounds__(64 * NB) void k_w4a16_wide(
   // scales and zero points of the workgroup's 16 NB rows, with the first
   // weight batch issued behind their loads
   const int wg_rows = max(0, min(16 * NB, N - wg_row0));
-  const rsrc_t sr = make_rsrc(wscale + (int64_t)min(wg_row0, N - 1) * G, (u32)(wg_rows * G * 2));
-  const rsrc_t zr = make_rsrc(wzero + (int64_t)min(wg_row0, N - 1) * G, (u32)(wg_rows * G * 2));
+  const rsrc_t sr = make_rsrc_uniform(wscale + (int64_t)min(wg_row0, N - 1) * G, (u32)(wg_rows * G * 2));
+  const rsrc_t zr = make_rsrc_uniform(wzero + (int64_t)min(wg_row0, N - 1) * G, (u32)(wg_rows * G * 2));
   ScaleZeroStage<kThreads, 4> sz;
   sz.load(sr, zr, 16 * NB * G, 0);
   __builtin_amdgcn_sched_barrier(0);

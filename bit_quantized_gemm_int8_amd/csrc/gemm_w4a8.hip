@@ -589,7 +589,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec2(
   for (int b = 0; b < 2; ++b) {
     const int nb = n0 + 16 * b;
     const int rows = max(0, min(16, N - nb));
-    wr[b] = make_rsrc(wq + (int64_t)min(nb, N) * Kw, (u32)(rows * RB));
+    wr[b] = make_rsrc_uniform(wq + (int64_t)min(nb, N) * Kw, (u32)(rows * RB));
   }
   const UnitLanes ul = unit_lanes(lane, RB);
   const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
@@ -610,8 +610,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec2(
   Batch b0, b1;
   ScaleZeroStage<kThreads, 4> sz;
   const int srows = max(0, min(32, N - n0));
-  const rsrc_t sr = make_rsrc(wscale + (int64_t)min(n0, N) * G, (u32)(srows * G * 2));
-  const rsrc_t zr = make_rsrc(wzero + (int64_t)min(n0, N) * G, (u32)(srows * G * 2));
+  const rsrc_t sr = make_rsrc_uniform(wscale + (int64_t)min(n0, N) * G, (u32)(srows * G * 2));
+  const rsrc_t zr = make_rsrc_uniform(wzero + (int64_t)min(n0, N) * G, (u32)(srows * G * 2));
   sz.load(sr, zr, 32 * G, 0);
   __builtin_amdgcn_sched_barrier(0);
   load(b0, ub);
@@ -685,6 +685,187 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec2(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide kernel (17-64 token rows on layers of at least 384 weight blocks): as
+// k_w8a8_wide / k_w4a16_wide, a workgroup of NB waves owns NB 16-row weight
+// blocks, one per wave over the whole K, and the waves move through K in
+// phases of PU units (2 PU groups).  A phase's token rows (16 MT rows x
+// 256 PU bytes) are staged once in LDS for all NB waves, each 16-byte chunk
+// already permuted to the unpack order, and the per-(group, row) token sums
+// that carry the zero point are formed while staging (byte sums reduced over
+// the 8 lanes that hold a group's chunks); two-deep ring, one barrier per
+// phase.  The weight stream runs WR phases ahead in a register ring: with one
+// wave per SIMD nothing else hides its latency.  Each unpacked weight fragment
+// feeds the MFMAs of all MT m-tiles.
+// ---------------------------------------------------------------------------
+template <int MT, int NB, int PU, int WR, typename OutT>
+__global__ __launch_bounds__(64 * NB) void k_w4a8_wide(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, const int32_t* __restrict__ wq,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
+    OutT* __restrict__ y) {
+  static_assert(WR % 2 == 0, "the token batches alternate within one ring turn");
+  constexpr bool kI32 = __is_same(OutT, int32_t);
+  constexpr int MR = 16 * MT, PB = 2 * kUnitBytes * PU, kThreads = 64 * NB;   // PB: token bytes per row
+  constexpr int kPitch = PB + 16;                                              // odd number of 16-byte chunks
+  constexpr int kRowChunks = PB / 16, kChunks = MR * kRowChunks;
+  constexpr int CPT = (kChunks + kThreads - 1) / kThreads;
+  constexpr int GP = 2 * PU;                                                   // groups per phase
+  extern __shared__ __attribute__((aligned(16))) u32 szl[];   // 16 NB x sz_pitch(G) words
+  __shared__ __attribute__((aligned(16))) int8_t xbuf[2][MR * kPitch];
+  __shared__ __attribute__((aligned(16))) int tsum[2][GP][MR];
+  __shared__ __attribute__((aligned(16))) int8_t tiles[NB][kTileBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  const int G = K >> 7, Kw = K >> 3, RB = Kw * 4;
+  const int wg_row0 = blockIdx.x * NB * 16, n_base = wg_row0 + wave * 16;
+  const int units = (RB + kUnitBytes - 1) / kUnitBytes;
+  const int phases = (units + PU - 1) / PU;
+
+  const int rows_n = max(0, min(16, N - n_base));
+  const rsrc_t wr = make_rsrc_uniform(wq + (int64_t)min(n_base, N - 1) * Kw, (u32)(rows_n * RB));
+  const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
+  const UnitLanes ul = unit_lanes(lane, RB);
+
+  using WSlot = v4i[PU][2];
+  struct XBatch {
+    v4i x[CPT];
+  };
+  auto load_w = [&](WSlot& d, int p) {
+#pragma unroll
+    for (int v = 0; v < PU; ++v) unit_load(d[v], wr, ul, p * PU + v, p < phases, RB);
+  };
+  auto load_x = [&](XBatch& bt, int p) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int chunk = tid + c * kThreads;
+      const int row = chunk / kRowChunks, kb = p * PB + (chunk % kRowChunks) * 16;
+      // rows past M and bytes past K read zeros (past the resource)
+      bt.x[c] = bld16(xr, chunk < kChunks && kb < K ? (u32)(row * K + kb) : kOOB);
+    }
+  };
+
+  // scales and zero points of the workgroup's 16 NB rows, with the first
+  // weight phases and token batch issued behind their loads
+  const int wg_rows = max(0, min(16 * NB, N - wg_row0));
+  const rsrc_t sr = make_rsrc_uniform(wscale + (int64_t)min(wg_row0, N - 1) * G, (u32)(wg_rows * G * 2));
+  const rsrc_t zr = make_rsrc_uniform(wzero + (int64_t)min(wg_row0, N - 1) * G, (u32)(wg_rows * G * 2));
+  ScaleZeroStage<kThreads, 4> sz;
+  sz.load(sr, zr, 16 * NB * G, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  WSlot wring[WR];
+  XBatch xb[2];
+#pragma unroll
+  for (int s = 0; s < WR - 1; ++s) load_w(wring[s], s);
+  load_x(xb[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
+  sz.finish(sr, zr, szl, G, 16 * NB * G);
+
+  const u32* szrow = szl + (wave * 16 + r) * sz_pitch(G);
+  int8_t* tile = tiles[wave];
+  v4f yacc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) yacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int n = n_base + r;
+  auto process = [&](const XBatch& bt, const WSlot& w, int p) {
+    int8_t* buf = xbuf[p & 1];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int chunk = tid + c * kThreads;   // chunk % 8 == tid % 8 (kThreads % 8 == 0)
+      const bool in = chunk < kChunks;
+      // the 8 chunks of a group are held by 8 consecutive lanes
+      int t = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t = __builtin_amdgcn_sdot4(bt.x[c][e], 0x01010101, t, false);
+      t = sum_lanes8(t);
+      if (in) {
+        const int row = chunk / kRowChunks, col = chunk % kRowChunks;
+        st16(buf + row * kPitch + col * 16, shuffle_act16(bt.x[c]));
+        if ((col & 7) == 0) tsum[p & 1][col >> 3][row] = t;
+      }
+    }
+    // Panel p (and, at p = 0, the scales) complete once every wave is here;
+    // the buffers phase p + 1 overwrites were last read at phase p - 1.
+    lds_barrier();
+#pragma unroll
+    for (int v = 0; v < PU; ++v) {
+      v4i f[2];
+      unit_transpose(tile, w[v], ul, f);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int gl = 2 * v + s2, g = p * GP + gl;
+        const bool gin = g < G;
+        const u32 szw = gin ? szrow[g] : 0u;       // past G: zero codes, tokens and scale
+        const int z = (int)f16_bits_to_f32((uint16_t)(szw >> 16));
+        const v4i bw0 = unpack_u4_pair((u32)f[s2][0], (u32)f[s2][1]);
+        const v4i bw1 = unpack_u4_pair((u32)f[s2][2], (u32)f[s2][3]);
+        const float sc = f16_bits_to_f32((uint16_t)(szw & 0xFFFFu));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int8_t* xf = buf + (16 * mt + r) * kPitch + 128 * gl + 32 * j;
+          const v4i ts = *reinterpret_cast<const v4i*>(&tsum[p & 1][gl][16 * mt + 4 * j]);
+          v4i acc;   // |z| <= 15, |token sum| <= 128 * 127: exact 24-bit products
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = __mul24(-z, ts[e]);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ld16(xf), bw0, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ld16(xf + 16), bw1, acc, 0, 0, 0);
+          if constexpr (kI32) {
+            if (gin && n < N) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int m = 16 * mt + 4 * j + e;
+                if (m < M) y[((int64_t)m * G + g) * N + n] = acc[e];
+              }
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yacc[mt][e] = __builtin_fmaf(sc, (float)acc[e], yacc[mt][e]);
+          }
+        }
+      }
+    }
+  };
+  // every wave runs the same number of phases, so all reach every barrier;
+  // the ring turn is unrolled so every slot index is static
+  for (int p0 = 0; p0 < phases; p0 += WR) {
+#pragma unroll
+    for (int s = 0; s < WR; ++s) {
+      const int p = p0 + s;
+      if (p >= phases) break;
+      load_w(wring[(s + WR - 1) % WR], p + WR - 1);
+      if (p + 1 < phases) load_x(xb[(s + 1) & 1], p + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      process(xb[s & 1], wring[s], p);
+    }
+  }
+
+  if constexpr (!kI32) {
+    if (n < N) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 16 * mt + 4 * j + e;
+          if (m < M) store_out<OutT>(y, (int64_t)m * N + n, yacc[mt][e] * xs[m]);
+        }
+    }
+  }
+}
+
+template <int MT, typename OutT>
+static void launch_w4a8_wide(const int8_t* xq, const float* xs, const int32_t* wq,
+                             const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
+                             size_t lds, hipStream_t st) {
+  constexpr int PU = MT <= 2 ? 2 : 1, WR = MT <= 2 ? 4 : 8;
+  const int nb = wide_waves(N), nblocks = (N + 15) / 16;
+  const dim3 grid((unsigned)((nblocks + nb - 1) / nb));
+  switch (nb) {
+    case 2: k_w4a8_wide<MT, 2, PU, WR, OutT><<<grid, dim3(128), lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
+    case 3: k_w4a8_wide<MT, 3, PU, WR, OutT><<<grid, dim3(192), lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
+    default: k_w4a8_wide<MT, 4, PU, WR, OutT><<<grid, dim3(256), lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
+  }
+}
+
 template <typename OutT>
 static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* wq,
                               const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
@@ -710,6 +891,14 @@ static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* 
       case 8: k_w4a8_dec<8, WAVES, UB, false, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, nullptr, nullptr, M, N, K, y); break;
       default: k_w4a8_dec<16, WAVES, UB, false, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, nullptr, nullptr, M, N, K, y); break;
     }
+    return hipGetLastError();
+  }
+  const size_t lds_wide = (size_t)16 * wide_waves(N) * sz_pitch(K / 128) * 4;
+  if (M > 16 && M <= 64 && wide_waves(N) >= 2 && lds_wide <= kDecLdsMaxBytes) {
+    // 17..64 token rows on wide layers: the token rows staged once per
+    // workgroup of 2-4 weight blocks
+    if (M <= 32) launch_w4a8_wide<2, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st);
+    else launch_w4a8_wide<4, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st);
     return hipGetLastError();
   }
   if (M <= 64 && lds <= kDecLdsMaxBytes) {

@@ -66,15 +66,15 @@ __global__ __launch_bounds__(64 * kSp24Waves) void k_w4a8_sp24(
   const int rows_n = min(16, N - n_base), rows_m = min(16, M - m_base);
   // tile blockIdx.x: group g's 16 rows are 768 contiguous bytes; row r's
   // block j at 48 r + 12 j (rows past N are stored as zeros)
-  const rsrc_t wr = make_rsrc(wsp + (int64_t)blockIdx.x * G * 192, (u32)(G * 768));
+  const rsrc_t wr = make_rsrc_uniform(wsp + (int64_t)blockIdx.x * G * 192, (u32)(G * 768));
   const u32 woff = (u32)(48 * r + 12 * j);
   // token row r: inputs 16 j and 64 + 16 j of the group
-  const rsrc_t xr = make_rsrc(xq + (int64_t)m_base * K, (u32)(rows_m * K));
+  const rsrc_t xr = make_rsrc_uniform(xq + (int64_t)m_base * K, (u32)(rows_m * K));
   const u32 xoff = (u32)(r * K + 16 * j);
 
   ScaleZeroStage<kThreads, 2> sz;
-  const rsrc_t sr = make_rsrc(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
-  const rsrc_t zr = make_rsrc(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  const rsrc_t sr = make_rsrc_uniform(wscale + (int64_t)n_base * G, (u32)(rows_n * G * 2));
+  const rsrc_t zr = make_rsrc_uniform(wzero + (int64_t)n_base * G, (u32)(rows_n * G * 2));
   sz.load(sr, zr, 16 * G, 0);
   sz.finish(sr, zr, szl, G, 16 * G);
   lds_barrier();

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
   const int pitch = stage_pitch(kUnitBytes * ((units + phases - 1) / phases));
 
   const int rows_n = min(16, N - n_base);
-  const rsrc_t wr = make_rsrc(wq + (int64_t)n_base * K, (u32)(rows_n * K));
+  const rsrc_t wr = make_rsrc_uniform(wq + (int64_t)n_base * K, (u32)(rows_n * K));
   const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
   const UnitLanes ul = unit_lanes(lane, K);
 
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(64 * NB) void k_w8a8_wide(
 
   // rows past N (including a whole wave's block past N) read zeros
   const int rows_n = max(0, min(16, N - n_base));
-  const rsrc_t wr = make_rsrc(wq + (int64_t)min(n_base, N - 1) * K, (u32)(rows_n * K));
+  const rsrc_t wr = make_rsrc_uniform(wq + (int64_t)min(n_base, N - 1) * K, (u32)(rows_n * K));
   const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
   const UnitLanes ul = unit_lanes(lane, K);
 

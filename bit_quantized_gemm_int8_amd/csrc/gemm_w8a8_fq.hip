@@ -106,7 +106,7 @@ __global__ __launch_bounds__(64 * kFqWaves) void k_w8a8_fq(
   // 2. this wave's first kFqDepth weight units, in flight during the
   //    quantization below
   const int rows_n = max(0, min(16, N - n_base));
-  const rsrc_t wr = make_rsrc(wq + (int64_t)min(n_base, N) * K, (u32)(rows_n * K));
+  const rsrc_t wr = make_rsrc_uniform(wq + (int64_t)min(n_base, N) * K, (u32)(rows_n * K));
   const UnitLanes ul = unit_lanes(lane, K);
   v4i b[kFqDepth][2];
 #pragma unroll

@@ -27,6 +27,16 @@ __device__ __forceinline__ v4i ld16_stream(const void* p) {
 
 __device__ __forceinline__ void st16(void* p, v4i v) { *reinterpret_cast<v4i*>(p) = v; }
 
+// Sum over each aligned group of 8 lanes, every lane of the group receiving
+// it: DPP swaps of neighbours and of pairs (quad permutations), then the
+// mirror within each half row pairs the two quads.
+__device__ __forceinline__ int sum_lanes8(int t) {
+  t += __builtin_amdgcn_mov_dpp(t, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+  t += __builtin_amdgcn_mov_dpp(t, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+  t += __builtin_amdgcn_mov_dpp(t, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  return t;
+}
+
 // ---- raw buffer loads --------------------------------------------------------
 // A buffer resource covers [base, base + bytes); a load whose offset lies past
 // the end returns zeros instead of touching memory, so edge tiles and masked
@@ -37,6 +47,15 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+// The same from values every lane holds alike, pinned to scalar registers: a
+// resource the compiler keeps in vector registers costs a waterfall loop
+// around every load that uses it.
+__device__ __forceinline__ rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return make_rsrc((const void*)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
 }
 __device__ __forceinline__ v4i bld16(rsrc_t r, u32 off) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));

@@ -93,8 +93,8 @@ __global__ __launch_bounds__(256) void k_quant_rows_wave(const void* __restrict_
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;   // wave-uniform
-  const rsrc_t xr = make_rsrc(reinterpret_cast<const char*>(x) + row * K * E, (u32)(K * E));
-  const rsrc_t qr = make_rsrc(xq + row * K, (u32)K);
+  const rsrc_t xr = make_rsrc_uniform(reinterpret_cast<const char*>(x) + row * K * E, (u32)(K * E));
+  const rsrc_t qr = make_rsrc_uniform(xq + row * K, (u32)K);
   v4i raw[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) raw[c] = bld16(xr, (u32)(1024 * c + 16 * lane));

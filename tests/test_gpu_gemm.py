@@ -131,7 +131,12 @@ W4_SHAPES = [(16, 4096, 11008), (1, 16, 128), (5, 17, 256), (16, 300, 1024), (17
              (32, 4096, 11008), (64, 40, 256), (48, 300, 640), (20, 16, 128), (57, 33, 1152),
              # two weight blocks per wave on wide layers (N / 32 >= 256): full,
              # ragged last pair of blocks with an odd group count, 16 rows
-             (1, 8192, 1024), (3, 8200, 384), (16, 11008, 4096)]
+             (1, 8192, 1024), (3, 8200, 384), (16, 11008, 4096),
+             # 17-64 rows on wide layers (2-4 weight blocks per workgroup, the
+             # token rows staged once): 2 and 4 m-tiles, ragged rows and last
+             # workgroup, odd group counts, a group count past one phase ring
+             (32, 11008, 4096), (48, 11008, 4096), (17, 6160, 1152), (33, 12288, 4224),
+             (64, 16400, 256), (40, 7000, 640)]
 
 
 @pytest.mark.parametrize("M,N,K", W4_SHAPES)
@@ -155,7 +160,8 @@ def _w4a8_floor(xq, sx, packed, sc, zz):
 
 @pytest.mark.parametrize("fmt", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("M,N,K", [(16, 4096, 11008), (5, 17, 256), (33, 40, 640), (2, 48, 14336),
-                                   (64, 300, 1024), (4, 8200, 1024), (16, 11008, 4096)])
+                                   (64, 300, 1024), (4, 8200, 1024), (16, 11008, 4096),
+                                   (32, 11008, 4096), (57, 7000, 1152)])
 def test_w4a8_scaled(fmt, M, N, K):
     rng = np.random.default_rng(M + 3 * N + K)
     packed, sc, zz = _u4_weights(rng, K, N)
