@@ -687,38 +687,56 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec2(
 
 // ---------------------------------------------------------------------------
 // Wide kernel (17-64 token rows on layers of at least 384 weight blocks): as
-// k_w8a8_wide / k_w4a16_wide, a workgroup of NB waves owns NB 16-row weight
-// blocks, one per wave over the whole K, and the waves move through K in
-// phases of PU units (2 PU groups).  A phase's token rows (16 MT rows x
-// 256 PU bytes) are staged once in LDS for all NB waves, each 16-byte chunk
-// already permuted to the unpack order, and the per-(group, row) token sums
-// that carry the zero point are formed while staging (byte sums reduced over
-// the 8 lanes that hold a group's chunks); two-deep ring, one barrier per
-// phase.  The weight stream runs WR phases ahead in a register ring: with one
-// wave per SIMD nothing else hides its latency.  Each unpacked weight fragment
-// feeds the MFMAs of all MT m-tiles.
+// k_w8a8_wide / k_w4a16_wide, a workgroup owns NB 16-row weight blocks and
+// moves through K in phases of PU units (2 PU groups).  Each block has KS
+// waves that split a phase's units between them, so a SIMD holds more than
+// one wave to hide the per-group LDS and MFMA latencies; their partial sums
+// meet in LDS at the end.  A phase's token rows (16 MT rows x 256 PU bytes)
+// are staged once in LDS for all waves, each 16-byte chunk already permuted
+// to the unpack order, and the per-(group, row) token sums that carry the
+// zero point are formed while staging (byte sums reduced over the 8 lanes
+// that hold a group's chunks); two-deep LDS ring, one barrier per phase.  The
+// weight stream runs WR phases ahead and the token rows XR phases ahead, in
+// register rings.  Each unpacked weight fragment feeds the MFMAs of all MT
+// m-tiles.
 // ---------------------------------------------------------------------------
-template <int MT, int NB, int PU, int WR, typename OutT>
-__global__ __launch_bounds__(64 * NB) void k_w4a8_wide(
+// Static LDS of k_w4a8_wide (token ring, token sums, weight tiles, partial
+// sums), checked against the kernel's arrays.
+template <int MT, int NB, int KS, int MS, int PU, bool I32>
+__host__ __device__ constexpr size_t w4a8_wide_static_lds() {
+  return (size_t)2 * 16 * MT * (2 * kUnitBytes * PU + 16) + (size_t)2 * 2 * PU * 16 * MT * 4 +
+         (size_t)NB * KS * MS * kTileBytes + (size_t)((I32 || KS == 1) ? 1 : NB * MS * (KS - 1)) * (MT / MS) * 64 * 16;
+}
+
+template <int MT, int NB, int KS, int MS, int PU, int WR, int XR, typename OutT>
+__global__ __launch_bounds__(64 * NB * KS * MS) void k_w4a8_wide(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, const int32_t* __restrict__ wq,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
     OutT* __restrict__ y) {
-  static_assert(WR % 2 == 0, "the token batches alternate within one ring turn");
+  static_assert(PU % KS == 0, "every wave of a block takes the same number of units");
+  static_assert(MT % MS == 0, "every wave of a block takes the same number of m-tiles");
+  constexpr int L = WR % XR == 0 ? WR : WR * XR;   // ring turn: every slot index static
   constexpr bool kI32 = __is_same(OutT, int32_t);
-  constexpr int MR = 16 * MT, PB = 2 * kUnitBytes * PU, kThreads = 64 * NB;   // PB: token bytes per row
-  constexpr int kPitch = PB + 16;                                              // odd number of 16-byte chunks
+  constexpr int UPW = PU / KS;                     // units per wave and phase
+  constexpr int MTW = MT / MS;                     // m-tiles per wave
+  constexpr int MR = 16 * MT, PB = 2 * kUnitBytes * PU, kThreads = 64 * NB * KS * MS;   // PB: token bytes per row
+  constexpr int kPitch = PB + 16;                                                   // odd number of 16-byte chunks
   constexpr int kRowChunks = PB / 16, kChunks = MR * kRowChunks;
   constexpr int CPT = (kChunks + kThreads - 1) / kThreads;
-  constexpr int GP = 2 * PU;                                                   // groups per phase
+  constexpr int GP = 2 * PU;                                                        // groups per phase
   extern __shared__ __attribute__((aligned(16))) u32 szl[];   // 16 NB x sz_pitch(G) words
   __shared__ __attribute__((aligned(16))) int8_t xbuf[2][MR * kPitch];
   __shared__ __attribute__((aligned(16))) int tsum[2][GP][MR];
-  __shared__ __attribute__((aligned(16))) int8_t tiles[NB][kTileBytes];
+  __shared__ __attribute__((aligned(16))) int8_t tiles[NB * KS * MS][kTileBytes];
+  __shared__ v4f red[(kI32 || KS == 1) ? 1 : NB * MS * (KS - 1)][MTW][64];
+  static_assert(sizeof(xbuf) + sizeof(tsum) + sizeof(tiles) + sizeof(red) ==
+                w4a8_wide_static_lds<MT, NB, KS, MS, PU, kI32>(), "static LDS bookkeeping");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int blk = wave % NB, ks = (wave / NB) % KS, ms = wave / (NB * KS);
   const int r = lane & 15, j = lane >> 4;
   const int G = K >> 7, Kw = K >> 3, RB = Kw * 4;
-  const int wg_row0 = blockIdx.x * NB * 16, n_base = wg_row0 + wave * 16;
+  const int wg_row0 = blockIdx.x * NB * 16, n_base = wg_row0 + blk * 16;
   const int units = (RB + kUnitBytes - 1) / kUnitBytes;
   const int phases = (units + PU - 1) / PU;
 
@@ -727,13 +745,13 @@ __global__ __launch_bounds__(64 * NB) void k_w4a8_wide(
   const rsrc_t xr = make_rsrc(xq, (u32)(M * K));
   const UnitLanes ul = unit_lanes(lane, RB);
 
-  using WSlot = v4i[PU][2];
+  using WSlot = v4i[UPW][2];
   struct XBatch {
     v4i x[CPT];
   };
   auto load_w = [&](WSlot& d, int p) {
 #pragma unroll
-    for (int v = 0; v < PU; ++v) unit_load(d[v], wr, ul, p * PU + v, p < phases, RB);
+    for (int v = 0; v < UPW; ++v) unit_load(d[v], wr, ul, p * PU + ks * UPW + v, p < phases, RB);
   };
   auto load_x = [&](XBatch& bt, int p) {
 #pragma unroll
@@ -746,7 +764,7 @@ __global__ __launch_bounds__(64 * NB) void k_w4a8_wide(
   };
 
   // scales and zero points of the workgroup's 16 NB rows, with the first
-  // weight phases and token batch issued behind their loads
+  // weight phases and token batches issued behind their loads
   const int wg_rows = max(0, min(16 * NB, N - wg_row0));
   const rsrc_t sr = make_rsrc_uniform(wscale + (int64_t)min(wg_row0, N - 1) * G, (u32)(wg_rows * G * 2));
   const rsrc_t zr = make_rsrc_uniform(wzero + (int64_t)min(wg_row0, N - 1) * G, (u32)(wg_rows * G * 2));
@@ -754,18 +772,20 @@ __global__ __launch_bounds__(64 * NB) void k_w4a8_wide(
   sz.load(sr, zr, 16 * NB * G, 0);
   __builtin_amdgcn_sched_barrier(0);
   WSlot wring[WR];
-  XBatch xb[2];
+  XBatch xring[XR];
 #pragma unroll
-  for (int s = 0; s < WR - 1; ++s) load_w(wring[s], s);
-  load_x(xb[0], 0);
+  for (int q = 0; q < (WR > XR ? WR : XR) - 1; ++q) {
+    if (q < WR - 1) load_w(wring[q], q);
+    if (q < XR - 1) load_x(xring[q], q);
+  }
   __builtin_amdgcn_sched_barrier(0);
   sz.finish(sr, zr, szl, G, 16 * NB * G);
 
-  const u32* szrow = szl + (wave * 16 + r) * sz_pitch(G);
+  const u32* szrow = szl + (blk * 16 + r) * sz_pitch(G);
   int8_t* tile = tiles[wave];
-  v4f yacc[MT];
+  v4f yacc[MTW];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) yacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MTW; ++mt) yacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
   const int n = n_base + r;
   auto process = [&](const XBatch& bt, const WSlot& w, int p) {
     int8_t* buf = xbuf[p & 1];
@@ -788,12 +808,12 @@ __global__ __launch_bounds__(64 * NB) void k_w4a8_wide(
     // the buffers phase p + 1 overwrites were last read at phase p - 1.
     lds_barrier();
 #pragma unroll
-    for (int v = 0; v < PU; ++v) {
+    for (int v = 0; v < UPW; ++v) {
       v4i f[2];
       unit_transpose(tile, w[v], ul, f);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const int gl = 2 * v + s2, g = p * GP + gl;
+        const int gl = 2 * (ks * UPW + v) + s2, g = p * GP + gl;
         const bool gin = g < G;
         const u32 szw = gin ? szrow[g] : 0u;       // past G: zero codes, tokens and scale
         const int z = (int)f16_bits_to_f32((uint16_t)(szw >> 16));
@@ -801,7 +821,8 @@ __global__ __launch_bounds__(64 * NB) void k_w4a8_wide(
         const v4i bw1 = unpack_u4_pair((u32)f[s2][2], (u32)f[s2][3]);
         const float sc = f16_bits_to_f32((uint16_t)(szw & 0xFFFFu));
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+        for (int mw = 0; mw < MTW; ++mw) {
+          const int mt = ms * MTW + mw;
           const int8_t* xf = buf + (16 * mt + r) * kPitch + 128 * gl + 32 * j;
           const v4i ts = *reinterpret_cast<const v4i*>(&tsum[p & 1][gl][16 * mt + 4 * j]);
           v4i acc;   // |z| <= 15, |token sum| <= 128 * 127: exact 24-bit products
@@ -819,50 +840,80 @@ __global__ __launch_bounds__(64 * NB) void k_w4a8_wide(
             }
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) yacc[mt][e] = __builtin_fmaf(sc, (float)acc[e], yacc[mt][e]);
+            for (int e = 0; e < 4; ++e) yacc[mw][e] = __builtin_fmaf(sc, (float)acc[e], yacc[mw][e]);
           }
         }
       }
     }
   };
   // every wave runs the same number of phases, so all reach every barrier;
-  // the ring turn is unrolled so every slot index is static
-  for (int p0 = 0; p0 < phases; p0 += WR) {
+  // loads for phases past the end read zeros without touching memory
+  for (int p0 = 0; p0 < phases; p0 += L) {
 #pragma unroll
-    for (int s = 0; s < WR; ++s) {
+    for (int s = 0; s < L; ++s) {
       const int p = p0 + s;
       if (p >= phases) break;
       load_w(wring[(s + WR - 1) % WR], p + WR - 1);
-      if (p + 1 < phases) load_x(xb[(s + 1) & 1], p + 1);
+      load_x(xring[(s + XR - 1) % XR], p + XR - 1);
       __builtin_amdgcn_sched_barrier(0);
-      process(xb[s & 1], wring[s], p);
+      process(xring[s % XR], wring[s % WR], p);
     }
   }
 
   if constexpr (!kI32) {
+    if constexpr (KS > 1) {
+      // the block's other waves hand their partial sums to wave ks = 0
+      if (ks > 0) {
+#pragma unroll
+        for (int mw = 0; mw < MTW; ++mw) red[((ks - 1) * MS + ms) * NB + blk][mw][lane] = yacc[mw];
+      }
+      lds_barrier();
+      if (ks > 0) return;
+#pragma unroll
+      for (int o = 0; o < KS - 1; ++o)
+#pragma unroll
+        for (int mw = 0; mw < MTW; ++mw) {
+          const v4f t = red[(o * MS + ms) * NB + blk][mw][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yacc[mw][e] += t[e];
+        }
+    }
     if (n < N) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mw = 0; mw < MTW; ++mw)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = 16 * mt + 4 * j + e;
-          if (m < M) store_out<OutT>(y, (int64_t)m * N + n, yacc[mt][e] * xs[m]);
+          const int m = 16 * (ms * MTW + mw) + 4 * j + e;
+          if (m < M) store_out<OutT>(y, (int64_t)m * N + n, yacc[mw][e] * xs[m]);
         }
     }
   }
 }
 
+template <int MT, int NB, int KS, int MS, typename OutT>
+static bool launch_w4a8_wide_nb(const int8_t* xq, const float* xs, const int32_t* wq,
+                                const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
+                                size_t lds, hipStream_t st) {
+  constexpr int PU = KS, WR = 2, XR = 2;   // measured on MI355X (K = 4096, N = 11008 / 14336)
+  if (w4a8_wide_static_lds<MT, NB, KS, MS, PU, __is_same(OutT, int32_t)>() + lds > kLdsBytesPerCU) return false;
+  const int nblocks = (N + 15) / 16;
+  const dim3 grid((unsigned)((nblocks + NB - 1) / NB)), block(64 * NB * KS * MS);
+  k_w4a8_wide<MT, NB, KS, MS, PU, WR, XR, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y);
+  return true;
+}
+
+// 2-4 weight blocks per workgroup (wide_waves); per block 4 waves (K split in
+// 4, or in 2 with the m-tiles split in 2) where the workgroup stays at 12
+// waves or fewer, else 2 (measured on MI355X: 16-wave workgroups were slower)
 template <int MT, typename OutT>
-static void launch_w4a8_wide(const int8_t* xq, const float* xs, const int32_t* wq,
+static bool launch_w4a8_wide(const int8_t* xq, const float* xs, const int32_t* wq,
                              const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
                              size_t lds, hipStream_t st) {
-  constexpr int PU = MT <= 2 ? 2 : 1, WR = MT <= 2 ? 4 : 8;
-  const int nb = wide_waves(N), nblocks = (N + 15) / 16;
-  const dim3 grid((unsigned)((nblocks + nb - 1) / nb));
-  switch (nb) {
-    case 2: k_w4a8_wide<MT, 2, PU, WR, OutT><<<grid, dim3(128), lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
-    case 3: k_w4a8_wide<MT, 3, PU, WR, OutT><<<grid, dim3(192), lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
-    default: k_w4a8_wide<MT, 4, PU, WR, OutT><<<grid, dim3(256), lds, st>>>(xq, xs, wq, ws, wz, M, N, K, y); break;
+  constexpr int KS = MT <= 2 ? 4 : 2, MS = MT <= 2 ? 1 : 2;
+  switch (wide_waves(N)) {
+    case 2: return launch_w4a8_wide_nb<MT, 2, KS, MS, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds, st);
+    case 3: return launch_w4a8_wide_nb<MT, 3, KS, MS, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds, st);
+    default: return launch_w4a8_wide_nb<MT, 4, 2, 1, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds, st);
   }
 }
 
@@ -894,12 +945,12 @@ static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* 
     return hipGetLastError();
   }
   const size_t lds_wide = (size_t)16 * wide_waves(N) * sz_pitch(K / 128) * 4;
-  if (M > 16 && M <= 64 && wide_waves(N) >= 2 && lds_wide <= kDecLdsMaxBytes) {
+  if (M > 16 && M <= 64 && wide_waves(N) >= 2) {
     // 17..64 token rows on wide layers: the token rows staged once per
-    // workgroup of 2-4 weight blocks
-    if (M <= 32) launch_w4a8_wide<2, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st);
-    else launch_w4a8_wide<4, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st);
-    return hipGetLastError();
+    // workgroup of 2-4 weight blocks (unless K is too long for LDS)
+    const bool done = M <= 32 ? launch_w4a8_wide<2, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st)
+                              : launch_w4a8_wide<4, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st);
+    if (done) return hipGetLastError();
   }
   if (M <= 64 && lds <= kDecLdsMaxBytes) {
     // 17..64 token rows: one weight stream for 2 or 4 tiles of 16 rows

@@ -31,6 +31,7 @@ constexpr int kTileBytes = 16 * kUnitBytes;
 // Largest dynamic LDS a decode launch stages (token rows, scales): 80 KB, so
 // that two workgroups still share the 160 KB of a CU.
 constexpr size_t kDecLdsMaxBytes = 80 * 1024;
+constexpr size_t kLdsBytesPerCU = 160 * 1024;   // LDS of one CDNA4 compute unit
 
 __device__ __forceinline__ int unit_slot(int row, int chunk) {
   return row * kUnitBytes + ((chunk ^ ((row >> 1) & 7)) << 4);

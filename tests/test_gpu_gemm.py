@@ -136,7 +136,7 @@ W4_SHAPES = [(16, 4096, 11008), (1, 16, 128), (5, 17, 256), (16, 300, 1024), (17
              # token rows staged once): 2 and 4 m-tiles, ragged rows and last
              # workgroup, odd group counts, a group count past one phase ring
              (32, 11008, 4096), (48, 11008, 4096), (17, 6160, 1152), (33, 12288, 4224),
-             (64, 16400, 256), (40, 7000, 640)]
+             (64, 16400, 256), (40, 7000, 640), (20, 14400, 1024), (24, 12288, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", W4_SHAPES)
@@ -148,6 +148,34 @@ def test_w4a8_group_acc_bitwise(M, N, K):
     acc = qg.gemm_w4a8_g128(to_dev(xq), None, wqd, None, zzd, out_dtype=torch.int32)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_np(acc), oracle.gemm_w4a8_g128_acc(xq, packed, zz))
+
+
+@pytest.mark.parametrize("M", [24, 40])
+def test_w4a8_long_k_sampled(M):
+    """17-64 rows on a wide layer whose K is too long for the wide kernel's
+    LDS (K = 36864: 288 groups of scales per weight row); the launch takes
+    the multi-tile kernel instead.  Seeded random codes, zero points and
+    scales; per-group sums exact and scaled outputs checked on sampled
+    columns (the first, the last and 46 drawn)."""
+    N, K = 12288, 36864
+    G = K // 128
+    rng = np.random.default_rng(M * 7 + 1)
+    packed = rng.integers(0, 2 ** 32, (N, K // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    zz = rng.integers(0, 16, (N, G)).astype(np.float16)
+    sc = (rng.random((N, G)) * 1e-3 + 1e-4).astype(np.float16)
+    xq = _codes(rng, (M, K))
+    sx = (rng.random(M) * 0.05 + 1e-3).astype(np.float32)
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 46, replace=False)]))
+    wqd, scd, zzd = _w4_devs(packed, sc, zz)
+    xqd = to_dev(xq)
+    acc = qg.gemm_w4a8_g128(xqd, None, wqd, None, zzd, out_dtype=torch.int32)
+    y = qg.gemm_w4a8_g128(xqd, to_dev(sx), wqd, scd, zzd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(cols).to(acc.device)
+    p, s, z = packed[cols], sc[cols], zz[cols]
+    np.testing.assert_array_equal(to_np(acc.index_select(2, idx)), oracle.gemm_w4a8_g128_acc(xq, p, z))
+    assert_close(out_f64(y.index_select(1, idx)), oracle.gemm_w4a8_g128(xq, sx, p, s, z), "f32",
+                 floor=_w4a8_floor(xq, sx, p, s, z), what="w4a8 long K")
 
 
 def _w4a8_floor(xq, sx, packed, sc, zz):
