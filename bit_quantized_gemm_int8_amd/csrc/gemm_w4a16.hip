@@ -404,33 +404,48 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
 }
 
 // ---------------------------------------------------------------------------
-// Wide decode kernel (up to 64 token rows, MT m-tiles of 16): a workgroup of
-// NB waves owns NB x 16 weight rows, one 16-row block per wave over the whole
-// K, the waves moving through K in phases of PU units (2 PU groups).  A
-// phase's panel of token rows (16 MT rows x 256 PU halves, chunks already in
-// the unpack order) is staged in LDS once for all NB waves (two-deep ring,
-// one barrier per phase), and each unpacked weight fragment feeds the MFMAs
-// of all MT m-tiles.  Scales and zero points of the workgroup's rows are
-// staged in LDS at the start.
+// Wide decode kernel (up to 64 token rows, MT m-tiles of 16): a workgroup owns
+// NB 16-row weight blocks and moves through K in phases of PU units (2 PU
+// groups).  Each block has KS x MS waves: KS split a phase's units, MS split
+// the m-tiles (reading the same weights), so that a SIMD holds more than one
+// wave to hide the LDS and MFMA latencies; the KS partial sums meet in LDS at
+// the end.  A phase's panel of token rows (16 MT rows x 256 PU halves, chunks
+// already in the unpack order) is staged in LDS once for all waves (two-deep
+// ring, one barrier per phase), and each unpacked weight fragment feeds the
+// MFMAs of the wave's m-tiles.  Scales and zero points of the workgroup's
+// rows are staged in LDS at the start.
 // ---------------------------------------------------------------------------
-template <int MT, int NB, int PU, int XDT, typename OutT>
-__global__ __launch_bounds__(64 * NB) void k_w4a16_wide(
+template <int MT, int NB, int KS, int MS, int PU>
+__host__ __device__ constexpr size_t w4a16_wide_static_lds() {
+  return (size_t)2 * 16 * MT * (512 * PU + 16) + (size_t)NB * KS * MS * kTileBytes +
+         (size_t)(KS == 1 ? 1 : NB * MS * (KS - 1)) * (MT / MS) * 64 * 16;
+}
+
+template <int MT, int NB, int KS, int MS, int PU, int XDT, typename OutT>
+__global__ __launch_bounds__(64 * NB * KS * MS) void k_w4a16_wide(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ wq,
     const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
     OutT* __restrict__ y) {
-  constexpr int MR = 16 * MT, PB = 512 * PU, kThreads = 64 * NB;   // PB: panel bytes per row
+  static_assert(PU % KS == 0, "every wave of a block takes the same number of units");
+  static_assert(MT % MS == 0, "every wave of a block takes the same number of m-tiles");
+  constexpr int UPW = PU / KS, MTW = MT / MS;                       // units, m-tiles per wave
+  constexpr int MR = 16 * MT, PB = 512 * PU, kThreads = 64 * NB * KS * MS;   // PB: panel bytes per row
   constexpr int kPitch = PB + 16;                                   // odd number of 16-byte chunks
   constexpr int kRowChunks = PB / 16, kChunks = MR * kRowChunks;
   constexpr int CPT = (kChunks + kThreads - 1) / kThreads;
   constexpr bool kFull = CPT * kThreads == kChunks;
   extern __shared__ __attribute__((aligned(16))) u32 szl[];          // 16 NB x sz_pitch(G) words
   __shared__ __attribute__((aligned(16))) int8_t xbuf[2][MR * kPitch];
-  __shared__ __attribute__((aligned(16))) int8_t tiles[NB][kTileBytes];
+  __shared__ __attribute__((aligned(16))) int8_t tiles[NB * KS * MS][kTileBytes];
+  __shared__ v4f red[KS == 1 ? 1 : NB * MS * (KS - 1)][MTW][64];
+  static_assert(sizeof(xbuf) + sizeof(tiles) + sizeof(red) == w4a16_wide_static_lds<MT, NB, KS, MS, PU>(),
+                "static LDS bookkeeping");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int blk = wave % NB, ks = (wave / NB) % KS, ms = wave / (NB * KS);
   const int r = lane & 15, j = lane >> 4;
   const int G = K >> 7, Kw = K >> 3, RB = Kw * 4;
-  const int wg_row0 = blockIdx.x * NB * 16, n_base = wg_row0 + wave * 16;
+  const int wg_row0 = blockIdx.x * NB * 16, n_base = wg_row0 + blk * 16;
   const int units = (RB + kUnitBytes - 1) / kUnitBytes;
   const int phases = (units + PU - 1) / PU;
 
@@ -440,11 +455,11 @@ __global__ __launch_bounds__(64 * NB) void k_w4a16_wide(
   const UnitLanes ul = unit_lanes(lane, RB);
 
   struct Batch {
-    v4i w[PU][2], x[CPT];
+    v4i w[UPW][2], x[CPT];
   };
   auto load = [&](Batch& bt, int p) {
 #pragma unroll
-    for (int v = 0; v < PU; ++v) unit_load(bt.w[v], wr, ul, p * PU + v, true, RB);
+    for (int v = 0; v < UPW; ++v) unit_load(bt.w[v], wr, ul, p * PU + ks * UPW + v, true, RB);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int chunk = tid + c * kThreads;
@@ -466,11 +481,11 @@ __global__ __launch_bounds__(64 * NB) void k_w4a16_wide(
   load(b0, 0);
   sz.finish(sr, zr, szl, G, 16 * NB * G);
 
-  const u32* szrow = szl + (wave * 16 + r) * sz_pitch(G);
+  const u32* szrow = szl + (blk * 16 + r) * sz_pitch(G);
   int8_t* tile = tiles[wave];
-  v4f yacc[MT];
+  v4f yacc[MTW];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) yacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int mw = 0; mw < MTW; ++mw) yacc[mw] = v4f{0.f, 0.f, 0.f, 0.f};
   auto process = [&](const Batch& bt, int p) {
     int8_t* buf = xbuf[p & 1];
 #pragma unroll
@@ -483,12 +498,13 @@ __global__ __launch_bounds__(64 * NB) void k_w4a16_wide(
     // the buffer phase p + 1 overwrites was last read at phase p - 1.
     lds_barrier();
 #pragma unroll
-    for (int v = 0; v < PU; ++v) {
+    for (int v = 0; v < UPW; ++v) {
       v4i f[2];
       unit_transpose(tile, bt.w[v], ul, f);
+      const int u = ks * UPW + v;   // unit within the phase
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const int g = 2 * (p * PU + v) + s2;
+        const int g = 2 * (p * PU + u) + s2;
         const u32 szw = g < G ? szrow[g] : 0u;     // past G: zero codes and scale
         const float zf = f16_bits_to_f32((uint16_t)(szw >> 16));
         v4i bw[4];
@@ -503,10 +519,10 @@ __global__ __launch_bounds__(64 * NB) void k_w4a16_wide(
           for (int h = 0; h < 4; ++h) bw[h] = unpack_bf16((u32)f[s2][h], zb);
         }
         const float sc = f16_bits_to_f32((uint16_t)(szw & 0xFFFFu));
-        const int kin = 512 * v + 256 * s2 + 64 * j;
+        const int kin = 512 * u + 256 * s2 + 64 * j;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int8_t* xf = buf + (16 * mt + r) * kPitch + kin;
+        for (int mw = 0; mw < MTW; ++mw) {
+          const int8_t* xf = buf + (16 * (ms * MTW + mw) + r) * kPitch + kin;
           v4f pacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int h = 0; h < 4; ++h) {
@@ -519,7 +535,7 @@ __global__ __launch_bounds__(64 * NB) void k_w4a16_wide(
                                                              __builtin_bit_cast(v8bf, bw[h]), pacc, 0, 0, 0);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) yacc[mt][i] = __builtin_fmaf(sc, pacc[i], yacc[mt][i]);
+          for (int i = 0; i < 4; ++i) yacc[mw][i] = __builtin_fmaf(sc, pacc[i], yacc[mw][i]);
         }
       }
     }
@@ -531,30 +547,76 @@ __global__ __launch_bounds__(64 * NB) void k_w4a16_wide(
     process(b1, p + 1);
   }
 
+  if constexpr (KS > 1) {
+    // the block's other waves hand their partial sums to wave ks = 0
+    if (ks > 0) {
+#pragma unroll
+      for (int mw = 0; mw < MTW; ++mw) red[((ks - 1) * MS + ms) * NB + blk][mw][lane] = yacc[mw];
+    }
+    lds_barrier();
+    if (ks > 0) return;
+#pragma unroll
+    for (int o = 0; o < KS - 1; ++o)
+#pragma unroll
+      for (int mw = 0; mw < MTW; ++mw) {
+        const v4f t = red[(o * MS + ms) * NB + blk][mw][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yacc[mw][i] += t[i];
+      }
+  }
   const int n = n_base + r;
   if (n < N) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mw = 0; mw < MTW; ++mw)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = 16 * mt + 4 * j + i;
-        if (m < M) y[(int64_t)m * N + n] = Out<OutT>::cvt(yacc[mt][i]);
+        const int m = 16 * (ms * MTW + mw) + 4 * j + i;
+        if (m < M) y[(int64_t)m * N + n] = Out<OutT>::cvt(yacc[mw][i]);
       }
   }
 }
 
+template <int MT, int NB, int KS, int MS, int PU, int XDT, typename OutT>
+static bool launch_w4a16_wide_nb(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
+                                 const uint16_t* wz, int M, int N, int K, OutT* y, size_t lds,
+                                 hipStream_t st) {
+  if (w4a16_wide_static_lds<MT, NB, KS, MS, PU>() + lds > kLdsBytesPerCU) return false;
+  const int nblocks = (N + 15) / 16;
+  const dim3 grid((unsigned)((nblocks + NB - 1) / NB)), block(64 * NB * KS * MS);
+  k_w4a16_wide<MT, NB, KS, MS, PU, XDT, OutT><<<grid, block, lds, st>>>(x, wq, ws, wz, M, N, K, y);
+  return true;
+}
+
+// Waves per weight block (K split KS ways, m-tiles MS ways), measured on
+// MI355X (K = 4096 and 11008; N = 4096, 12288, 14336): 2 (4 with one block per
+// workgroup, narrow layers), or the m-tiles split where the K split would need
+// too much LDS (PU = KS units of token rows per phase).  K = 4096, N = 12288:
+// 17-32 rows 17.2 -> 12.2 us, 64 rows 25.6 -> 22.0; 16 rows on N = 14336
+// 13.0 -> 10.2.
+template <int MT, int NB>
+struct W16Split {
+  static constexpr int KS = MT == 1 ? (NB == 1 ? 4 : 2) : MT <= 3 ? 2 : 1;
+  static constexpr int MS = MT == 2 ? (NB == 1 ? 2 : 1) : MT == 3 ? 1 : MT == 4 ? (NB == 1 ? 4 : 2) : 1;
+  static constexpr int PU = KS > 1 ? KS : (MT == 1 ? 2 : 1);
+};
+
+template <int MT, int NB, int XDT, typename OutT>
+static bool launch_w4a16_wide_split(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
+                                    const uint16_t* wz, int M, int N, int K, OutT* y, size_t lds,
+                                    hipStream_t st) {
+  using S = W16Split<MT, NB>;
+  return launch_w4a16_wide_nb<MT, NB, S::KS, S::MS, S::PU, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds, st);
+}
+
 template <int MT, int XDT, typename OutT>
-static void launch_w4a16_wide(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
+static bool launch_w4a16_wide(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
                               const uint16_t* wz, int M, int N, int K, OutT* y, size_t lds,
                               hipStream_t st) {
-  constexpr int PU = MT == 1 ? 2 : 1;   // measured on MI355X (K = 4096, N = 12288)
-  const int nb = wide_waves(N), nblocks = (N + 15) / 16;
-  const dim3 grid((unsigned)((nblocks + nb - 1) / nb));
-  switch (nb) {
-    case 1: k_w4a16_wide<MT, 1, PU, XDT, OutT><<<grid, dim3(64), lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-    case 2: k_w4a16_wide<MT, 2, PU, XDT, OutT><<<grid, dim3(128), lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-    case 3: k_w4a16_wide<MT, 3, PU, XDT, OutT><<<grid, dim3(192), lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
-    default: k_w4a16_wide<MT, 4, PU, XDT, OutT><<<grid, dim3(256), lds, st>>>(x, wq, ws, wz, M, N, K, y); break;
+  switch (wide_waves(N)) {
+    case 1: return launch_w4a16_wide_split<MT, 1, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds, st);
+    case 2: return launch_w4a16_wide_split<MT, 2, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds, st);
+    case 3: return launch_w4a16_wide_split<MT, 3, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds, st);
+    default: return launch_w4a16_wide_split<MT, 4, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds, st);
   }
 }
 
@@ -604,43 +666,34 @@ static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint1
     }
     return hipGetLastError();
   }
-  const int nblocks16 = (N + 15) / 16;
-  if (M > 8 && M <= 16 && K >= 1536 && (nblocks16 <= 512 || (nblocks16 <= 768 && K >= 4096))) {
-    // 9-16 token rows: the decode kernel with 16 rows, their tokens staged
-    // in phases of K small enough for the scales of up to 64 weight rows to
-    // fit beside them.  Measured on MI355X against the wide kernel: faster
-    // on layers of up to 512 16-row blocks with K >= 1536 (K = 4096, N = 4096:
-    // 9.9 against 14.9 us) and on 768 blocks at K = 4096 (12.7 against 14.1);
-    // slower at K = 1024, and on 688-1024 blocks with shorter K.
+  if (M <= 8) {
+    // token rows too long for LDS at once: the decode kernel walks K in
+    // phases, each staging its slice of the token rows (measured on MI355X,
+    // K = 11008, N = 4096, 4 rows: 11.7 us against 14.1 with the wide kernel)
+    const int nblocks = (N + 15) / 16;
     const int units = (K / 2 + kUnitBytes - 1) / kUnitBytes;
     auto tok_lds = [&](int ph) {
-      return (size_t)16 * stage_pitch(std::min(2 * K, kSliceUnitBytes * ((units + ph - 1) / ph)));
+      return (size_t)mr * stage_pitch(std::min(2 * K, kSliceUnitBytes * ((units + ph - 1) / ph)));
     };
-    const size_t sz64 = (size_t)64 * sz_pitch(G) * 4;
+    const size_t sz16 = (size_t)16 * sz_pitch(G) * 4;
     int phases = 1;
-    while (phases < units && tok_lds(phases) + sz64 > kDecLdsMaxBytes) ++phases;
-    if (tok_lds(phases) + sz64 <= kDecLdsMaxBytes) {
-      const int nblocks = nblocks16;
-      const size_t lds16 = tok_lds(phases) + (size_t)16 * sz_pitch(G) * 4;
-      const size_t wg_lds = lds16 + 4 * (kTileBytes + 64 * sizeof(v4f));
-      const int per_cu = (int)std::min<size_t>(7, kW16CuLdsBytes / wg_lds);
-      if (nblocks > per_cu * kW16CUs && nblocks <= 4 * kW16CUs)
-        dec_w4a16_mr<12, true, XDT, OutT>(16, x, wq, ws, wz, M, N, K, y, tok_lds(phases) + sz64,
-                                          kW16CUs, phases, st);
-      else if (nblocks <= 384)
-        dec_w4a16_mr<8, true, XDT, OutT>(16, x, wq, ws, wz, M, N, K, y, lds16, nblocks, phases, st);
+    while (phases < units && tok_lds(phases) + sz16 > kDecLdsMaxBytes) ++phases;
+    if (tok_lds(phases) + sz16 <= kDecLdsMaxBytes) {
+      if (nblocks <= 384)
+        dec_w4a16_mr<8, true, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, tok_lds(phases) + sz16, nblocks, phases, st);
       else
-        dec_w4a16_mr<4, true, XDT, OutT>(16, x, wq, ws, wz, M, N, K, y, lds16, nblocks, phases, st);
+        dec_w4a16_mr<4, true, XDT, OutT>(mr, x, wq, ws, wz, M, N, K, y, tok_lds(phases) + sz16, nblocks, phases, st);
       return hipGetLastError();
     }
   }
   const size_t lds_wide = (size_t)16 * wide_waves(N) * sz_pitch(G) * 4;
   if (M <= 64 && lds_wide <= kDecLdsMaxBytes) {
-    if (M <= 16) launch_w4a16_wide<1, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
-    else if (M <= 32) launch_w4a16_wide<2, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
-    else if (M <= 48) launch_w4a16_wide<3, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
-    else launch_w4a16_wide<4, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
-    return hipGetLastError();
+    bool done;
+    if (M <= 16) done = launch_w4a16_wide<1, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
+    else if (M <= 32) done = launch_w4a16_wide<2, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
+    else if (M <= 48) done = launch_w4a16_wide<3, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
+    else done = launch_w4a16_wide<4, XDT, OutT>(x, wq, ws, wz, M, N, K, y, lds_wide, st);
+    if (done) return hipGetLastError();
   }
   constexpr int MT = 1, NT = 1, WAVES = 8, U = 2;  // measured on MI355X
   dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));

@@ -225,7 +225,13 @@ def _w4a16_floor(x64, packed, sc, zz):
                                    # last block past 256 blocks, long K
                                    (1, 17, 128), (3, 40, 640), (4, 4100, 4096),
                                    (1, 4096, 11008), (2, 1000, 4224), (1, 40, 12288),
-                                   (4, 64, 1152)])
+                                   (4, 64, 1152),
+                                   # 9-64 rows on wide layers, 2-4 weight blocks per
+                                   # workgroup, each block's K split over 2 waves
+                                   # (2-3 m-tiles) or its m-tiles (4): odd group
+                                   # counts, ragged rows and last block, one phase
+                                   (24, 6160, 1152), (40, 12304, 640), (64, 14400, 512),
+                                   (17, 16400, 384), (12, 14336, 1024), (49, 7000, 1152)])
 def test_w4a16(xfmt, fmt, M, N, K):
     rng = np.random.default_rng(M * 5 + N + K)
     packed, sc, zz = _u4_weights(rng, K, N)
