@@ -947,7 +947,10 @@ static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* 
   const size_t lds_wide = (size_t)16 * wide_waves(N) * sz_pitch(K / 128) * 4;
   if (M > 16 && M <= 64 && wide_waves(N) >= 2) {
     // 17..64 token rows on wide layers: the token rows staged once per
-    // workgroup of 2-4 weight blocks (unless K is too long for LDS)
+    // workgroup of 2-4 weight blocks (unless K is too long for LDS).  With
+    // one block per workgroup (N < 6144) the multi-tile kernel below was
+    // faster (measured on MI355X: K = 11008, N = 4096, 17 rows 13.0 against
+    // 18.0 us; K = 4096, N = 4096, 64 rows 13.0 against 14.0)
     const bool done = M <= 32 ? launch_w4a8_wide<2, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st)
                               : launch_w4a8_wide<4, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st);
     if (done) return hipGetLastError();

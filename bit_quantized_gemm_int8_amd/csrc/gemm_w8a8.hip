@@ -154,29 +154,44 @@ __global__ __launch_bounds__(64 * WAVES) void k_w8a8_dec(
 }
 
 // ---------------------------------------------------------------------------
-// Wide decode kernel (up to 64 token rows, MT m-tiles of 16): a workgroup of
-// NB waves owns NB x 16 weight rows; wave w streams its own 16 rows over the
-// whole K as whole-line units, and the waves move through K in phases of PU
-// units.  A phase's panel of token rows (16 MT rows x 128 PU bytes) is staged
-// in LDS once for all NB waves (two-deep ring, one barrier per phase), so one
-// token-row byte read from L2 serves 16 NB weight rows.  Every wave owns its
-// outputs whole: no cross-wave reduction.
+// Wide decode kernel (up to 64 token rows, MT m-tiles of 16): a workgroup owns
+// NB 16-row weight blocks, streamed over the whole K as whole-line units, and
+// moves through K in phases of PU units.  Each block has KS x MS waves: KS
+// split a phase's units, MS split the m-tiles (reading the same weights), so
+// that a SIMD holds more than one wave to hide the LDS and MFMA latencies;
+// the KS partial sums (exact int32) meet in LDS at the end.  A phase's panel
+// of token rows (16 MT rows x 128 PU bytes) is staged in LDS once for all
+// waves (two-deep ring, one barrier per phase), so one token-row byte read
+// from L2 serves 16 NB weight rows.
 // ---------------------------------------------------------------------------
-template <int MT, int NB, int PU, typename OutT>
-__global__ __launch_bounds__(64 * NB) void k_w8a8_wide(
+template <int MT, int NB, int KS, int MS, int PU>
+__host__ __device__ constexpr size_t w8a8_wide_static_lds() {
+  return (size_t)2 * 16 * MT * (kUnitBytes * PU + 16) + (size_t)NB * KS * MS * kTileBytes +
+         (size_t)(KS == 1 ? 1 : NB * MS * (KS - 1)) * (MT / MS) * 64 * 16;
+}
+
+template <int MT, int NB, int KS, int MS, int PU, typename OutT>
+__global__ __launch_bounds__(64 * NB * KS * MS) void k_w8a8_wide(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, const int8_t* __restrict__ wq,
     const float* __restrict__ ws, int M, int N, int K, OutT* __restrict__ y) {
-  constexpr int MR = 16 * MT, PB = kUnitBytes * PU, kThreads = 64 * NB;
+  static_assert(PU % KS == 0, "every wave of a block takes the same number of units");
+  static_assert(MT % MS == 0, "every wave of a block takes the same number of m-tiles");
+  constexpr int UPW = PU / KS, MTW = MT / MS;                     // units, m-tiles per wave
+  constexpr int MR = 16 * MT, PB = kUnitBytes * PU, kThreads = 64 * NB * KS * MS;
   constexpr int kPitch = PB + 16;                      // odd number of 16-byte chunks
   constexpr int kRowChunks = PB / 16, kChunks = MR * kRowChunks;
   constexpr int CPT = (kChunks + kThreads - 1) / kThreads;
   constexpr bool kFull = CPT * kThreads == kChunks;
   __shared__ __attribute__((aligned(16))) int8_t xbuf[2][MR * kPitch];
-  __shared__ __attribute__((aligned(16))) int8_t tiles[NB][kTileBytes];
+  __shared__ __attribute__((aligned(16))) int8_t tiles[NB * KS * MS][kTileBytes];
+  __shared__ v4i red[KS == 1 ? 1 : NB * MS * (KS - 1)][MTW][64];
+  static_assert(sizeof(xbuf) + sizeof(tiles) + sizeof(red) == w8a8_wide_static_lds<MT, NB, KS, MS, PU>(),
+                "static LDS bookkeeping");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int blk = wave % NB, ks = (wave / NB) % KS, ms = wave / (NB * KS);
   const int r = lane & 15, j = lane >> 4;
-  const int n_base = (blockIdx.x * NB + wave) * 16;
+  const int n_base = (blockIdx.x * NB + blk) * 16;
   const int units = (K + kUnitBytes - 1) / kUnitBytes;
   const int phases = (units + PU - 1) / PU;
 
@@ -187,11 +202,11 @@ __global__ __launch_bounds__(64 * NB) void k_w8a8_wide(
   const UnitLanes ul = unit_lanes(lane, K);
 
   struct Batch {
-    v4i w[PU][2], x[CPT];
+    v4i w[UPW][2], x[CPT];
   };
   auto load = [&](Batch& bt, int p) {
 #pragma unroll
-    for (int v = 0; v < PU; ++v) unit_load(bt.w[v], wr, ul, p * PU + v, true, K);
+    for (int v = 0; v < UPW; ++v) unit_load(bt.w[v], wr, ul, p * PU + ks * UPW + v, true, K);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int chunk = tid + c * kThreads;
@@ -203,9 +218,9 @@ __global__ __launch_bounds__(64 * NB) void k_w8a8_wide(
   };
 
   int8_t* tile = tiles[wave];
-  v4i acc[MT];
+  v4i acc[MTW];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4i{0, 0, 0, 0};
+  for (int mw = 0; mw < MTW; ++mw) acc[mw] = v4i{0, 0, 0, 0};
   auto process = [&](const Batch& bt, int p) {
     int8_t* buf = xbuf[p & 1];
 #pragma unroll
@@ -218,17 +233,17 @@ __global__ __launch_bounds__(64 * NB) void k_w8a8_wide(
     // overwrites was last read at phase p - 1, before this barrier.
     lds_barrier();
 #pragma unroll
-    for (int v = 0; v < PU; ++v) {
+    for (int v = 0; v < UPW; ++v) {
       v4i f[2];
       unit_transpose(tile, bt.w[v], ul, f);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         // past K the weight operand is zero; keep the panel read in range
-        const int kin = kUnitBytes * v + 64 * s2 + 16 * j;
+        const int kin = kUnitBytes * (ks * UPW + v) + 64 * s2 + 16 * j;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const v4i a = ld16(buf + (16 * mt + r) * kPitch + kin);
-          acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, f[s2], acc[mt], 0, 0, 0);
+        for (int mw = 0; mw < MTW; ++mw) {
+          const v4i a = ld16(buf + (16 * (ms * MTW + mw) + r) * kPitch + kin);
+          acc[mw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, f[s2], acc[mw], 0, 0, 0);
         }
       }
     }
@@ -247,16 +262,33 @@ __global__ __launch_bounds__(64 * NB) void k_w8a8_wide(
     process(b1, p + 1);
   }
 
+  if constexpr (KS > 1) {
+    // the block's other waves hand their partial sums to wave ks = 0
+    if (ks > 0) {
+#pragma unroll
+      for (int mw = 0; mw < MTW; ++mw) red[((ks - 1) * MS + ms) * NB + blk][mw][lane] = acc[mw];
+    }
+    lds_barrier();
+    if (ks > 0) return;
+#pragma unroll
+    for (int o = 0; o < KS - 1; ++o)
+#pragma unroll
+      for (int mw = 0; mw < MTW; ++mw) {
+        const v4i t = red[(o * MS + ms) * NB + blk][mw][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mw][i] += t[i];
+      }
+  }
   if (n_out < N) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mw = 0; mw < MTW; ++mw)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = 16 * mt + 4 * j + i;
+        const int m = 16 * (ms * MTW + mw) + 4 * j + i;
         if (m < M) {
           float sx = 0.f;
           if constexpr (!std::is_same<OutT, int32_t>::value) sx = xs[m];
-          y[(int64_t)m * N + n_out] = w8a8_epilogue<OutT>(acc[mt][i], sx, sw);
+          y[(int64_t)m * N + n_out] = w8a8_epilogue<OutT>(acc[mw][i], sx, sw);
         }
       }
   }
@@ -549,17 +581,39 @@ __global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict
 }
 
 constexpr int kPrefillWaves = 8;
+constexpr size_t kWideLdsBytesPerCU = 160 * 1024;
+
+// Waves per weight block (K split KS ways, PU units per phase), measured on
+// MI355X: with one block per workgroup (narrow layers, N < 6144) 4 (K = 11008,
+// N = 4096, 64 rows 38.5 -> 19.2 us; K = N = 4096 16.8 -> 10.0 us), and 4 for
+// 33-64 rows over 2-3 blocks (K = 4096, N = 8192, 64 rows 13.8 -> 12.7 us;
+// N = 11008 15.3 -> 14.7).  Otherwise the single wave per block streams near
+// the weight-read rate already and a split only adds its reduction.
+template <int MT, int NB>
+struct W8Split {
+  static constexpr int KS = NB == 1 || (MT >= 3 && NB <= 3) ? 4 : 1;
+  static constexpr int MS = 1;
+  static constexpr int PU = KS > 1 ? 4 : (MT <= 2 ? 4 : 2);
+};
+
+template <int MT, int NB, typename OutT>
+static void launch_w8a8_wide_nb(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
+                                int M, int N, int K, OutT* y, hipStream_t st) {
+  using S = W8Split<MT, NB>;
+  static_assert(w8a8_wide_static_lds<MT, NB, S::KS, S::MS, S::PU>() <= kWideLdsBytesPerCU, "LDS of a CU");
+  const int nblocks = (N + 15) / 16;
+  const dim3 grid((unsigned)((nblocks + NB - 1) / NB)), block(64 * NB * S::KS * S::MS);
+  k_w8a8_wide<MT, NB, S::KS, S::MS, S::PU, OutT><<<grid, block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
+}
+
 template <int MT, typename OutT>
 static void launch_w8a8_wide(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
                              int M, int N, int K, OutT* y, hipStream_t st) {
-  constexpr int PU = MT <= 2 ? 4 : 2;   // measured on MI355X (K = 4096, N = 11008)
-  const int nb = wide_waves(N), nblocks = (N + 15) / 16;
-  const dim3 grid((unsigned)((nblocks + nb - 1) / nb));
-  switch (nb) {
-    case 1: k_w8a8_wide<MT, 1, PU, OutT><<<grid, dim3(64), 0, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-    case 2: k_w8a8_wide<MT, 2, PU, OutT><<<grid, dim3(128), 0, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-    case 3: k_w8a8_wide<MT, 3, PU, OutT><<<grid, dim3(192), 0, st>>>(xq, xs, wq, ws, M, N, K, y); break;
-    default: k_w8a8_wide<MT, 4, PU, OutT><<<grid, dim3(256), 0, st>>>(xq, xs, wq, ws, M, N, K, y); break;
+  switch (wide_waves(N)) {
+    case 1: launch_w8a8_wide_nb<MT, 1, OutT>(xq, xs, wq, ws, M, N, K, y, st); break;
+    case 2: launch_w8a8_wide_nb<MT, 2, OutT>(xq, xs, wq, ws, M, N, K, y, st); break;
+    case 3: launch_w8a8_wide_nb<MT, 3, OutT>(xq, xs, wq, ws, M, N, K, y, st); break;
+    default: launch_w8a8_wide_nb<MT, 4, OutT>(xq, xs, wq, ws, M, N, K, y, st); break;
   }
 }
 

@@ -28,6 +28,10 @@ W8A8_SHAPES = [(16, 512, 512), (1, 16, 16), (3, 17, 48), (8, 11008, 4096), (17, 
                # wide decode kernel: three weight blocks per workgroup with the last
                # workgroup partly past N, and the full 64-token FFN-up shape
                (40, 10256, 512), (64, 11008, 4096),
+               # each weight block's K split over 4 waves: 2 blocks per workgroup
+               # with K not a multiple of 128 (ragged last phase) and an odd chunk
+               # count, one block per workgroup (narrow layers) with long K
+               (48, 8200, 1040), (64, 6144, 272), (20, 2048, 11008), (57, 3000, 4112),
                # decode kernel with long token rows (above 80 KB of LDS, one
                # workgroup per compute unit), the last size that fits and the first
                # that does not; 8 and 4 waves per workgroup on either side of 384
