@@ -686,8 +686,9 @@ def measured_peaks(steps):
 
 # ------------------------------------------------------------ batch sweep
 
-SWEEP_LAYERS = (("w8a8", 4096, 11008, "bf16"), ("w4a8", 11008, 4096, "bf16"),
-                ("w4a8", 4096, 11008, "bf16"), ("w4a16", 4096, 12288, "f16"))
+SWEEP_LAYERS = (("w8a8", 4096, 11008, "bf16"), ("w8a8", 11008, 4096, "bf16"),
+                ("w4a8", 11008, 4096, "bf16"), ("w4a8", 4096, 11008, "bf16"),
+                ("w4a16", 4096, 12288, "f16"), ("w4a16", 11008, 4096, "f16"))
 SWEEP_M = (1, 2, 4, 8, 16, 32, 64)
 
 
