@@ -782,7 +782,7 @@ KERNEL_OF = {
     "w8a8_decode_ffn_up": [("k_w8a8_dec<8,", "unsigned short>")],
     "w8a8_tiny": [("k_w8a8_fq<16,", "float>")],
     "w4a8_ffn_down": [("k_w4a8_dec<16, 8, 1, false, unsigned short>",)],
-    "w4a8_decode_ffn_up": [("k_w4a8_fdec<8, 2, false, unsigned short>",)],
+    "w4a8_decode_ffn_up": [("k_w4a8_wide<1, 3, 4, 1, 4, 2, 2, unsigned short>",)],
     "w4a8_outl_ffn_down": [("k_w4a8_dec<16, 8, 1, true, unsigned short>",)],
     "w4a8_sp24_ffn_down": [("k_w4a8_sp24<unsigned short>",)],
     "w4a16_qkv": [("k_w4a16_dec<1,", "_Float16>"), ("k_w4a16_decILi1E", "DF16_E")],
@@ -792,7 +792,7 @@ KERNEL_OF = {
 # profile file label of each workload's dominant kernel
 KERNEL_LABEL = {
     "w8a8_decode_ffn_up": "gemm_w8a8_dec", "w8a8_tiny": "gemm_w8a8_fq",
-    "w4a8_ffn_down": "gemm_w4a8_dec", "w4a8_decode_ffn_up": "gemm_w4a8_panel", "w4a16_qkv": "gemm_w4a16_dec", "w8a8_prefill": "gemm_w8a8_tiled",
+    "w4a8_ffn_down": "gemm_w4a8_dec", "w4a8_decode_ffn_up": "gemm_w4a8_wide", "w4a16_qkv": "gemm_w4a16_dec", "w8a8_prefill": "gemm_w8a8_tiled",
     "kv_llama2_7b_4k": "kv_quant_seg", "w4a8_outl_ffn_down": "gemm_w4a8_outl_dec",
     "w4a8_sp24_ffn_down": "gemm_w4a8_sp24",
 }

@@ -686,7 +686,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a8_dec2(
 }
 
 // ---------------------------------------------------------------------------
-// Wide kernel (17-64 token rows on layers of at least 384 weight blocks): as
+// Wide kernel (up to 64 token rows on layers of at least 384 weight blocks): as
 // k_w8a8_wide / k_w4a16_wide, a workgroup owns NB 16-row weight blocks and
 // moves through K in phases of PU units (2 PU groups).  Each block has KS
 // waves that split a phase's units between them, so a SIMD holds more than
@@ -922,6 +922,20 @@ static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* 
                               const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
                               hipStream_t st) {
   const size_t lds = (size_t)16 * sz_pitch(K / 128) * 4;
+  if (M <= 64 && wide_waves(N) >= 2) {
+    // layers of more than 384 blocks: the token rows staged once per
+    // workgroup of 2-4 weight blocks (unless K is too long for LDS).
+    // Measured on MI355X against the decode kernels below (K = 4096, N =
+    // 11008): 1 row 8.8 -> 7.1 us, 8 rows 9.4 -> 7.9, 16 rows 10.3 -> 7.7;
+    // 17-64 rows against the multi-tile kernel: 32 rows 21.0 -> 10.6.  With
+    // one block per workgroup (N < 6144) the kernels below were faster
+    // (K = 11008, N = 4096, 17 rows: 13.0 against 18.0 us).
+    const size_t lds_wide = (size_t)16 * wide_waves(N) * sz_pitch(K / 128) * 4;
+    const bool done = M <= 16   ? launch_w4a8_wide<1, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st)
+                      : M <= 32 ? launch_w4a8_wide<2, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st)
+                                : launch_w4a8_wide<4, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st);
+    if (done) return hipGetLastError();
+  }
   if (M <= 16 && 2 * lds <= kDecLdsMaxBytes && (N + 31) / 32 >= 256) {
     // wide layers (measured on MI355X, K = 4096: N = 11008 M = 16 14.4 ->
     // 11.0 us, M = 1 at N = 12288 10.1 -> 9.3 us); at N = 4096 its 128
@@ -943,17 +957,6 @@ static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* 
       default: k_w4a8_dec<16, WAVES, UB, false, OutT><<<grid, block, lds, st>>>(xq, xs, wq, ws, wz, nullptr, nullptr, M, N, K, y); break;
     }
     return hipGetLastError();
-  }
-  const size_t lds_wide = (size_t)16 * wide_waves(N) * sz_pitch(K / 128) * 4;
-  if (M > 16 && M <= 64 && wide_waves(N) >= 2) {
-    // 17..64 token rows on wide layers: the token rows staged once per
-    // workgroup of 2-4 weight blocks (unless K is too long for LDS).  With
-    // one block per workgroup (N < 6144) the multi-tile kernel below was
-    // faster (measured on MI355X: K = 11008, N = 4096, 17 rows 13.0 against
-    // 18.0 us; K = 4096, N = 4096, 64 rows 13.0 against 14.0)
-    const bool done = M <= 32 ? launch_w4a8_wide<2, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st)
-                              : launch_w4a8_wide<4, OutT>(xq, xs, wq, ws, wz, M, N, K, y, lds_wide, st);
-    if (done) return hipGetLastError();
   }
   if (M <= 64 && lds <= kDecLdsMaxBytes) {
     // 17..64 token rows: one weight stream for 2 or 4 tiles of 16 rows

@@ -423,16 +423,18 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
-// When quantize_gemm_w4a8 takes the panel pair: on layers of more than 256
-// 16-row weight blocks.  Measured on MI355X, whole steps (quantizer + GEMM)
-// against the per-token quantizer + plain W4A8 kernel, weights rotated
-// through 600 MB: K = 4096, N = 11008: 1-8 rows 7-9% faster, 16 rows level;
-// N = 12288, 1 row 7% faster.  On 256 blocks or fewer the pair was slower
-// at every size tried (K = 11008, N = 4096: 6-11%; K = 4096, N = 4096: 2-6%):
-// the panel quantizer costs ~0.4 us more than the plain one, more than the
-// panel GEMM gains there.
+// When quantize_gemm_w4a8 takes the panel pair: on layers of 257-383 16-row
+// weight blocks.  Measured on MI355X, whole calls (quantizer + GEMM) against
+// the per-token quantizer + the plain W4A8 GEMM, weights rotated through
+// 600 MB.  On 256 blocks or fewer the pair was slower at every size tried
+// (K = 11008, N = 4096: 6-11%; K = 4096, N = 4096: 2-6%): the panel quantizer
+// costs ~0.4 us more than the plain one, more than the panel GEMM gains
+// there.  From 384 blocks the plain GEMM is the wide kernel, which is faster
+// than the pair at every size tried (K = 4096, N = 11008: 1 row 10.3 against
+// 9.1 us, 16 rows 13.2 against 10.3; N = 14336, 28672 likewise).
 bool use_panel(int64_t M, int64_t N, int64_t K) {
-  return plan_gemm(M, N, K).ok && (N + 15) / 16 > 256;
+  const int64_t nblocks = (N + 15) / 16;
+  return plan_gemm(M, N, K).ok && nblocks > 256 && nblocks < 384;
 }
 
 template <int DT>

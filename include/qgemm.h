@@ -271,9 +271,11 @@ qg_status_t gemm_w4a8_g128_panel(const void* panel, int64_t panel_bytes, const f
  *   workspace as the panel, where it is 0 quantize_per_token_i8 then
  *   gemm_w4a8_g128, and workspace may be NULL.  Smaller than required:
  *   QG_ERR_SHAPE; NULL while required: QG_ERR_NULL.
- * The panel pair runs for 1 <= M <= 16 and K <= 16384 on N > 4096 (more than
- * 256 blocks of 16 output channels); on narrower layers the plain kernels
- * measured faster per call.
+ * The panel pair runs for 1 <= M <= 16 and K <= 16384 on 4096 < N < 6129
+ * (257-383 blocks of 16 output channels); elsewhere the plain kernels
+ * measured faster per call (on 384 blocks or more the plain GEMM is the wide
+ * kernel, which stages the token rows once per workgroup of several weight
+ * blocks).
  * K must be a positive multiple of 128 with K / 128 <= 65535.  N == 0
  * computes xq and x_scale only.
  */

@@ -149,11 +149,11 @@ def test_validation_codes():
     f4 = lib.quantize_gemm_w4a8_g128
     f4.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P,
                    ctypes.c_int, P, P, P, ctypes.c_int64, P]
-    ws = 32 * 2112                                                   # 16 x 12288 x 4096 needs it
-    assert f4(A, 2, A, A, A, 16, 12288, 4096, A, 2, A, A, A, ws - 16, None) == SHAPE
-    assert f4(A, 2, A, A, A, 16, 12288, 4096, A, 2, A, A, None, ws, None) == NULL
-    assert f4(A, 2, A, A, A, 16, 12288, 4096, A, 2, A, A, MIS, ws, None) == ALIGN
-    assert f4(A, 2, A, A, A, 16, 12288, 4096, A, 2, A, A, A, -1, None) == SHAPE
+    ws = 32 * 2112                                                   # 16 x 4160 x 4096 needs it
+    assert f4(A, 2, A, A, A, 16, 4160, 4096, A, 2, A, A, A, ws - 16, None) == SHAPE
+    assert f4(A, 2, A, A, A, 16, 4160, 4096, A, 2, A, A, None, ws, None) == NULL
+    assert f4(A, 2, A, A, A, 16, 4160, 4096, A, 2, A, A, MIS, ws, None) == ALIGN
+    assert f4(A, 2, A, A, A, 16, 4160, 4096, A, 2, A, A, A, -1, None) == SHAPE
     assert f4(A, 2, A, A, A, 8, 16, 192, A, 2, A, A, A, ws, None) == SHAPE      # K % 128
     assert f4(A, 3, A, A, A, 8, 16, 4096, A, 2, A, A, A, ws, None) == DTYPE
     assert f4(A, 2, A, A, A, 8, 16, 4096, A, 9, A, A, A, ws, None) == DTYPE
@@ -205,15 +205,16 @@ def test_fused_plan_on_the_host():
 
 def test_w4a8_workspace_on_the_host():
     """quantize_gemm_w4a8_g128_workspace_bytes: (K / 128) x 2112 bytes where
-    the panel pair runs (1..16 rows, K <= 16384, more than 256 blocks of 16
+    the panel pair runs (1..16 rows, K <= 16384, 257-383 blocks of 16
     channels), 0 where the call runs the two plain kernels; the panel's own
     size."""
     import bit_quantized_gemm_int8_amd as q
     _lib()
     wb = q.quantize_gemm_w4a8_g128_workspace_bytes
     assert wb(16, 4112, 11008) == 86 * 2112           # 257 weight blocks: the panel pair
-    assert wb(16, 11008, 4096) == 32 * 2112
-    assert wb(1, 12288, 4096) == 32 * 2112
+    assert wb(16, 6128, 4096) == 32 * 2112            # 383 blocks
+    assert wb(16, 6144, 4096) == 0                    # 384 blocks: the wide GEMM
+    assert wb(16, 11008, 4096) == 0 and wb(1, 12288, 4096) == 0
     assert wb(2, 4112, 16384) == 128 * 2112           # the longest K
     assert wb(2, 4112, 16512) == 0
     assert wb(16, 4096, 11008) == 0                   # 256 blocks: the plain kernels

@@ -3,7 +3,7 @@
 Its codes and scales must be those of quantize_per_token_i8 and its int32
 per-group accumulators those of gemm_w4a8_g128, bit for bit, whichever form
 the library picks (the panel pair quantize_per_token_i8_panel +
-gemm_w4a8_g128_panel on layers of more than 256 weight blocks, the plain
+gemm_w4a8_g128_panel on layers of 257-383 weight blocks, the plain
 kernels otherwise); the panel pair is also run explicitly on every shape the
 panel takes.  Scaled outputs are held to the oracle with the W4A8 rounding
 bound.  The panel's layout is checked byte for byte against its documented
@@ -143,7 +143,7 @@ def test_dirty_workspace_and_smaller_second_call():
 
 
 def test_workspace_too_small_is_rejected():
-    M, N, K = 4, 8192, 4096
+    M, N, K = 4, 4160, 4096
     x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
     wq = torch.zeros((N, K // 8), dtype=torch.int32, device="cuda")
     z = torch.zeros((N, K // 128), dtype=torch.float16, device="cuda")
@@ -164,13 +164,14 @@ def test_codes_only_when_n_is_zero():
     assert y.shape == (4, 0) and torch.equal(xq, xq2) and torch.equal(xs, xs2)
 
 
-def test_graph_replay():
-    M, N, K = 8, 11008, 4096
+@pytest.mark.parametrize("N", [4160, 11008])   # the panel pair; the plain quantizer + wide GEMM
+def test_graph_replay(N):
+    M, K = 8, 4096
     rng = np.random.default_rng(9)
     packed, sc, zz = _weights(rng, K, N)
     wq, s_d, z_d = to_dev(packed), to_dev(sc), to_dev(zz)
     x = _x(77, M, K, "bf16")
-    ws = torch.empty(qg.quantize_gemm_w4a8_g128_workspace_bytes(M, N, K), dtype=torch.uint8,
+    ws = torch.empty(max(qg.quantize_gemm_w4a8_g128_workspace_bytes(M, N, K), 1), dtype=torch.uint8,
                      device="cuda")
     y, xq, xs = qg.quantize_gemm_w4a8_g128(x, wq, s_d, z_d, workspace=ws)
     torch.cuda.synchronize()
