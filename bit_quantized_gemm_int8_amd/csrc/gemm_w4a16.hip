@@ -635,9 +635,8 @@ static void dec_w4a16_mr(int mr, const uint16_t* x, const int32_t* wq, const uin
   }
 }
 
-// Compute units of an MI355X, and the LDS of one.
+// Compute units of an MI355X.
 constexpr int kW16CUs = 256;
-constexpr size_t kW16CuLdsBytes = 160 * 1024;
 
 template <int XDT, typename OutT>
 static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
@@ -649,7 +648,7 @@ static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint1
     const int nblocks = (N + 15) / 16;
     // one-block workgroups of 4 waves that fit a CU (LDS; at most 7 by registers)
     const size_t wg_lds = lds + 4 * (kTileBytes + 64 * sizeof(v4f));
-    const int per_cu = (int)std::min<size_t>(7, kW16CuLdsBytes / wg_lds);
+    const int per_cu = (int)std::min<size_t>(7, kLdsBytesPerCU / wg_lds);
     const size_t lds_multi = (size_t)mr * stage_pitch(2 * K) + (size_t)64 * sz_pitch(G) * 4;
     if (nblocks > per_cu * kW16CUs && nblocks <= 4 * kW16CUs && lds_multi <= kDecLdsMaxBytes) {
       // more blocks than one-block workgroups can be resident at once: one

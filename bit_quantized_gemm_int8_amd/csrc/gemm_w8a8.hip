@@ -581,7 +581,6 @@ __global__ __launch_bounds__(64 * NW) void k_w8a8_tiled(const int8_t* __restrict
 }
 
 constexpr int kPrefillWaves = 8;
-constexpr size_t kWideLdsBytesPerCU = 160 * 1024;
 
 // Waves per weight block (K split KS ways, PU units per phase), measured on
 // MI355X: with one block per workgroup (narrow layers, N < 6144) 4 (K = 11008,
@@ -600,7 +599,7 @@ template <int MT, int NB, typename OutT>
 static void launch_w8a8_wide_nb(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
                                 int M, int N, int K, OutT* y, hipStream_t st) {
   using S = W8Split<MT, NB>;
-  static_assert(w8a8_wide_static_lds<MT, NB, S::KS, S::MS, S::PU>() <= kWideLdsBytesPerCU, "LDS of a CU");
+  static_assert(w8a8_wide_static_lds<MT, NB, S::KS, S::MS, S::PU>() <= kLdsBytesPerCU, "LDS of a CU");
   const int nblocks = (N + 15) / 16;
   const dim3 grid((unsigned)((nblocks + NB - 1) / NB)), block(64 * NB * S::KS * S::MS);
   k_w8a8_wide<MT, NB, S::KS, S::MS, S::PU, OutT><<<grid, block, 0, st>>>(xq, xs, wq, ws, M, N, K, y);
@@ -623,9 +622,8 @@ static void launch_w8a8_wide(const int8_t* xq, const float* xs, const int8_t* wq
 // staging its own slice of the rows.
 constexpr size_t kDecLdsBigBytes = 112 * 1024;
 
-// Compute units of an MI355X, and the LDS of one.
+// Compute units of an MI355X.
 constexpr int kDecCUs = 256;
-constexpr size_t kCuLdsBytes = 160 * 1024;
 
 // LDS bytes of the decode kernel's token slice with `phases` phases (the
 // kernel's own pitch: whole units per phase).
@@ -677,7 +675,7 @@ static hipError_t gemm_w8a8_t(const int8_t* xq, const float* xs, const int8_t* w
       // One-block workgroups of 4 waves: how many fit a CU (LDS, and 28
       // waves at this kernel's register count).
       const size_t wg_lds = lds + 4 * (kTileBytes + 64 * sizeof(v4i));
-      const int per_cu = (int)std::min<size_t>(7, kCuLdsBytes / wg_lds);
+      const int per_cu = (int)std::min<size_t>(7, kLdsBytesPerCU / wg_lds);
       if (nblocks > per_cu * kDecCUs && nblocks <= 4 * kDecCUs && lds <= kDecLdsMaxBytes) {
         // more blocks than one-block workgroups can be resident at once: one
         // workgroup of 12 waves per CU over 3-4 blocks instead of a second
