@@ -29,8 +29,11 @@ W8A8_CASES = [
     (16, 4096, 2048),    # same, 4 waves (K < 4096)
     (16, 4096, 2032),    # wide (K < 2048)
     (16, 4112, 4096),    # wide (N/16 = 257)
-    (17, 64, 4096),      # wide (M > 16)
-    (64, 64, 1024),      # wide, 4 tiles of 16 rows
+    (17, 64, 4096),      # wide (M > 16), one block per workgroup: K split over 4 waves
+    (64, 64, 1024),      # wide, 4 tiles of 16 rows, K split over 4 waves
+    (17, 8192, 1024),    # wide, 2 blocks per workgroup, one wave per block (2 m-tiles)
+    (33, 8192, 1024),    # wide, 2 blocks per workgroup, K split over 4 waves (3 m-tiles)
+    (33, 16400, 1024),   # wide, 4 blocks per workgroup, one wave per block
     (65, 64, 1024),      # LDS-tiled prefill kernel
     (8, 6144, 4096),     # decode, 8 waves (N/16 = 384)
     (8, 6160, 4096),     # decode, 4 waves (N/16 = 385)
@@ -60,8 +63,14 @@ def test_w8a8_boundaries(M, N, K):
 
 W4A8_CASES = [
     (16, 64, 1024),      # decode kernel (M <= 16)
-    (4, 8160, 1024),     # decode kernel (N / 32 = 255)
-    (4, 8176, 1024),     # two weight blocks per wave (N / 32 = 256, last block ragged)
+    (4, 6128, 1024),     # decode kernel (383 blocks of 16 rows)
+    (4, 6144, 1024),     # wide kernel (384 blocks: 2 per workgroup, K split over 4 waves)
+    (16, 6144, 1024),    # wide kernel, 16 rows
+    (1, 12304, 1024),    # wide kernel, 3 blocks per workgroup, the last workgroup ragged
+    (8, 16400, 1024),    # wide kernel, 4 blocks per workgroup (K split over 2 waves)
+    (17, 6128, 1024),    # one weight stream, 2 tiles of 16 rows (383 blocks)
+    (17, 6144, 1024),    # wide kernel, 2 m-tiles
+    (33, 6144, 1024),    # wide kernel, 4 m-tiles (K and m-tiles split over 2 waves each)
     (17, 64, 1024),      # one weight stream, 2 tiles of 16 rows
     (32, 64, 1024),      # 2 tiles, both full
     (33, 64, 1024),      # 4 tiles
@@ -92,15 +101,17 @@ W4A16_CASES = [
     (8, 6144, 1024),     # decode, 8 waves (N/16 = 384)
     (8, 6160, 1024),     # decode, 4 waves
     (8, 64, 4864),       # decode with token rows near 80 KB
-    (8, 64, 4992),       # rows past 80 KB: wide kernel
-    (9, 64, 1024),       # wide kernel (9..16 rows, K < 1536)
-    (16, 4096, 1536),    # 16-row decode kernel (K >= 1536, N/16 <= 512)
-    (16, 4096, 1408),    # wide kernel (K < 1536)
-    (16, 8192, 2048),    # 16-row decode kernel, 512 blocks
-    (16, 8208, 2048),    # wide kernel (513 blocks, K < 4096)
-    (12, 12288, 4096),   # 16-row decode kernel, 768 blocks over 12-wave workgroups, 2 phases
-    (12, 12304, 4096),   # wide kernel (769 blocks)
-    (10, 4096, 11008),   # 16-row decode kernel, 7 phases of K
+    (8, 64, 4992),       # rows past 80 KB: decode kernel in 2 phases of K
+    (4, 64, 11008),      # 4 rows of K = 11008 (86 KB): 2 phases
+    (2, 64, 11008),      # 2 rows (43 KB): one phase
+    (9, 64, 1024),       # wide kernel (9..16 rows), one block per workgroup, K split in 4
+    (16, 4096, 1536),    # wide kernel, 256 blocks
+    (16, 8192, 2048),    # wide kernel, 2 blocks per workgroup, K split in 2
+    (12, 12304, 4096),   # wide kernel, 3 blocks per workgroup, the last ragged
+    (10, 4096, 11008),   # wide kernel, long K (86 groups)
+    (17, 4096, 1024),    # wide kernel, 2 m-tiles, one block per workgroup: 2 x 2 waves
+    (48, 12288, 512),    # wide kernel, 3 m-tiles, K split in 2
+    (64, 6144, 256),     # wide kernel, 4 m-tiles split over 2 waves
     (65, 40, 256),       # direct-load kernel (M > 64)
 ]
 

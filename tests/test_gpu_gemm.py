@@ -154,14 +154,16 @@ def test_w4a8_group_acc_bitwise(M, N, K):
     np.testing.assert_array_equal(to_np(acc), oracle.gemm_w4a8_g128_acc(xq, packed, zz))
 
 
-@pytest.mark.parametrize("M", [24, 40])
-def test_w4a8_long_k_sampled(M):
-    """17-64 rows on a wide layer whose K is too long for the wide kernel's
-    LDS (K = 36864: 288 groups of scales per weight row); the launch takes
-    the multi-tile kernel instead.  Seeded random codes, zero points and
-    scales; per-group sums exact and scaled outputs checked on sampled
-    columns (the first, the last and 46 drawn)."""
-    N, K = 12288, 36864
+@pytest.mark.parametrize("M,K", [(24, 36864), (40, 40960), (8, 65536)])
+def test_w4a8_long_k_sampled(M, K):
+    """A wide layer whose K is too long for the wide kernel's LDS with float
+    outputs (scales of 288-512 groups per weight row): that launch takes the
+    multi-tile kernel (17-64 rows) or the two-blocks-per-wave decode kernel
+    (up to 16) instead, while the int32 per-group outputs, whose kernel keeps
+    no partial sums in LDS, still fit the wide kernel.  Seeded random codes,
+    zero points and scales; per-group sums exact and scaled outputs checked
+    on sampled columns (the first, the last and 46 drawn)."""
+    N = 12288
     G = K // 128
     rng = np.random.default_rng(M * 7 + 1)
     packed = rng.integers(0, 2 ** 32, (N, K // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)
