@@ -785,14 +785,14 @@ KERNEL_OF = {
     "w4a8_decode_ffn_up": [("k_w4a8_wide<1, 3, 4, 1, 4, 2, 2, unsigned short>",)],
     "w4a8_outl_ffn_down": [("k_w4a8_dec<16, 8, 1, true, unsigned short>",)],
     "w4a8_sp24_ffn_down": [("k_w4a8_sp24<unsigned short>",)],
-    "w4a16_qkv": [("k_w4a16_dec<1,", "_Float16>"), ("k_w4a16_decILi1E", "DF16_E")],
+    "w4a16_qkv": [("k_w4a16_gemv<4, 2,",), ("k_w4a16_gemvILi4ELi2E",)],
     "w8a8_prefill": [("k_w8a8_tiled<", "unsigned short>")],
     "kv_llama2_7b_4k": [("k_kv_quant_seg<2, 4>",)],
 }
 # profile file label of each workload's dominant kernel
 KERNEL_LABEL = {
     "w8a8_decode_ffn_up": "gemm_w8a8_dec", "w8a8_tiny": "gemm_w8a8_fq",
-    "w4a8_ffn_down": "gemm_w4a8_dec", "w4a8_decode_ffn_up": "gemm_w4a8_wide", "w4a16_qkv": "gemm_w4a16_dec", "w8a8_prefill": "gemm_w8a8_tiled",
+    "w4a8_ffn_down": "gemm_w4a8_dec", "w4a8_decode_ffn_up": "gemm_w4a8_wide", "w4a16_qkv": "gemm_w4a16_gemv", "w8a8_prefill": "gemm_w8a8_tiled",
     "kv_llama2_7b_4k": "kv_quant_seg", "w4a8_outl_ffn_down": "gemm_w4a8_outl_dec",
     "w4a8_sp24_ffn_down": "gemm_w4a8_sp24",
 }

@@ -620,6 +620,170 @@ static bool launch_w4a16_wide(const uint16_t* x, const int32_t* wq, const uint16
   }
 }
 
+// ---------------------------------------------------------------------------
+// One fp16 token row (M = 1): a matrix-vector product, where a 16x16 MFMA
+// would spend 15 of its 16 rows on padding.  It runs on the vector ALU.
+//
+// Lane l of a wave covers bytes 16 l .. 16 l + 15 of every kilobyte c of a
+// weight row: codes k = 2048 c + 32 l + [0, 32), a quarter of group
+// g = 16 c + l / 4.  The lane keeps the matching 32 activations of every c
+// in registers, shuffled once into the unpack order.  A wave owns R
+// consecutive weight rows and issues all its R x C one-kilobyte weight loads
+// (whole cache lines) before the first multiply; no LDS, no barrier.
+//
+// Per packed word of 8 codes (nibble j = code j):
+//   (w & 0x000F000F) | 0x64006400 = fp16 (1024 + q0, 1024 + q4), plus the
+//       pair -(1024 + z): (q0 - z, q4 - z);
+//   (w & 0x00F000F0) | 0x64006400 = (1024 + 16 q1, 1024 + 16 q5), times 1/16
+//       plus -(64 + z) in one packed fma: (q1 - z, q5 - z);
+//   the same of w >> 8 for codes (2, 6) and (3, 7).
+// Every fp16 result is an exact small integer; v_dot2_f32_f16 adds
+// x_a (q_a - z) + x_b (q_b - z) into a binary32 sum.  The four lanes of a
+// group add their sums (DPP), the group sum is scaled by s in binary32 (as in
+// the matrix-core kernels), and the lanes' totals are summed over the wave at
+// the end.
+// ---------------------------------------------------------------------------
+constexpr int kGemvWaves = 4;
+
+template <int CTRL>
+__device__ __forceinline__ float mov_dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+template <int R, int C, typename OutT>
+__global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ wq,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int N, int K,
+    OutT* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = (blockIdx.x * kGemvWaves + wave) * R;
+  if (n0 >= N) return;   // wave-uniform
+  const int G = K >> 7, RB = K >> 1;   // groups and packed bytes per weight row
+  const int rows = min(R, N - n0);
+  const rsrc_t wr = make_rsrc_uniform(wq + (int64_t)n0 * (K >> 3), (u32)(rows * RB));
+  const rsrc_t sr = make_rsrc_uniform(wscale + (int64_t)n0 * G, (u32)(rows * G * 2));
+  const rsrc_t zr = make_rsrc_uniform(wzero + (int64_t)n0 * G, (u32)(rows * G * 2));
+  const rsrc_t xr = make_rsrc_uniform(x, (u32)(K * 2));
+
+  // Activations first (L2 hits, needed by the first multiply), then the
+  // scales and zero points, then the weight stream in the order it is used.
+  // Pieces past the row end read as zeros: x through its resource's range,
+  // weights, scales and zero points through kOOB (their resources span the
+  // wave's rows).
+  v4i xv[C][4];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[c][i] = bld16(xr, (u32)(4096 * c + 64 * lane + 16 * i));
+  uint16_t sb[R][C], zb[R][C];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int g = 16 * c + (lane >> 2);
+      const u32 o = g < G ? (u32)(2 * (r * G + g)) : kOOB;
+      sb[r][c] = bld2(sr, o);
+      zb[r][c] = bld2(zr, o);
+    }
+  v4i wv[R][C];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int b = 1024 * c + 16 * lane;
+      wv[r][c] = bld16_nt(wr, b < RB ? (u32)(r * RB + b) : kOOB);
+    }
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[c][i] = shuffle_halves(xv[c][i]);
+
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  float yacc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    yacc[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const float zf = f16_bits_to_f32(zb[r][c]);
+      const u32 a = f32_to_f16_bits(-(1024.f + zf)), b = f32_to_f16_bits(-(64.f + zf));
+      const h2 nz_lo = __builtin_bit_cast(h2, a | (a << 16));
+      const h2 nz_hi = __builtin_bit_cast(h2, b | (b << 16));
+      float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32 w = (u32)wv[r][c][i], w8 = w >> 8;
+        const h2 d0 = __builtin_bit_cast(h2, and_or(w, 0x000F000Fu, 0x64006400u)) + nz_lo;
+        const h2 d1 = __builtin_elementwise_fma(
+            __builtin_bit_cast(h2, and_or(w, 0x00F000F0u, 0x64006400u)), sixteenth, nz_hi);
+        const h2 d2 = __builtin_bit_cast(h2, and_or(w8, 0x000F000Fu, 0x64006400u)) + nz_lo;
+        const h2 d3 = __builtin_elementwise_fma(
+            __builtin_bit_cast(h2, and_or(w8, 0x00F000F0u, 0x64006400u)), sixteenth, nz_hi);
+        // (the components pass through int: this compiler's bit_cast of a
+        // vector component expression reads component 0 whatever the index)
+        p0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (int)xv[c][i][0]), d0, p0, false);
+        p1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (int)xv[c][i][1]), d1, p1, false);
+        p0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (int)xv[c][i][2]), d2, p0, false);
+        p1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (int)xv[c][i][3]), d3, p1, false);
+      }
+      // the group's sum over its four lanes, identical in all four
+      float p = p0 + p1;
+      p += mov_dpp_f<0xB1>(p);   // quad_perm [1,0,3,2]
+      p += mov_dpp_f<0x4E>(p);   // quad_perm [2,3,0,1]
+      yacc[r] = __builtin_fmaf(f16_bits_to_f32(sb[r][c]), p, yacc[r]);
+    }
+  }
+
+  // Sum over the 16 quads: rotations by 4 and 8 within each row of 16 lanes,
+  // then the four rows.  Lane r stores weight row r's output.
+  float mine = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float v = yacc[r];
+    v += mov_dpp_f<0x124>(v);   // row_ror:4
+    v += mov_dpp_f<0x128>(v);   // row_ror:8
+    const float t = (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+    mine = lane == r ? t : mine;
+  }
+  if (lane < rows) y[n0 + lane] = Out<OutT>::cvt(mine);
+}
+
+template <int R, int C, typename OutT>
+static void launch_w4a16_gemv_rc(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
+                                 const uint16_t* wz, int N, int K, OutT* y, hipStream_t st) {
+  const int waves = (N + R - 1) / R;
+  const dim3 grid((unsigned)((waves + kGemvWaves - 1) / kGemvWaves)), block(64 * kGemvWaves);
+  k_w4a16_gemv<R, C, OutT><<<grid, block, 0, st>>>(x, wq, ws, wz, N, K, y);
+}
+
+// Weight rows of at most 2 KB (K <= 4096), where it measured faster than the
+// matrix-core decode kernel on MI355X (A/B, graphs of 200 calls, weights
+// rotated through 600 MB; us, this kernel / decode kernel): K = 4096 with
+// N = 12288 7.73-7.84 / 7.82-8.13, N = 11008 6.81-6.86 / 7.18-7.60,
+// N = 4096 4.14-4.15 / 4.49-4.52.  Longer rows lose: the dequantizing VALU
+// work (13 instructions per 8 codes, against 11 with the matrix cores) no
+// longer hides under the stream (K = 11008, N = 4096: 10.2 / 8.1; K = 8192,
+// N = 28672: 26.8 / 25.0).  Four rows per wave (eight 1 KB loads in flight)
+// at 2 KB per row, eight at 1 KB.
+template <typename OutT>
+static bool launch_w4a16_gemv(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
+                              const uint16_t* wz, int N, int K, OutT* y, hipStream_t st) {
+  if (K > 2048) {
+    if (K > 4096) return false;
+    launch_w4a16_gemv_rc<4, 2, OutT>(x, wq, ws, wz, N, K, y, st);
+  } else {
+    launch_w4a16_gemv_rc<8, 1, OutT>(x, wq, ws, wz, N, K, y, st);
+  }
+  return true;
+}
+
 template <int WAVES, bool GEN, int XDT, typename OutT>
 static void dec_w4a16_mr(int mr, const uint16_t* x, const int32_t* wq, const uint16_t* ws,
                          const uint16_t* wz, int M, int N, int K, OutT* y, size_t lds, int groups,
@@ -642,6 +806,9 @@ template <int XDT, typename OutT>
 static hipError_t gemm_w4a16_t(const uint16_t* x, const int32_t* wq, const uint16_t* ws,
                                const uint16_t* wz, int M, int N, int K, OutT* y, hipStream_t st) {
   const int G = K / 128;
+  if constexpr (XDT == F16) {
+    if (M == 1 && launch_w4a16_gemv<OutT>(x, wq, ws, wz, N, K, y, st)) return hipGetLastError();
+  }
   const int mr = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
   const size_t lds = (size_t)mr * stage_pitch(2 * K) + (size_t)16 * sz_pitch(G) * 4;
   if (M <= 8 && lds <= kDecLdsMaxBytes) {

@@ -425,7 +425,9 @@ qg_status_t gemm_w4a8_g128_sparse24(const int8_t* xq, const float* x_scale, cons
 /*
  * W4A16 weight-only GEMM: 16-bit float activations, g=128 uint4 weights
  * unpacked to exact (q - z) values in registers and fed to the fp16 (or bf16)
- * matrix cores; each group's binary32 partial sum is then scaled by s.
+ * matrix cores (one fp16 token row with K <= 4096: to fp16 dot products on
+ * the vector ALU instead); each group's binary32 partial sum is then scaled
+ * by s.
  * 「第4章：量化」 §3.1 (weight-only 4-bit), §3.5 (fused dequantization);
  * 「Quantization & Flash Attention」 §2.2 (the AWQ-folded weights it serves).
  *   p[m,g,n] = sum_{k in g} x[m,k] (q[n,k] - z[n,g]);  y[m,n] = sum_g s[n,g] p[m,g,n]

@@ -113,6 +113,13 @@ W4A16_CASES = [
     (48, 12288, 512),    # wide kernel, 3 m-tiles, K split in 2
     (64, 6144, 256),     # wide kernel, 4 m-tiles split over 2 waves
     (65, 40, 256),       # direct-load kernel (M > 64)
+    (1, 64, 4096),       # one token row: vector-ALU kernel, 2 KB weight rows, 4 per wave
+    (1, 50, 3200),       # same, second kilobyte of each row ragged, last wave 2 rows
+    (1, 37, 2048),       # same, 1 KB rows, 8 per wave
+    (1, 37, 1152),       # same, 576-byte rows (lanes past the row end idle)
+    (1, 16, 128),        # same, one group
+    (1, 12300, 4096),    # same, 3075 waves
+    (1, 64, 4224),       # rows past 2 KB: the matrix-core decode kernel
 ]
 
 

@@ -256,17 +256,39 @@ def test_w4a16(xfmt, fmt, M, N, K):
     print(f"w4a16 x{xfmt}->{fmt} {M}x{N}x{K}: {n} of {yref.size} within the floor only")
 
 
-def test_w4a16_exact_case_bitwise():
+@pytest.mark.parametrize("M,N,K", [(4, 48, 512), (1, 48, 512), (1, 40, 4096)])
+def test_w4a16_exact_case_bitwise(M, N, K):
     """Power-of-two scales and small-integer activations make every partial sum
-    exact in binary32, so the fp32 output must equal y_exact bit for bit."""
-    rng = np.random.default_rng(9)
-    M, N, K = 4, 48, 512
+    exact in binary32, so the fp32 output must equal y_exact bit for bit (one
+    token row runs the vector-ALU kernel, four rows the matrix cores)."""
+    rng = np.random.default_rng(9 + M + K)
     codes = rng.integers(0, 16, (N, K)).astype(np.uint8)
     packed = oracle.pack_u4(codes)
     G = K // 128
     zz = rng.integers(0, 16, (N, G)).astype(np.float16)
     sc = (2.0 ** rng.integers(-8, -2, (N, G))).astype(np.float16)
     xh = rng.integers(-8, 9, (M, K)).astype(np.float16)
+    y = qg.gemm_w4a16_g128(to_dev(xh), to_dev(packed), to_dev(sc), to_dev(zz),
+                           out_dtype=torch.float32)
+    np.testing.assert_array_equal(out_f64(y), oracle.gemm_w4a16_g128(xh.astype(np.float64),
+                                                                     packed, sc, zz))
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (1, 2048), (4, 1024)])
+def test_w4a16_subnormal_activations_bitwise(M, K):
+    """fp16 subnormal activations k 2^-24 (|k| <= 8) must enter the products
+    unflushed.  With scales 2^-4 or 2^-3 every partial sum is an integer
+    multiple of 2^-28 below 2^24 units, so the fp32 output is exact and must
+    equal y_exact bit for bit; a flushed subnormal would change it."""
+    rng = np.random.default_rng(17 + M + K)
+    N = 72
+    G = K // 128
+    codes = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    packed = oracle.pack_u4(codes)
+    zz = rng.integers(0, 16, (N, G)).astype(np.float16)
+    sc = (2.0 ** rng.integers(-4, -2, (N, G))).astype(np.float16)
+    xh = (rng.integers(-8, 9, (M, K)) * 2.0 ** -24).astype(np.float16)
+    assert np.count_nonzero(np.abs(xh) < 2.0 ** -14) > K // 2   # mostly subnormal
     y = qg.gemm_w4a16_g128(to_dev(xh), to_dev(packed), to_dev(sc), to_dev(zz),
                            out_dtype=torch.float32)
     np.testing.assert_array_equal(out_f64(y), oracle.gemm_w4a16_g128(xh.astype(np.float64),
