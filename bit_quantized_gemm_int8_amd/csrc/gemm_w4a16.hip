@@ -10,9 +10,11 @@
 // exact small integer; the scale multiplies the binary32 group sum, never
 // the 16-bit operand, so the only roundings are those of binary32 sums.
 //
-// fp16 unpack: (w >> 4i) & 0x000F000F | 0x64006400 is the fp16 pair
-// (1024 + q_i, 1024 + q_{i+4}); a packed fp16 subtract of (1024 + z) leaves
-// (q - z) exactly.  The activation halves are shuffled into the matching
+// fp16 unpack: (w & 0x000F000F) | 0x64006400 is the fp16 pair
+// (1024 + q_0, 1024 + q_4), and a packed fp16 add of -(1024 + z) leaves
+// (q - z) exactly; the odd nibbles (w & 0x00F000F0) give 1024 + 16 q, which one
+// packed fma by 1/16 and -(64 + z) takes to (q - z) exactly; w >> 8 gives the
+// other four codes.  The activation halves are shuffled into the matching
 // [0,4,1,5,2,6,3,7] order.
 #include "qg_decode.hpp"
 #include "qg_device.hpp"
@@ -42,16 +44,33 @@ __device__ __forceinline__ u32 and_or(u32 x, u32 mask, u32 bits) {
   return r;
 }
 
-// 8 codes of word w -> (q - z) as fp16 halves in order [q0 q4 q1 q5 q2 q6 q3 q7]
-__device__ __forceinline__ v4i unpack_f16(u32 w, u32 zz /* fp16 pair of 1024 + z */) {
-  v4i r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32 t = and_or(w >> (4 * i), 0x000F000Fu, 0x64006400u);
-    const h2 d = __builtin_bit_cast(h2, t) - __builtin_bit_cast(h2, zz);
-    r[i] = __builtin_bit_cast(int, d);
-  }
-  return r;
+// The zero point z (an integer 0..15) as the two packed fp16 addends the
+// unpack uses: -(1024 + z) and -(64 + z), both exact.
+struct ZeroF16 {
+  h2 lo, hi;
+};
+__device__ __forceinline__ ZeroF16 zero_f16(float zf) {
+  const u32 a = f32_to_f16_bits(-(1024.f + zf)), b = f32_to_f16_bits(-(64.f + zf));
+  return ZeroF16{__builtin_bit_cast(h2, a | (a << 16)), __builtin_bit_cast(h2, b | (b << 16))};
+}
+
+// 8 codes of word w -> (q - z) as fp16 halves in order [q0 q4 q1 q5 q2 q6 q3 q7]:
+//   (w & 0x000F000F) | 0x64006400 = (1024 + q0, 1024 + q4), plus -(1024 + z);
+//   (w & 0x00F000F0) | 0x64006400 = (1024 + 16 q1, 1024 + 16 q5), times 1/16
+//       plus -(64 + z) in one packed fma;
+//   the same of w >> 8 for (q2, q6) and (q3, q7).
+// Every step is exact (small integers); 9 instructions per word.
+__device__ __forceinline__ v4i unpack_f16(u32 w, const ZeroF16& zp) {
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const u32 w8 = w >> 8;
+  const h2 d0 = __builtin_bit_cast(h2, and_or(w, 0x000F000Fu, 0x64006400u)) + zp.lo;
+  const h2 d1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(w, 0x00F000F0u, 0x64006400u)),
+                                          sixteenth, zp.hi);
+  const h2 d2 = __builtin_bit_cast(h2, and_or(w8, 0x000F000Fu, 0x64006400u)) + zp.lo;
+  const h2 d3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(w8, 0x00F000F0u, 0x64006400u)),
+                                          sixteenth, zp.hi);
+  return v4i{__builtin_bit_cast(int, d0), __builtin_bit_cast(int, d1), __builtin_bit_cast(int, d2),
+             __builtin_bit_cast(int, d3)};
 }
 
 // bf16: (q - z) built exactly in binary32 (2^23 + q minus 2^23 + z), whose
@@ -113,10 +132,9 @@ __device__ __forceinline__ void w4a16_mma(const W4A16Batch<MT, NT, U>& bt, int g
       const float s = f16_bits_to_f32(bt.sbits[u][t]);
       v4i b[4];
       if constexpr (XDT == F16) {
-        const u32 zh = f32_to_f16_bits(1024.f + zf);
-        const u32 zz = zh | (zh << 16);
+        const ZeroF16 zp = zero_f16(zf);
 #pragma unroll
-        for (int h = 0; h < 4; ++h) b[h] = unpack_f16((u32)bt.wv[u][t][h], zz);
+        for (int h = 0; h < 4; ++h) b[h] = unpack_f16((u32)bt.wv[u][t][h], zp);
       } else {
         const float zb = 8388608.f + zf;
 #pragma unroll
@@ -351,10 +369,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_dec(
           const float zf = f16_bits_to_f32((uint16_t)(szw >> 16));
           v4i bw[4];
           if constexpr (XDT == F16) {
-            const u32 zh = f32_to_f16_bits(1024.f + zf);
-            const u32 zz = zh | (zh << 16);
+            const ZeroF16 zp = zero_f16(zf);
 #pragma unroll
-            for (int h = 0; h < 4; ++h) bw[h] = unpack_f16((u32)f[s][h], zz);
+            for (int h = 0; h < 4; ++h) bw[h] = unpack_f16((u32)f[s][h], zp);
           } else {
             const float zb = 8388608.f + zf;
 #pragma unroll
@@ -509,10 +526,9 @@ __global__ __launch_bounds__(64 * NB * KS * MS) void k_w4a16_wide(
         const float zf = f16_bits_to_f32((uint16_t)(szw >> 16));
         v4i bw[4];
         if constexpr (XDT == F16) {
-          const u32 zh = f32_to_f16_bits(1024.f + zf);
-          const u32 zz = zh | (zh << 16);
+          const ZeroF16 zp = zero_f16(zf);
 #pragma unroll
-          for (int h = 0; h < 4; ++h) bw[h] = unpack_f16((u32)f[s2][h], zz);
+          for (int h = 0; h < 4; ++h) bw[h] = unpack_f16((u32)f[s2][h], zp);
         } else {
           const float zb = 8388608.f + zf;
 #pragma unroll
@@ -705,33 +721,26 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(
 #pragma unroll
     for (int i = 0; i < 4; ++i) xv[c][i] = shuffle_halves(xv[c][i]);
 
-  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   float yacc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     yacc[r] = 0.f;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const float zf = f16_bits_to_f32(zb[r][c]);
-      const u32 a = f32_to_f16_bits(-(1024.f + zf)), b = f32_to_f16_bits(-(64.f + zf));
-      const h2 nz_lo = __builtin_bit_cast(h2, a | (a << 16));
-      const h2 nz_hi = __builtin_bit_cast(h2, b | (b << 16));
+      const ZeroF16 zp = zero_f16(f16_bits_to_f32(zb[r][c]));
       float p0 = 0.f, p1 = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const u32 w = (u32)wv[r][c][i], w8 = w >> 8;
-        const h2 d0 = __builtin_bit_cast(h2, and_or(w, 0x000F000Fu, 0x64006400u)) + nz_lo;
-        const h2 d1 = __builtin_elementwise_fma(
-            __builtin_bit_cast(h2, and_or(w, 0x00F000F0u, 0x64006400u)), sixteenth, nz_hi);
-        const h2 d2 = __builtin_bit_cast(h2, and_or(w8, 0x000F000Fu, 0x64006400u)) + nz_lo;
-        const h2 d3 = __builtin_elementwise_fma(
-            __builtin_bit_cast(h2, and_or(w8, 0x00F000F0u, 0x64006400u)), sixteenth, nz_hi);
-        // (the components pass through int: this compiler's bit_cast of a
-        // vector component expression reads component 0 whatever the index)
-        p0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (int)xv[c][i][0]), d0, p0, false);
-        p1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (int)xv[c][i][1]), d1, p1, false);
-        p0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (int)xv[c][i][2]), d2, p0, false);
-        p1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (int)xv[c][i][3]), d3, p1, false);
+        const v4i d = unpack_f16((u32)wv[r][c][i], zp);
+        // (vector components pass through int: this compiler's bit_cast of
+        // a component expression reads component 0 whatever the index)
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          p0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (int)xv[c][i][e]),
+                                      __builtin_bit_cast(h2, (int)d[e]), p0, false);
+          p1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (int)xv[c][i][e + 1]),
+                                      __builtin_bit_cast(h2, (int)d[e + 1]), p1, false);
+        }
       }
       // the group's sum over its four lanes, identical in all four
       float p = p0 + p1;
