@@ -917,11 +917,173 @@ static bool launch_w4a8_wide(const int8_t* xq, const float* xs, const int32_t* w
   }
 }
 
+// ---------------------------------------------------------------------------
+// One token row (M = 1): a matrix-vector product on the vector ALU's int8 dot
+// products, where a 16x16 MFMA would spend 15 of its 16 rows on padding.
+// Lane l of a wave covers bytes 16 l .. 16 l + 15 of every kilobyte c of a
+// weight row: codes k = 2048 c + 32 l + [0, 32), a quarter of group
+// g = 16 c + l / 4.  It keeps the matching 32 activation bytes of every c in
+// registers, split once into the even- and odd-code bytes of each word (the
+// order w & 0x0F0F0F0F and (w >> 4) & 0x0F0F0F0F unpack to), and the
+// group's token sum (byte sums reduced over the group's four lanes).  A wave
+// owns R consecutive weight rows and issues all their loads up front.  Per
+// word of 8 codes: two masks, a shift and two v_dot4_i32_i8 -- exact int32.
+// The group's four lanes add their sums (DPP), the zero point enters as
+// -z * (token sum), and the group sum is scaled by s in binary32 as in the
+// matrix-core kernels; the wave sums its lanes at the end.
+// ---------------------------------------------------------------------------
+constexpr int kGemvWaves = 4;
+
+__device__ __forceinline__ int quad_sum_i(int t) {
+  t += __builtin_amdgcn_mov_dpp(t, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  t += __builtin_amdgcn_mov_dpp(t, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  return t;
+}
+
+template <int R, int C, typename OutT>
+__global__ __launch_bounds__(64 * kGemvWaves) void k_w4a8_gemv(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, const int32_t* __restrict__ wq,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int N, int K,
+    OutT* __restrict__ y) {
+  constexpr bool kI32 = __is_same(OutT, int32_t);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = (blockIdx.x * kGemvWaves + wave) * R;
+  if (n0 >= N) return;   // wave-uniform
+  const int G = K >> 7, RB = K >> 1;   // groups and packed bytes per weight row
+  const int rows = min(R, N - n0);
+  const rsrc_t wr = make_rsrc_uniform(wq + (int64_t)n0 * (K >> 3), (u32)(rows * RB));
+  const rsrc_t sr = make_rsrc_uniform(wscale + (int64_t)n0 * G, (u32)(rows * G * 2));
+  const rsrc_t zr = make_rsrc_uniform(wzero + (int64_t)n0 * G, (u32)(rows * G * 2));
+  const rsrc_t xr = make_rsrc_uniform(xq, (u32)K);
+
+  // activations first, then scales and zero points, then the weight stream;
+  // pieces past the row end read zeros (x through its resource's range, the
+  // rest through kOOB: their resources span the wave's rows)
+  v4i xv[C][2];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) xv[c][h] = bld16(xr, (u32)(2048 * c + 32 * lane + 16 * h));
+  uint16_t sb[R][C], zb[R][C];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int g = 16 * c + (lane >> 2);
+      const u32 o = g < G ? (u32)(2 * (r * G + g)) : kOOB;
+      sb[r][c] = bld2(sr, o);
+      zb[r][c] = bld2(zr, o);
+    }
+  v4i wv[R][C];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int b = 1024 * c + 16 * lane;
+      wv[r][c] = bld16_nt(wr, b < RB ? (u32)(r * RB + b) : kOOB);
+    }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // word i of the lane's piece holds codes 8i..8i+7: its activation bytes are
+  // dwords 2i, 2i+1 of the 32 loaded bytes
+  u32 xe[C][4], xo[C][4];
+  int tsum[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32 d0 = (u32)xv[c][i >> 1][2 * (i & 1)], d1 = (u32)xv[c][i >> 1][2 * (i & 1) + 1];
+      even_odd_bytes(d0, d1, xe[c][i], xo[c][i]);
+      t = __builtin_amdgcn_sdot4((int)d0, 0x01010101, t, false);
+      t = __builtin_amdgcn_sdot4((int)d1, 0x01010101, t, false);
+    }
+    tsum[c] = quad_sum_i(t);   // the group's token sum, in all four lanes
+  }
+
+  float yacc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    yacc[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      int a = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32 w = (u32)wv[r][c][i];
+        a = __builtin_amdgcn_sdot4((int)xe[c][i], (int)(w & 0x0F0F0F0Fu), a, false);
+        a = __builtin_amdgcn_sdot4((int)xo[c][i], (int)((w >> 4) & 0x0F0F0F0Fu), a, false);
+      }
+      // |z| <= 15 and |token sum| <= 128 * 127: the 24-bit multiply is exact
+      const int z = (int)f16_bits_to_f32(zb[r][c]);
+      const int acc = quad_sum_i(a) - __mul24(z, tsum[c]);
+      if constexpr (kI32) {
+        const int g = 16 * c + (lane >> 2);
+        if ((lane & 3) == 0 && g < G && r < rows) y[(int64_t)g * N + n0 + r] = acc;
+      } else {
+        yacc[r] = __builtin_fmaf(f16_bits_to_f32(sb[r][c]), (float)acc, yacc[r]);
+      }
+    }
+  }
+
+  if constexpr (!kI32) {
+    // sum over the 16 quads: rotations by 4 and 8 within each row of 16
+    // lanes, then the four rows; lane r stores weight row r's output
+    float mine = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int v = __float_as_int(yacc[r]);
+      v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false)));
+      v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false)));
+      const float t = (__int_as_float(__builtin_amdgcn_readlane(v, 0)) + __int_as_float(__builtin_amdgcn_readlane(v, 16))) +
+                      (__int_as_float(__builtin_amdgcn_readlane(v, 32)) + __int_as_float(__builtin_amdgcn_readlane(v, 48)));
+      mine = lane == r ? t : mine;
+    }
+    if (lane < rows) store_out<OutT>(y, n0 + lane, mine * xs[0]);
+  }
+}
+
+template <int R, int C, typename OutT>
+static void launch_w4a8_gemv_rc(const int8_t* xq, const float* xs, const int32_t* wq, const uint16_t* ws,
+                                const uint16_t* wz, int N, int K, OutT* y, hipStream_t st) {
+  const int waves = (N + R - 1) / R;
+  const dim3 grid((unsigned)((waves + kGemvWaves - 1) / kGemvWaves)), block(64 * kGemvWaves);
+  k_w4a8_gemv<R, C, OutT><<<grid, block, 0, st>>>(xq, xs, wq, ws, wz, N, K, y);
+}
+
+// K up to 16384 (8 KB per weight row); rows per wave for about 8 kilobyte
+// weight loads in flight per wave (4 and 16 measured alike or slower).
+// Measured on MI355X against the matrix-core kernels it replaces at one row
+// (A/B, graphs of 200 calls, weights rotated through 600 MB; us, K x N):
+// 11008 x 4096 6.79-6.82 / 7.89-7.91, 4096 x 11008 5.90-5.91 / 6.96-7.04,
+// 4096 x 12288 6.18-6.27 / 7.16, 4096 x 4096 3.73-3.75 / 4.90,
+// 14336 x 4096 7.85 / 8.87-8.92, 8192 x 28672 20.53-20.54 / 26.24-26.31;
+// the int32 group sums are the same bit for bit.
+template <typename OutT>
+static bool launch_w4a8_gemv(const int8_t* xq, const float* xs, const int32_t* wq, const uint16_t* ws,
+                             const uint16_t* wz, int N, int K, OutT* y, hipStream_t st) {
+  constexpr int L = 8;
+  constexpr auto rows = [](int c) { return L / c < 1 ? 1 : L / c; };
+  switch ((K / 2 + 1023) / 1024) {
+    case 1: launch_w4a8_gemv_rc<rows(1), 1, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
+    case 2: launch_w4a8_gemv_rc<rows(2), 2, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
+    case 3: launch_w4a8_gemv_rc<rows(3), 3, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
+    case 4: launch_w4a8_gemv_rc<rows(4), 4, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
+    case 5: launch_w4a8_gemv_rc<rows(5), 5, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
+    case 6: launch_w4a8_gemv_rc<rows(6), 6, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
+    case 7: launch_w4a8_gemv_rc<rows(7), 7, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
+    case 8: launch_w4a8_gemv_rc<rows(8), 8, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
+    default: return false;
+  }
+}
+
 template <typename OutT>
 static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* wq,
                               const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
                               hipStream_t st) {
   const size_t lds = (size_t)16 * sz_pitch(K / 128) * 4;
+  if (M == 1 && launch_w4a8_gemv<OutT>(xq, xs, wq, ws, wz, N, K, y, st)) return hipGetLastError();
   if (M <= 64 && wide_waves(N) >= 2) {
     // layers of more than 384 blocks: the token rows staged once per
     // workgroup of 2-4 weight blocks (unless K is too long for LDS).

@@ -66,7 +66,7 @@ W4A8_CASES = [
     (4, 6128, 1024),     # decode kernel (383 blocks of 16 rows)
     (4, 6144, 1024),     # wide kernel (384 blocks: 2 per workgroup, K split over 4 waves)
     (16, 6144, 1024),    # wide kernel, 16 rows
-    (1, 12304, 1024),    # wide kernel, 3 blocks per workgroup, the last workgroup ragged
+    (2, 12304, 1024),    # wide kernel, 3 blocks per workgroup, the last workgroup ragged
     (8, 16400, 1024),    # wide kernel, 4 blocks per workgroup (K split over 2 waves)
     (17, 6128, 1024),    # one weight stream, 2 tiles of 16 rows (383 blocks)
     (17, 6144, 1024),    # wide kernel, 2 m-tiles
@@ -79,6 +79,14 @@ W4A8_CASES = [
     (2, 16, 163712),     # decode kernel with 1279 groups (scales at 80 KB of LDS)
     (2, 16, 163840),     # 1280 groups: direct-load kernel
     (20, 16, 163712),    # 2 tiles with 1279 groups
+    (1, 64, 4096),       # one token row: int8 dot-product kernel, 2 KB weight rows, 4 per wave
+    (1, 50, 3200),       # same, second kilobyte of each row ragged, last wave 2 rows
+    (1, 12304, 1024),    # same, 1 KB rows, 8 per wave
+    (1, 37, 1152),       # same, 576-byte rows (lanes past the row end idle)
+    (1, 16, 128),        # same, one group
+    (1, 4100, 11008),    # same, 6 KB rows, one per wave
+    (1, 24, 16384),      # same, 8 KB rows (the longest it takes)
+    (1, 24, 16512),      # rows past 8 KB: the matrix-core decode kernel
 ]
 
 
