@@ -918,8 +918,9 @@ static bool launch_w4a8_wide(const int8_t* xq, const float* xs, const int32_t* w
 }
 
 // ---------------------------------------------------------------------------
-// One token row (M = 1): a matrix-vector product on the vector ALU's int8 dot
-// products, where a 16x16 MFMA would spend 15 of its 16 rows on padding.
+// One or two token rows (MR): a matrix-vector product on the vector ALU's
+// int8 dot products, where a 16x16 MFMA would spend 15 of its 16 rows on
+// padding.
 // Lane l of a wave covers bytes 16 l .. 16 l + 15 of every kilobyte c of a
 // weight row: codes k = 2048 c + 32 l + [0, 32), a quarter of group
 // g = 16 c + l / 4.  It keeps the matching 32 activation bytes of every c in
@@ -940,10 +941,10 @@ __device__ __forceinline__ int quad_sum_i(int t) {
   return t;
 }
 
-template <int R, int C, typename OutT>
+template <int MR, int R, int C, typename OutT>
 __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a8_gemv(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, const int32_t* __restrict__ wq,
-    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int N, int K,
+    const uint16_t* __restrict__ wscale, const uint16_t* __restrict__ wzero, int M, int N, int K,
     OutT* __restrict__ y) {
   constexpr bool kI32 = __is_same(OutT, int32_t);
   const int lane = threadIdx.x & 63;
@@ -955,16 +956,21 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a8_gemv(
   const rsrc_t wr = make_rsrc_uniform(wq + (int64_t)n0 * (K >> 3), (u32)(rows * RB));
   const rsrc_t sr = make_rsrc_uniform(wscale + (int64_t)n0 * G, (u32)(rows * G * 2));
   const rsrc_t zr = make_rsrc_uniform(wzero + (int64_t)n0 * G, (u32)(rows * G * 2));
-  const rsrc_t xr = make_rsrc_uniform(xq, (u32)K);
+  const rsrc_t xr = make_rsrc_uniform(xq, (u32)(M * K));   // token rows past M read zeros
 
   // activations first, then scales and zero points, then the weight stream;
   // pieces past the row end read zeros (x through its resource's range, the
   // rest through kOOB: their resources span the wave's rows)
-  v4i xv[C][2];
+  v4i xv[MR][C][2];
 #pragma unroll
-  for (int c = 0; c < C; ++c)
+  for (int m = 0; m < MR; ++m)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) xv[c][h] = bld16(xr, (u32)(2048 * c + 32 * lane + 16 * h));
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = 2048 * c + 32 * lane + 16 * h;
+        xv[m][c][h] = bld16(xr, k < K ? (u32)(m * K + k) : kOOB);
+      }
   uint16_t sb[R][C], zb[R][C];
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -987,69 +993,85 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a8_gemv(
 
   // word i of the lane's piece holds codes 8i..8i+7: its activation bytes are
   // dwords 2i, 2i+1 of the 32 loaded bytes
-  u32 xe[C][4], xo[C][4];
-  int tsum[C];
+  u32 xe[MR][C][4], xo[MR][C][4];
+  int tsum[MR][C];
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    int t = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32 d0 = (u32)xv[c][i >> 1][2 * (i & 1)], d1 = (u32)xv[c][i >> 1][2 * (i & 1) + 1];
-      even_odd_bytes(d0, d1, xe[c][i], xo[c][i]);
-      t = __builtin_amdgcn_sdot4((int)d0, 0x01010101, t, false);
-      t = __builtin_amdgcn_sdot4((int)d1, 0x01010101, t, false);
-    }
-    tsum[c] = quad_sum_i(t);   // the group's token sum, in all four lanes
-  }
-
-  float yacc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    yacc[r] = 0.f;
+  for (int m = 0; m < MR; ++m)
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      int a = 0;
+      int t = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32 d0 = (u32)xv[m][c][i >> 1][2 * (i & 1)], d1 = (u32)xv[m][c][i >> 1][2 * (i & 1) + 1];
+        even_odd_bytes(d0, d1, xe[m][c][i], xo[m][c][i]);
+        t = __builtin_amdgcn_sdot4((int)d0, 0x01010101, t, false);
+        t = __builtin_amdgcn_sdot4((int)d1, 0x01010101, t, false);
+      }
+      tsum[m][c] = quad_sum_i(t);   // the group's token sum, in all four lanes
+    }
+
+  float yacc[MR][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) yacc[m][r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      u32 lo[4], hi[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const u32 w = (u32)wv[r][c][i];
-        a = __builtin_amdgcn_sdot4((int)xe[c][i], (int)(w & 0x0F0F0F0Fu), a, false);
-        a = __builtin_amdgcn_sdot4((int)xo[c][i], (int)((w >> 4) & 0x0F0F0F0Fu), a, false);
+        lo[i] = w & 0x0F0F0F0Fu;
+        hi[i] = (w >> 4) & 0x0F0F0F0Fu;
       }
       // |z| <= 15 and |token sum| <= 128 * 127: the 24-bit multiply is exact
       const int z = (int)f16_bits_to_f32(zb[r][c]);
-      const int acc = quad_sum_i(a) - __mul24(z, tsum[c]);
-      if constexpr (kI32) {
-        const int g = 16 * c + (lane >> 2);
-        if ((lane & 3) == 0 && g < G && r < rows) y[(int64_t)g * N + n0 + r] = acc;
-      } else {
-        yacc[r] = __builtin_fmaf(f16_bits_to_f32(sb[r][c]), (float)acc, yacc[r]);
+      const float s = f16_bits_to_f32(sb[r][c]);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        int a = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a = __builtin_amdgcn_sdot4((int)xe[m][c][i], (int)lo[i], a, false);
+          a = __builtin_amdgcn_sdot4((int)xo[m][c][i], (int)hi[i], a, false);
+        }
+        const int acc = quad_sum_i(a) - __mul24(z, tsum[m][c]);
+        if constexpr (kI32) {
+          const int g = 16 * c + (lane >> 2);
+          if ((lane & 3) == 0 && g < G && r < rows && m < M) y[((int64_t)m * G + g) * N + n0 + r] = acc;
+        } else {
+          yacc[m][r] = __builtin_fmaf(s, (float)acc, yacc[m][r]);
+        }
       }
     }
   }
 
   if constexpr (!kI32) {
     // sum over the 16 quads: rotations by 4 and 8 within each row of 16
-    // lanes, then the four rows; lane r stores weight row r's output
+    // lanes, then the four rows; lane m R + r stores token row m, weight row r
     float mine = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      int v = __float_as_int(yacc[r]);
-      v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false)));
-      v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false)));
-      const float t = (__int_as_float(__builtin_amdgcn_readlane(v, 0)) + __int_as_float(__builtin_amdgcn_readlane(v, 16))) +
-                      (__int_as_float(__builtin_amdgcn_readlane(v, 32)) + __int_as_float(__builtin_amdgcn_readlane(v, 48)));
-      mine = lane == r ? t : mine;
-    }
-    if (lane < rows) store_out<OutT>(y, n0 + lane, mine * xs[0]);
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        int v = __float_as_int(yacc[m][r]);
+        v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false)));
+        v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false)));
+        const float t = (__int_as_float(__builtin_amdgcn_readlane(v, 0)) + __int_as_float(__builtin_amdgcn_readlane(v, 16))) +
+                        (__int_as_float(__builtin_amdgcn_readlane(v, 32)) + __int_as_float(__builtin_amdgcn_readlane(v, 48)));
+        mine = lane == m * R + r ? t : mine;
+      }
+    const int m = lane / R, r = lane - m * R;
+    if (m < MR && m < M && r < rows) store_out<OutT>(y, (int64_t)m * N + n0 + r, mine * xs[m]);
   }
 }
 
-template <int R, int C, typename OutT>
+template <int MR, int R, int C, typename OutT>
 static void launch_w4a8_gemv_rc(const int8_t* xq, const float* xs, const int32_t* wq, const uint16_t* ws,
-                                const uint16_t* wz, int N, int K, OutT* y, hipStream_t st) {
+                                const uint16_t* wz, int M, int N, int K, OutT* y, hipStream_t st) {
   const int waves = (N + R - 1) / R;
   const dim3 grid((unsigned)((waves + kGemvWaves - 1) / kGemvWaves)), block(64 * kGemvWaves);
-  k_w4a8_gemv<R, C, OutT><<<grid, block, 0, st>>>(xq, xs, wq, ws, wz, N, K, y);
+  k_w4a8_gemv<MR, R, C, OutT><<<grid, block, 0, st>>>(xq, xs, wq, ws, wz, M, N, K, y);
 }
 
 // K up to 16384 (8 KB per weight row); rows per wave for about 8 kilobyte
@@ -1060,22 +1082,35 @@ static void launch_w4a8_gemv_rc(const int8_t* xq, const float* xs, const int32_t
 // 4096 x 12288 6.18-6.27 / 7.16, 4096 x 4096 3.73-3.75 / 4.90,
 // 14336 x 4096 7.85 / 8.87-8.92, 8192 x 28672 20.53-20.54 / 26.24-26.31;
 // the int32 group sums are the same bit for bit.
-template <typename OutT>
-static bool launch_w4a8_gemv(const int8_t* xq, const float* xs, const int32_t* wq, const uint16_t* ws,
-                             const uint16_t* wz, int N, int K, OutT* y, hipStream_t st) {
+template <int MR, typename OutT>
+static bool launch_w4a8_gemv_mr(const int8_t* xq, const float* xs, const int32_t* wq, const uint16_t* ws,
+                                const uint16_t* wz, int M, int N, int K, OutT* y, hipStream_t st) {
   constexpr int L = 8;
   constexpr auto rows = [](int c) { return L / c < 1 ? 1 : L / c; };
   switch ((K / 2 + 1023) / 1024) {
-    case 1: launch_w4a8_gemv_rc<rows(1), 1, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
-    case 2: launch_w4a8_gemv_rc<rows(2), 2, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
-    case 3: launch_w4a8_gemv_rc<rows(3), 3, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
-    case 4: launch_w4a8_gemv_rc<rows(4), 4, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
-    case 5: launch_w4a8_gemv_rc<rows(5), 5, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
-    case 6: launch_w4a8_gemv_rc<rows(6), 6, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
-    case 7: launch_w4a8_gemv_rc<rows(7), 7, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
-    case 8: launch_w4a8_gemv_rc<rows(8), 8, OutT>(xq, xs, wq, ws, wz, N, K, y, st); return true;
+    case 1: launch_w4a8_gemv_rc<MR, rows(1), 1, OutT>(xq, xs, wq, ws, wz, M, N, K, y, st); return true;
+    case 2: launch_w4a8_gemv_rc<MR, rows(2), 2, OutT>(xq, xs, wq, ws, wz, M, N, K, y, st); return true;
+    case 3: launch_w4a8_gemv_rc<MR, rows(3), 3, OutT>(xq, xs, wq, ws, wz, M, N, K, y, st); return true;
+    case 4: launch_w4a8_gemv_rc<MR, rows(4), 4, OutT>(xq, xs, wq, ws, wz, M, N, K, y, st); return true;
+    case 5: launch_w4a8_gemv_rc<MR, rows(5), 5, OutT>(xq, xs, wq, ws, wz, M, N, K, y, st); return true;
+    case 6: launch_w4a8_gemv_rc<MR, rows(6), 6, OutT>(xq, xs, wq, ws, wz, M, N, K, y, st); return true;
+    case 7: launch_w4a8_gemv_rc<MR, rows(7), 7, OutT>(xq, xs, wq, ws, wz, M, N, K, y, st); return true;
+    case 8: launch_w4a8_gemv_rc<MR, rows(8), 8, OutT>(xq, xs, wq, ws, wz, M, N, K, y, st); return true;
     default: return false;
   }
+}
+
+// Two token rows: the unpack is shared, the dot products double.  Measured
+// against the matrix-core kernels (us): K = 4096 with N = 4096 4.24-4.26 /
+// 5.01, N = 11008 6.76-6.77 / 7.25-7.41, N = 12288 7.28-7.68 / 7.52-7.84;
+// longer rows lose (K = 11008, N = 4096: 8.52-8.56 / 8.00-8.01), and so do
+// four rows everywhere (K = 4096, N = 11008: 9.6 / 7.5-7.8).
+template <typename OutT>
+static bool launch_w4a8_gemv(const int8_t* xq, const float* xs, const int32_t* wq, const uint16_t* ws,
+                             const uint16_t* wz, int M, int N, int K, OutT* y, hipStream_t st) {
+  if (M == 1) return launch_w4a8_gemv_mr<1, OutT>(xq, xs, wq, ws, wz, M, N, K, y, st);
+  if (M == 2 && K <= 4096) return launch_w4a8_gemv_mr<2, OutT>(xq, xs, wq, ws, wz, M, N, K, y, st);
+  return false;
 }
 
 template <typename OutT>
@@ -1083,7 +1118,7 @@ static hipError_t gemm_w4a8_t(const int8_t* xq, const float* xs, const int32_t* 
                               const uint16_t* ws, const uint16_t* wz, int M, int N, int K, OutT* y,
                               hipStream_t st) {
   const size_t lds = (size_t)16 * sz_pitch(K / 128) * 4;
-  if (M == 1 && launch_w4a8_gemv<OutT>(xq, xs, wq, ws, wz, N, K, y, st)) return hipGetLastError();
+  if (M <= 2 && launch_w4a8_gemv<OutT>(xq, xs, wq, ws, wz, M, N, K, y, st)) return hipGetLastError();
   if (M <= 64 && wide_waves(N) >= 2) {
     // layers of more than 384 blocks: the token rows staged once per
     // workgroup of 2-4 weight blocks (unless K is too long for LDS).

@@ -196,8 +196,8 @@ qg_status_t quantize_gemm_w8a8_plan(int x_dtype, int64_t M, int64_t N, int64_t K
  *    [M][K/128][N] int32 holding acc[m,g,n] (x_scale and w_scale_f16 unused).
  * K must be a positive multiple of 128 with K / 128 <= 65535 (as for
  * quantize_weight_u4_g128).  The int8 matrix cores take the products; one
- * token row with K <= 16384 takes int8 dot products on the vector ALU
- * (the same int32 acc bit for bit).
+ * token row with K <= 16384, or two with K <= 4096, take int8 dot products
+ * on the vector ALU (the same int32 acc bit for bit).
  */
 qg_status_t gemm_w4a8_g128(const int8_t* xq, const float* x_scale, const int32_t* wq,
                            const uint16_t* w_scale_f16, const uint16_t* w_zero_f16,

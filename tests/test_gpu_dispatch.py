@@ -87,6 +87,9 @@ W4A8_CASES = [
     (1, 4100, 11008),    # same, 6 KB rows, one per wave
     (1, 24, 16384),      # same, 8 KB rows (the longest it takes)
     (1, 24, 16512),      # rows past 8 KB: the matrix-core decode kernel
+    (2, 50, 4096),       # two token rows: the int8 dot-product kernel (K <= 4096)
+    (2, 37, 1152),       # same, ragged rows
+    (2, 50, 4224),       # two rows past K = 4096: the matrix-core decode kernel
 ]
 
 

@@ -196,8 +196,8 @@ def _w4a8_floor(xq, sx, packed, sc, zz):
 @pytest.mark.parametrize("M,N,K", [(16, 4096, 11008), (5, 17, 256), (33, 40, 640), (2, 48, 14336),
                                    (64, 300, 1024), (4, 8200, 1024), (16, 11008, 4096),
                                    (32, 11008, 4096), (57, 7000, 1152),
-                                   # one token row (int8 dot-product kernel)
-                                   (1, 4096, 11008), (1, 777, 4224)])
+                                   # one and two token rows (int8 dot-product kernel)
+                                   (1, 4096, 11008), (1, 777, 4224), (2, 4100, 4096)])
 def test_w4a8_scaled(fmt, M, N, K):
     rng = np.random.default_rng(M + 3 * N + K)
     packed, sc, zz = _u4_weights(rng, K, N)
