@@ -431,10 +431,15 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
 // costs ~0.4 us more than the plain one, more than the panel GEMM gains
 // there.  From 384 blocks the plain GEMM is the wide kernel, which is faster
 // than the pair at every size tried (K = 4096, N = 11008: 1 row 10.3 against
-// 9.1 us, 16 rows 13.2 against 10.3; N = 14336, 28672 likewise).
+// 9.1 us, 16 rows 13.2 against 10.3; N = 14336, 28672 likewise).  Where the
+// plain GEMM is the int8 dot-product kernel (one token row, or two with
+// K <= 4096) the plain pair is faster too (K = 4096, N = 5120: 1 row 6.86
+// against 8.89 us, 2 rows 7.85 against 8.96; K = 11008, N = 5120, 1 row
+// 11.2 against 18.6).
 bool use_panel(int64_t M, int64_t N, int64_t K) {
   const int64_t nblocks = (N + 15) / 16;
-  return plan_gemm(M, N, K).ok && nblocks > 256 && nblocks < 384;
+  const bool dot_kernel = M == 1 || (M == 2 && K <= 4096);
+  return !dot_kernel && plan_gemm(M, N, K).ok && nblocks > 256 && nblocks < 384;
 }
 
 template <int DT>

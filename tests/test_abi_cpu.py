@@ -205,9 +205,9 @@ def test_fused_plan_on_the_host():
 
 def test_w4a8_workspace_on_the_host():
     """quantize_gemm_w4a8_g128_workspace_bytes: (K / 128) x 2112 bytes where
-    the panel pair runs (1..16 rows, K <= 16384, 257-383 blocks of 16
-    channels), 0 where the call runs the two plain kernels; the panel's own
-    size."""
+    the panel pair runs (2..16 rows, K <= 16384, 257-383 blocks of 16
+    channels, not where the plain GEMM is the dot-product kernel), 0 where
+    the call runs the two plain kernels; the panel's own size."""
     import bit_quantized_gemm_int8_amd as q
     _lib()
     wb = q.quantize_gemm_w4a8_g128_workspace_bytes
@@ -217,6 +217,9 @@ def test_w4a8_workspace_on_the_host():
     assert wb(16, 11008, 4096) == 0 and wb(1, 12288, 4096) == 0
     assert wb(2, 4112, 16384) == 128 * 2112           # the longest K
     assert wb(2, 4112, 16512) == 0
+    assert wb(1, 4112, 4096) == 0                     # one row: the dot-product GEMM
+    assert wb(2, 4112, 4096) == 0                     # two rows, K <= 4096: likewise
+    assert wb(2, 4112, 4224) == 33 * 2112             # two rows past K = 4096: the pair
     assert wb(16, 4096, 11008) == 0                   # 256 blocks: the plain kernels
     assert wb(1, 4096, 4096) == 0 and wb(3, 100, 2048) == 0
     assert wb(17, 8192, 4096) == 0                    # past 16 rows
